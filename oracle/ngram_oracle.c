@@ -1,0 +1,278 @@
+/*
+ * ORACLE for the hashed N-gram embedding layer -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU definition of what the layer computes,
+ * used to check the GPU library.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It
+ * shares no source, header, table or helper with the GPU library.
+ *
+ * All floating point is IEEE double on values that are exact conversions of
+ * the fp32 / bf16 inputs; loops only, no BLAS, no blocking or reordering.
+ *
+ * Sources (page title, then the part of it followed):
+ *  [A] "Qwen 4用上DeepSeek的Engram！125B MoE一张4090能跑不用量化" (yktysq.com),
+ *      section "DeepSeek Engram 更复杂，Qwen 更精简": Engram's four components
+ *      (tokenizer compression; multi-head hashing into prime-sized tables and
+ *      concatenation; context-aware gating; kernel-4 causal conv with dilation
+ *      = max n-gram order; multi-branch sharing of table and value projection).
+ *  [B] "Qwen3.8-Flash-Next 深度研究：把容量从「计算」搬到「存储」" (zhichai.net),
+ *      §2.3 "Embedding：N-gram Embedding": the lookup (2-gram heads on
+ *      (x_{t-1}, x_t), 3-gram heads on (x_{t-2}, x_{t-1}, x_t)), concatenation
+ *      into E_t, and the layer formula E_t -> K_t, V_t; g_t = Gate(Norm(Q_t),
+ *      Norm(K_t)); U_t = g_t * V_t; Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))).
+ *  [C] same page, §3-D lineage table: Over-Encoding's "mod hash".
+ *
+ * Readings where the pages leave a step open (each is the plainest one the
+ * rest of the text supports):
+ *  - hash: key = XOR_i (uint64 c_{t-i} * A_{j,i}) mod 2^64, row = key mod p_j,
+ *    with the odd multipliers A passed in by the caller;
+ *  - positions before a sequence's start take the caller's history ids, else
+ *    the pad id;
+ *  - RMSNorm(x) = gamma * x / sqrt(mean(x^2) + eps); the gate's scaled dot
+ *    product divides by sqrt(d); the gate is the logistic sigmoid;
+ *  - conv tap i multiplies position t - i*dilation, depthwise, no bias, zero
+ *    before the sequence start (or the caller's normalised state rows).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+static double load_value(const void* base, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/*
+ * Step 1 -- tokenizer compression [A, first component]: c = LUT[x].
+ * An id outside [0, vocab) or a LUT entry outside [0, vocab_c) is invalid; it
+ * becomes pad_id.  Returns the number of invalid ids.
+ */
+int64_t orc_compress(const int32_t* raw, int64_t n, const int32_t* lut, int32_t vocab,
+                     int32_t vocab_c, int32_t pad_id, int32_t* comp) {
+  int64_t bad = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t x = raw[i];
+    int32_t c = pad_id;
+    if (x >= 0 && x < vocab) {
+      c = lut[x];
+      if (c < 0 || c >= vocab_c) {
+        c = pad_id;
+        ++bad;
+      }
+    } else {
+      ++bad;
+    }
+    comp[i] = c;
+  }
+  return bad;
+}
+
+/* Compressed id at position pos of sequence b (pos may be negative). */
+static int32_t context_id(const int32_t* comp, int32_t T, int32_t b, int64_t pos,
+                          const int32_t* hist, int32_t hist_len, int32_t pad_id) {
+  if (pos >= 0) return comp[(int64_t)b * T + pos];
+  int64_t h = (int64_t)hist_len + pos; /* hist[b][hist_len-1] is position -1 */
+  if (hist != NULL && h >= 0) return hist[(int64_t)b * hist_len + h];
+  return pad_id;
+}
+
+/*
+ * Step 2 -- n-gram keys and multi-head hashing [A, second component; B, the
+ * lookup rule; C, mod hash].  For order n = orders[o] and head k, table
+ * j = o*heads + k receives row
+ *     key = XOR_{i=0}^{n-1} ( c_{t-i} * mult[j*4 + i] )   (mod 2^64)
+ *     row = key mod rows[j].
+ * row_idx is [B*T, n_tables] with n_tables = n_orders*heads.
+ * hist (nullable) is [B, hist_len] compressed ids, oldest first.
+ */
+void orc_hash(const int32_t* comp, int32_t B, int32_t T, const int32_t* hist,
+              int32_t hist_len, int32_t pad_id, int32_t n_orders, const int32_t* orders,
+              int32_t heads, const int64_t* rows, const uint64_t* mult, int32_t* row_idx) {
+  const int32_t n_tables = n_orders * heads;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t t = 0; t < T; ++t) {
+      int32_t* out = row_idx + ((int64_t)b * T + t) * n_tables;
+      for (int32_t o = 0; o < n_orders; ++o) {
+        for (int32_t k = 0; k < heads; ++k) {
+          int32_t j = o * heads + k;
+          uint64_t key = 0;
+          for (int32_t i = 0; i < orders[o]; ++i) {
+            uint64_t c = (uint64_t)(uint32_t)context_id(comp, T, b, (int64_t)t - i, hist,
+                                                        hist_len, pad_id);
+            key ^= c * mult[(int64_t)j * 4 + i];
+          }
+          out[j] = (int32_t)(key % (uint64_t)rows[j]);
+        }
+      }
+    }
+  }
+}
+
+/*
+ * Step 3 -- gather and concatenate [A, second component; B, "16 row ids, 160
+ * values per row, concatenated into E_t"]: E_t = table_0[r_0] ++ table_1[r_1]
+ * ++ ... in table order (orders ascending, then heads).  e is [n_tok, mem]
+ * with mem = n_tables * row_dim.
+ */
+void orc_gather(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
+                const void* const* tables, int32_t dtype, int32_t row_dim, double* e) {
+  const int64_t mem = (int64_t)n_tables * row_dim;
+  for (int64_t t = 0; t < n_tok; ++t)
+    for (int32_t j = 0; j < n_tables; ++j) {
+      int64_t r = row_idx[t * n_tables + j];
+      for (int32_t c = 0; c < row_dim; ++c)
+        e[t * mem + (int64_t)j * row_dim + c] = load_value(tables[j], dtype, r * row_dim + c);
+    }
+}
+
+/*
+ * Step 4 -- key / value projections [B, E_t -> K_t, V_t]: out = E @ W with W
+ * stored [mem, d] row-major.  out is [n_tok, d].
+ */
+void orc_project(const double* e, int64_t n_tok, int32_t mem, const void* w, int32_t dtype,
+                 int32_t d, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t n = 0; n < d; ++n) {
+      double acc = 0.0;
+      for (int32_t m = 0; m < mem; ++m)
+        acc += e[t * mem + m] * load_value(w, dtype, (int64_t)m * d + n);
+      out[t * d + n] = acc;
+    }
+  }
+}
+
+/*
+ * Step 5 -- context-aware gate [A, third component; B, g_t = Gate(Norm(Q_t),
+ * Norm(K_t))]: the query is the layer's hidden state.
+ *     q = gamma_q * h / sqrt(mean(h^2) + eps),  k^ = gamma_k * k / sqrt(mean(k^2) + eps)
+ *     g = sigmoid( (q . k^) / sqrt(d) )
+ * hidden row for (token t, branch b) starts at t*tok_stride + b*branch_stride
+ * (branch_stride 0: one query shared by all branches).  k is [n_tok, nb, d].
+ * gamma_q / gamma_k (nullable = all ones) are in the hidden's dtype.
+ * gate is [n_tok, nb].
+ */
+void orc_gate(const void* hidden, int32_t dtype, int64_t tok_stride, int64_t branch_stride,
+              const double* k, int64_t n_tok, int32_t nb, int32_t d, const void* gamma_q,
+              const void* gamma_k, double eps, double* gate) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t b = 0; b < nb; ++b) {
+      int64_t hbase = t * tok_stride + (int64_t)b * branch_stride;
+      const double* kr = k + (t * nb + b) * (int64_t)d;
+      double hh = 0.0, kk = 0.0;
+      for (int32_t n = 0; n < d; ++n) {
+        double h = load_value(hidden, dtype, hbase + n);
+        hh += h * h;
+        kk += kr[n] * kr[n];
+      }
+      double inv_h = 1.0 / sqrt(hh / d + eps);
+      double inv_k = 1.0 / sqrt(kk / d + eps);
+      double dot = 0.0;
+      for (int32_t n = 0; n < d; ++n) {
+        double gq = gamma_q ? load_value(gamma_q, dtype, n) : 1.0;
+        double gk = gamma_k ? load_value(gamma_k, dtype, n) : 1.0;
+        double q = gq * load_value(hidden, dtype, hbase + n) * inv_h;
+        double kn = gk * kr[n] * inv_k;
+        dot += q * kn;
+      }
+      double z = dot / sqrt((double)d);
+      gate[t * nb + b] = 1.0 / (1.0 + exp(-z));
+    }
+  }
+}
+
+/*
+ * Step 6 -- gated value [B, U_t = g_t (.) V_t]: the value projection is shared
+ * by the branches [A, multi-branch integration].  v is [n_tok, d], u is
+ * [n_tok, nb, d].
+ */
+void orc_gated_value(const double* gate, const double* v, int64_t n_tok, int32_t nb, int32_t d,
+                     double* u) {
+  for (int64_t t = 0; t < n_tok; ++t)
+    for (int32_t b = 0; b < nb; ++b)
+      for (int32_t n = 0; n < d; ++n)
+        u[(t * nb + b) * (int64_t)d + n] = gate[t * nb + b] * v[t * d + n];
+}
+
+/*
+ * Step 7 -- convolution block [A, fourth component; B, Delta_t = U_t +
+ * SiLU(DWConv(RMSNorm(U_t)))]:
+ *     N_t     = gamma_u * U_t / sqrt(mean(U_t^2) + eps)          (per branch)
+ *     C_t     = sum_{i=0}^{kernel-1} w_i (.) N_{t - i*dil}       (depthwise)
+ *     Delta_t = U_t + C_t * sigmoid(C_t)
+ * u and delta are [B, T, nb, d]; w is [kernel, d] in w_dtype; gamma_u
+ * (nullable) in w_dtype.  A tap before the sequence start reads the caller's
+ * state row (already normalised) when state != NULL -- state is
+ * [B, (kernel-1)*dil, nb, d], its last row being position -1 -- else zero.
+ */
+void orc_conv_block(const double* u, int32_t B, int32_t T, int32_t nb, int32_t d,
+                    const void* w, int32_t w_dtype, int32_t kernel, int32_t dil,
+                    const void* gamma_u, double eps, const double* state, double* delta) {
+  const int64_t row = (int64_t)nb * d;
+  const int32_t span = (kernel - 1) * dil;
+  double* nrm = (double*)malloc(sizeof(double) * (size_t)((int64_t)B * T * row));
+  if (nrm == NULL) return;
+  /* N_t = RMSNorm(U_t), one row per (token, branch) */
+#pragma omp parallel for schedule(static)
+  for (int64_t tb = 0; tb < (int64_t)B * T * nb; ++tb) {
+    const double* ut = u + tb * d;
+    double ss = 0.0;
+    for (int32_t n = 0; n < d; ++n) ss += ut[n] * ut[n];
+    double inv = 1.0 / sqrt(ss / d + eps);
+    for (int32_t n = 0; n < d; ++n) {
+      double g = gamma_u ? load_value(gamma_u, w_dtype, n) : 1.0;
+      nrm[tb * d + n] = g * ut[n] * inv;
+    }
+  }
+  /* C_t = sum_i w_i (.) N_{t - i*dil};  Delta_t = U_t + SiLU(C_t) */
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t t = 0; t < T; ++t) {
+      for (int32_t br = 0; br < nb; ++br) {
+        int64_t off = ((int64_t)b * T + t) * row + (int64_t)br * d;
+        for (int32_t n = 0; n < d; ++n) {
+          double c = 0.0;
+          for (int32_t i = 0; i < kernel; ++i) {
+            int64_t p = (int64_t)t - (int64_t)i * dil;
+            double nval = 0.0;
+            if (p >= 0) {
+              nval = nrm[((int64_t)b * T + p) * row + (int64_t)br * d + n];
+            } else if (state != NULL) {
+              int64_t s = (int64_t)span + p; /* row inside the state; last row is p = -1 */
+              if (s >= 0) nval = state[((int64_t)b * span + s) * row + (int64_t)br * d + n];
+            }
+            c += load_value(w, w_dtype, (int64_t)i * d + n) * nval;
+          }
+          delta[off + n] = u[off + n] + c / (1.0 + exp(-c));
+        }
+      }
+    }
+  }
+  free(nrm);
+}
