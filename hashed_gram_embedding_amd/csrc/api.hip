@@ -1,0 +1,402 @@
+// extern "C" entry points of libngram.so: argument validation on the host,
+// workspace layout, and the launch sequence of each operation.  Every step
+// of the layer runs in the kernels of ids.hip, gather.hip, project.hip and
+// finalize.hip; this file launches them on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+
+using namespace ngram;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int64_t kMaxTokens = int64_t(1) << 28;
+
+int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+uint64_t mulmod(uint64_t a, uint64_t b, uint64_t m) {
+  return (uint64_t)((unsigned __int128)a * b % m);
+}
+uint64_t powmod(uint64_t a, uint64_t e, uint64_t m) {
+  uint64_t r = 1;
+  a %= m;
+  while (e) {
+    if (e & 1) r = mulmod(r, a, m);
+    a = mulmod(a, a, m);
+    e >>= 1;
+  }
+  return r;
+}
+
+// Deterministic Miller-Rabin for n < 2^32 (bases 2, 7, 61 suffice: Jaeschke,
+// "On strong pseudoprimes to several bases", Math. Comp. 1993).
+bool is_prime_u32(uint64_t n) {
+  if (n < 2) return false;
+  static const uint64_t small[] = {2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37, 61};
+  for (uint64_t p : small) {
+    if (n == p) return true;
+    if (n % p == 0) return false;
+  }
+  uint64_t d = n - 1;
+  int s = 0;
+  while (!(d & 1)) {
+    d >>= 1;
+    ++s;
+  }
+  for (uint64_t a : {2ull, 7ull, 61ull}) {
+    uint64_t x = powmod(a, d, n);
+    if (x == 1 || x == n - 1) continue;
+    bool comp = true;
+    for (int i = 1; i < s; ++i) {
+      x = mulmod(x, x, n);
+      if (x == n - 1) {
+        comp = false;
+        break;
+      }
+    }
+    if (comp) return false;
+  }
+  return true;
+}
+
+int validate(const ngram_config* c) {
+  if (c == nullptr) return NGRAM_EINVAL;
+  if (c->table_dtype != NGRAM_F32 && c->table_dtype != NGRAM_BF16) return NGRAM_EDTYPE;
+  if (c->act_dtype != NGRAM_F32 && c->act_dtype != NGRAM_BF16) return NGRAM_EDTYPE;
+  if (c->table_dtype != c->act_dtype) return NGRAM_EDTYPE;
+  if (c->n_orders < 1 || c->n_orders > NGRAM_MAX_ORDER) return NGRAM_EINVAL;
+  for (int o = 0; o < c->n_orders; ++o) {
+    if (c->orders[o] < 1 || c->orders[o] > NGRAM_MAX_ORDER) return NGRAM_EINVAL;
+    if (o > 0 && c->orders[o] <= c->orders[o - 1]) return NGRAM_EINVAL;
+  }
+  if (c->heads_per_order < 1) return NGRAM_EINVAL;
+  if ((int64_t)c->n_orders * c->heads_per_order > NGRAM_MAX_TABLES) return NGRAM_ESHAPE;
+  if (c->n_tables != c->n_orders * c->heads_per_order) return NGRAM_EINVAL;
+  for (int j = 0; j < c->n_tables; ++j) {
+    if (c->rows[j] < 2 || c->rows[j] > INT32_MAX) return NGRAM_ERANGE;
+    if (!is_prime_u32((uint64_t)c->rows[j])) return NGRAM_ERANGE;
+  }
+  const int es = esize_of(c->table_dtype);
+  if (c->row_dim < 1 || ((int64_t)c->row_dim * es) % 16 != 0) return NGRAM_ESHAPE;
+  if ((int64_t)c->mem_dim != (int64_t)c->n_tables * c->row_dim) return NGRAM_EINVAL;
+  if (c->hidden_dim < 4 || c->hidden_dim % 4 != 0) return NGRAM_ESHAPE;
+  if (c->table_dtype == NGRAM_BF16 && (c->mem_dim % 64 != 0 || c->hidden_dim % 32 != 0))
+    return NGRAM_ESHAPE;
+  if (c->n_branches < 1 || c->n_branches > NGRAM_MAX_BRANCHES) return NGRAM_EINVAL;
+  if (c->conv_kernel != 4) return NGRAM_EINVAL;
+  if (c->conv_dilation != c->orders[c->n_orders - 1]) return NGRAM_EINVAL;
+  if (c->vocab < 1 || c->vocab_compressed < 1) return NGRAM_EINVAL;
+  if (c->pad_id < 0 || c->pad_id >= c->vocab_compressed) return NGRAM_EINVAL;
+  if (!(c->rms_eps >= 0.0f) || !isfinite(c->rms_eps)) return NGRAM_EINVAL;
+  return NGRAM_OK;
+}
+
+HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
+  HashArgs a;
+  memset(&a, 0, sizeof a);
+  a.n_orders = c->n_orders;
+  a.heads = c->heads_per_order;
+  a.n_tables = c->n_tables;
+  a.max_order = c->orders[c->n_orders - 1];
+  a.pad_id = c->pad_id;
+  a.vocab = c->vocab;
+  a.vocab_c = c->vocab_compressed;
+  a.hist_len = hist_len;
+  for (int o = 0; o < c->n_orders; ++o) a.orders[o] = c->orders[o];
+  for (int j = 0; j < c->n_tables; ++j) {
+    a.rows[j] = (uint64_t)c->rows[j];
+    for (int i = 0; i < NGRAM_MAX_ORDER; ++i) a.mult[j][i] = c->hash_mult[j][i];
+  }
+  return a;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t row_idx = 0, e = 0, v = 0, parts = 0, total = 0;
+  ProjPlan plan;
+  int64_t v_stride = 0;  // fp32 elements between V rows
+  int64_t v_offset = 0;  // fp32 elements from the V buffer to row 0's values
+};
+
+// with_memory: the forward pass also keeps the row ids and E in the workspace.
+Layout layout_for(const ngram_config* c, int64_t n_tok, bool with_memory) {
+  Layout L;
+  const int dt = c->table_dtype;
+  const int nb = c->n_branches, d = c->hidden_dim;
+  L.plan = plan_projection(dt, n_tok, d);
+  size_t off = 0;
+  if (with_memory) {
+    L.row_idx = off;
+    off = align_up(off + (size_t)n_tok * c->n_tables * sizeof(int32_t));
+    L.e = off;
+    off = align_up(off + (size_t)n_tok * c->mem_dim * esize_of(dt));
+  }
+  L.v = off;
+  if (dt == NGRAM_BF16) {
+    off = align_up(off + (size_t)n_tok * d * sizeof(float));
+    L.v_stride = d;
+    L.v_offset = 0;
+  } else {  // the fp32 path keeps K and V: [n_tok, nb+1, d]
+    off = align_up(off + (size_t)n_tok * (nb + 1) * d * sizeof(float));
+    L.v_stride = (int64_t)(nb + 1) * d;
+    L.v_offset = (int64_t)nb * d;
+  }
+  L.parts = off;
+  off = align_up(off + (size_t)n_tok * (3 * nb + 1) * L.plan.np * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
+
+int check_tables(const ngram_config* c, const void* const* tables, TablePtrs* out) {
+  if (tables == nullptr) return NGRAM_EINVAL;
+  memset(out, 0, sizeof *out);
+  for (int j = 0; j < c->n_tables; ++j) {
+    if (tables[j] == nullptr) return NGRAM_EINVAL;
+    if (!aligned16(tables[j])) return NGRAM_EALIGN;
+    out->p[j] = tables[j];
+  }
+  return NGRAM_OK;
+}
+
+int check_hidden_stride(const ngram_config* c, int64_t hbs, int64_t* tok_stride) {
+  if (hbs != 0 && hbs != c->hidden_dim) return NGRAM_ESHAPE;
+  *tok_stride = hbs == 0 ? c->hidden_dim : (int64_t)c->n_branches * c->hidden_dim;
+  return NGRAM_OK;
+}
+
+ProjArgs proj_args(const ngram_config* c, const void* e, const void* w_k, const void* w_v,
+                   const void* hidden, int64_t h_tok, int64_t h_br, const void* gq,
+                   const void* gk, char* ws, const Layout& L, int64_t M) {
+  ProjArgs a;
+  a.e = e;
+  a.wk = w_k;
+  a.wv = w_v;
+  a.hidden = hidden;
+  a.h_tok_stride = h_tok;
+  a.h_branch_stride = h_br;
+  a.gamma_q = gq;
+  a.gamma_k = gk;
+  a.v = reinterpret_cast<float*>(ws + L.v);
+  a.parts = reinterpret_cast<float*>(ws + L.parts);
+  a.M = M;
+  a.K = c->mem_dim;
+  a.d = c->hidden_dim;
+  a.nb = c->n_branches;
+  a.np = L.plan.np;
+  return a;
+}
+
+ConvArgs conv_args_base(const ngram_config* c) {
+  ConvArgs a;
+  memset(&a, 0, sizeof a);
+  a.nb = c->n_branches;
+  a.d = c->hidden_dim;
+  a.eps = c->rms_eps;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ngram_status_str(int status) {
+  switch (status) {
+    case NGRAM_OK: return "NGRAM_OK";
+    case NGRAM_EINVAL: return "NGRAM_EINVAL: null pointer or inconsistent configuration";
+    case NGRAM_ESHAPE: return "NGRAM_ESHAPE: size out of range or not a supported multiple";
+    case NGRAM_EDTYPE: return "NGRAM_EDTYPE: unsupported dtype or dtype combination";
+    case NGRAM_EALIGN: return "NGRAM_EALIGN: device pointer not aligned";
+    case NGRAM_ERANGE: return "NGRAM_ERANGE: table rows not prime or out of range";
+    case NGRAM_EHIP: return "NGRAM_EHIP: HIP launch failed";
+    case NGRAM_EWORKSPACE: return "NGRAM_EWORKSPACE: workspace missing or too small";
+    default: return "unknown ngram status";
+  }
+}
+
+int ngram_abi_version(void) { return kAbiVersion; }
+
+int ngram_config_validate(const ngram_config* cfg) { return validate(cfg); }
+
+int ngram_compress_ids(const ngram_config* cfg, const int32_t* raw_ids, int64_t n,
+                       const int32_t* lut, int32_t* comp_ids, int32_t* err_flag, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (n < 0) return NGRAM_ESHAPE;
+  if (n == 0) return NGRAM_OK;
+  if (!raw_ids || !lut || !comp_ids) return NGRAM_EINVAL;
+  if (!aligned4(raw_ids) || !aligned4(lut) || !aligned4(comp_ids) || !aligned4(err_flag))
+    return NGRAM_EALIGN;
+  return hip_status(launch_compress(raw_ids, n, lut, cfg->vocab, cfg->vocab_compressed,
+                                    cfg->pad_id, comp_ids, err_flag,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int ngram_hash(const ngram_config* cfg, const int32_t* comp_ids, int32_t B, int32_t T,
+               const int32_t* history, int32_t* row_idx, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if ((int64_t)B * T == 0) return NGRAM_OK;
+  if (!comp_ids || !row_idx) return NGRAM_EINVAL;
+  if (!aligned4(comp_ids) || !aligned4(row_idx) || !aligned4(history)) return NGRAM_EALIGN;
+  const HashArgs a = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+  return hip_status(launch_hash(false, comp_ids, B, T, history, nullptr, a, row_idx, nullptr,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
+                 const void* const* tables, void* mem, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (n_tok < 0 || n_tok > kMaxTokens) return NGRAM_ESHAPE;
+  if (n_tok == 0) return NGRAM_OK;
+  if (!row_idx || !mem) return NGRAM_EINVAL;
+  TablePtrs tp;
+  st = check_tables(cfg, tables, &tp);
+  if (st) return st;
+  if (!aligned4(row_idx) || !aligned16(mem)) return NGRAM_EALIGN;
+  return hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim,
+                                  tp, mem, static_cast<hipStream_t>(stream)));
+}
+
+size_t ngram_gate_workspace_size(const ngram_config* cfg, int64_t n_tok) {
+  if (validate(cfg) != NGRAM_OK || n_tok < 0 || n_tok > kMaxTokens) return 0;
+  return layout_for(cfg, n_tok, false).total;
+}
+
+int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branch_stride,
+               const void* mem, const void* w_k, const void* w_v, const void* gamma_q,
+               const void* gamma_k, int64_t n_tok, float* gates, void* u, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (n_tok < 0 || n_tok > kMaxTokens) return NGRAM_ESHAPE;
+  int64_t h_tok = 0;
+  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
+  if (st) return st;
+  if (n_tok == 0) return NGRAM_OK;
+  if (!hidden || !mem || !w_k || !w_v || !gates) return NGRAM_EINVAL;
+  for (const void* p : {hidden, mem, w_k, w_v, gamma_q, gamma_k, (const void*)gates, (const void*)u})
+    if (!aligned16(p)) return NGRAM_EALIGN;
+  const Layout L = layout_for(cfg, n_tok, false);
+  if (!workspace) return NGRAM_EWORKSPACE;
+  if (workspace_bytes < L.total) return NGRAM_EWORKSPACE;
+  if (!aligned16(workspace)) return NGRAM_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const ProjArgs pa = proj_args(cfg, mem, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
+                                gamma_k, ws, L, n_tok);
+  st = hip_status(launch_projection(cfg->table_dtype, L.plan, pa, s));
+  if (st) return st;
+  ConvArgs ca = conv_args_base(cfg);
+  ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
+  ca.v_stride = L.v_stride;
+  ca.parts = reinterpret_cast<const float*>(ws + L.parts);
+  ca.np = L.plan.np;
+  ca.out = u;
+  ca.gates = gates;
+  return hip_status(launch_gate_values(cfg->act_dtype, ca, n_tok, s));
+}
+
+int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t T,
+                      const void* conv_w, const void* gamma_u, const float* conv_state,
+                      void* out, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if ((int64_t)B * T == 0) return NGRAM_OK;
+  if (!u || !conv_w || !out) return NGRAM_EINVAL;
+  for (const void* p : {u, conv_w, gamma_u, (const void*)conv_state, (const void*)out})
+    if (!aligned16(p)) return NGRAM_EALIGN;
+  ConvArgs ca = conv_args_base(cfg);
+  ca.u = u;
+  ca.conv_w = conv_w;
+  ca.gamma_u = gamma_u;
+  ca.state = conv_state;
+  ca.out = out;
+  ca.B = B;
+  ca.T = T;
+  ca.tile = conv_tile_for(T);
+  return hip_status(
+      launch_op_conv(cfg->act_dtype, cfg->conv_dilation, ca, static_cast<hipStream_t>(stream)));
+}
+
+size_t ngram_forward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T) {
+  if (validate(cfg) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
+  return layout_for(cfg, (int64_t)B * T, true).total;
+}
+
+int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                  const int32_t* history, const int32_t* lut, const void* const* tables,
+                  const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                  const void* w_v, const void* conv_w, const void* gamma_q,
+                  const void* gamma_k, const void* gamma_u, const float* conv_state,
+                  int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if (flags & ~NGRAM_ADD_RESIDUAL) return NGRAM_EINVAL;
+  int64_t h_tok = 0;
+  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
+  if (st) return st;
+  const int64_t n_tok = (int64_t)B * T;
+  if (n_tok == 0) return NGRAM_OK;
+  if (!raw_ids || !lut || !hidden || !w_k || !w_v || !conv_w || !out) return NGRAM_EINVAL;
+  TablePtrs tp;
+  st = check_tables(cfg, tables, &tp);
+  if (st) return st;
+  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut) || !aligned4(err_flag))
+    return NGRAM_EALIGN;
+  for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u,
+                        (const void*)conv_state, (const void*)out, (const void*)gates})
+    if (!aligned16(p)) return NGRAM_EALIGN;
+  const Layout L = layout_for(cfg, n_tok, true);
+  if (!workspace) return NGRAM_EWORKSPACE;
+  if (workspace_bytes < L.total) return NGRAM_EWORKSPACE;
+  if (!aligned16(workspace)) return NGRAM_EALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
+  void* e = ws + L.e;
+
+  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
+  if (st) return st;
+  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim, tp,
+                                e, s));
+  if (st) return st;
+  const ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
+                                gamma_k, ws, L, n_tok);
+  st = hip_status(launch_projection(cfg->table_dtype, L.plan, pa, s));
+  if (st) return st;
+  ConvArgs ca = conv_args_base(cfg);
+  ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
+  ca.v_stride = L.v_stride;
+  ca.parts = reinterpret_cast<const float*>(ws + L.parts);
+  ca.np = L.plan.np;
+  ca.conv_w = conv_w;
+  ca.gamma_u = gamma_u;
+  ca.state = conv_state;
+  ca.hidden = hidden;
+  ca.h_tok_stride = h_tok;
+  ca.h_branch_stride = hidden_branch_stride;
+  ca.out = out;
+  ca.gates = gates;
+  ca.B = B;
+  ca.T = T;
+  ca.tile = conv_tile_for(T);
+  ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
+  return hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+}
+
+}  // extern "C"

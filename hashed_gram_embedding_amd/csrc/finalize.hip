@@ -1,0 +1,235 @@
+// Gate, gated value and the convolution block.
+//
+// "Qwen3.8-Flash-Next 深度研究" §2.3: g_t = Gate(Norm(Q_t), Norm(K_t)),
+// U_t = g_t (.) V_t, Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))); Engram's third
+// and fourth components ("Qwen 4用上DeepSeek的Engram", section "DeepSeek Engram
+// 更复杂，Qwen 更精简"): a scalar sigmoid gate per token and branch from an
+// RMSNorm'd scaled dot product, and a depthwise causal conv of kernel 4 whose
+// dilation is the largest n-gram order.
+//
+// Streaming, HBM-bound work.  One workgroup takes a tile of consecutive
+// positions of one sequence and one branch:
+//   1. per position of the tile and its 3*dil-position halo it folds the
+//      projection's row partials into the gate g and the RMSNorm scale of
+//      U = g V (|U|^2 = g^2 |V|^2, so U itself is never reduced again), kept
+//      in LDS;
+//   2. each thread owns 4 columns and walks the positions in order, holding
+//      the normalised values of the last 3*dil+1 positions in registers, so
+//      every V element is read once per tile (plus the halo) and each output
+//      element is written once as a 16/8-byte vector.
+// The op-level ngram_causal_conv takes U itself and computes the row norms in
+// step 1 instead.
+#include "internal.h"
+
+namespace ngram {
+namespace {
+
+constexpr int kMaxTile = 64;
+constexpr int kMaxHalo = 3 * NGRAM_MAX_ORDER;
+
+__device__ __forceinline__ float4 f4(float x) { return make_float4(x, x, x, x); }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ float4 fma4(float4 a, float4 b, float4 c) {
+  return make_float4(fmaf(a.x, b.x, c.x), fmaf(a.y, b.y, c.y), fmaf(a.z, b.z, c.z), fmaf(a.w, b.w, c.w));
+}
+__device__ __forceinline__ float silu(float c) { return c / (1.0f + expf(-c)); }
+
+// Gate of branch br from the projection's row partials (layout
+// [3*nb+1][np]: dot, sum k^2, sum h^2 per branch, then sum v^2).
+__device__ __forceinline__ float gate_from_parts(const float* __restrict__ pr, int br, int np,
+                                                 int d, float eps) {
+  float dot = 0.0f, kk = 0.0f, hh = 0.0f;
+  for (int p = 0; p < np; ++p) {
+    dot += pr[(3 * br) * np + p];
+    kk += pr[(3 * br + 1) * np + p];
+    hh += pr[(3 * br + 2) * np + p];
+  }
+  const float fd = (float)d;
+  const float z = dot / (sqrtf(hh / fd + eps) * sqrtf(kk / fd + eps) * sqrtf(fd));
+  return 1.0f / (1.0f + expf(-z));
+}
+
+__device__ __forceinline__ float sum_parts(const float* __restrict__ pr, int np) {
+  float s = 0.0f;
+  for (int p = 0; p < np; ++p) s += pr[p];
+  return s;
+}
+
+// ngram_gate: gates and U = g V in the activation dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_values_kernel(ConvArgs a, int64_t M) {
+  __shared__ float s_alpha[NGRAM_MAX_BRANCHES];
+  const int64_t tok = blockIdx.x;
+  if (tok >= M) return;
+  const int nq = 3 * a.nb + 1;
+  const float* pr = a.parts + tok * nq * a.np;
+  if (threadIdx.x < a.nb) {
+    const float al = gate_from_parts(pr, threadIdx.x, a.np, a.d, a.eps);
+    s_alpha[threadIdx.x] = al;
+    if (a.gates) a.gates[tok * a.nb + threadIdx.x] = al;
+  }
+  __syncthreads();
+  T* out = static_cast<T*>(a.out);
+  if (out == nullptr) return;
+  const float* v = a.v + tok * a.v_stride;
+  for (int c = threadIdx.x * 4; c < a.d; c += blockDim.x * 4) {
+    const float4 vv = *reinterpret_cast<const float4*>(v + c);
+    for (int br = 0; br < a.nb; ++br)
+      Elem<T>::store4(out, (tok * a.nb + br) * a.d + c, mul4(f4(s_alpha[br]), vv));
+  }
+}
+
+// FUSED: source is fp32 V + partials (U = g V); else the act-dtype U rows.
+template <int DIL, typename T, bool FUSED>
+__global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
+  constexpr int HALO = 3 * DIL;
+  constexpr int R = HALO + 1;
+  __shared__ float s_alpha[kMaxTile + kMaxHalo];
+  __shared__ float s_scale[kMaxTile + kMaxHalo];
+
+  const int tiles = (a.T + a.tile - 1) / a.tile;
+  const int b = blockIdx.x / tiles;
+  const int p0 = (blockIdx.x - b * tiles) * a.tile;
+  const int p1 = min(p0 + a.tile, a.T);
+  const int br = blockIdx.y;
+  const int qs = p0 - HALO;
+  const int L = p1 - qs;
+  const int nb = a.nb, d = a.d;
+  const int64_t seq0 = (int64_t)b * a.T;
+
+  // ---- step 1: per-position scalars
+  if (FUSED) {
+    const int nq = 3 * nb + 1;
+    for (int i = threadIdx.x; i < L; i += blockDim.x) {
+      const int q = qs + i;
+      float al = 0.0f, sc = 0.0f;
+      if (q >= 0) {
+        const int64_t tok = seq0 + q;
+        const float* pr = a.parts + tok * nq * a.np;
+        al = gate_from_parts(pr, br, a.np, d, a.eps);
+        const float mv = sum_parts(pr + 3 * nb * a.np, a.np) / (float)d;
+        sc = al / sqrtf(al * al * mv + a.eps);
+        if (a.gates && q >= p0) a.gates[tok * nb + br] = al;
+      }
+      s_alpha[i] = al;
+      s_scale[i] = sc;
+    }
+  } else {
+    const T* U = static_cast<const T*>(a.u);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int i = wave; i < L; i += nw) {
+      const int q = qs + i;
+      float sc = 0.0f;
+      if (q >= 0) {
+        const T* row = U + ((seq0 + q) * nb + br) * d;
+        float ss = 0.0f;
+        for (int c = lane * 4; c < d; c += 256) {
+          const float4 x = Elem<T>::load4(row, c);
+          ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        sc = 1.0f / sqrtf(ss / (float)d + a.eps);
+      }
+      if (lane == 0) {
+        s_alpha[i] = 1.0f;
+        s_scale[i] = sc;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- step 2: walk the positions, 4 columns per thread
+  const T* __restrict__ CW = static_cast<const T*>(a.conv_w);
+  const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
+  T* __restrict__ OUT = static_cast<T*>(a.out);
+  const T* __restrict__ H = static_cast<const T*>(a.hidden);
+  for (int c0 = threadIdx.x * 4; c0 < d; c0 += blockDim.x * 4) {
+    const float4 w0 = Elem<T>::load4(CW, c0);
+    const float4 w1 = Elem<T>::load4(CW, d + c0);
+    const float4 w2 = Elem<T>::load4(CW, 2 * d + c0);
+    const float4 w3 = Elem<T>::load4(CW, 3 * d + c0);
+    const float4 gu = GU ? Elem<T>::load4(GU, c0) : f4(1.0f);
+    float4 ring[R];
+    for (int base = 0; base < L; base += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int i = base + u;
+        if (i < L) {
+          const int q = qs + i;
+          float4 src = f4(0.0f), nq = f4(0.0f);
+          if (q >= 0) {
+            if (FUSED) {
+              src = *reinterpret_cast<const float4*>(a.v + (seq0 + q) * a.v_stride + c0);
+            } else {
+              src = Elem<T>::load4(static_cast<const T*>(a.u), ((seq0 + q) * nb + br) * d + c0);
+            }
+            nq = mul4(mul4(gu, src), f4(s_scale[i]));
+          } else if (a.state) {
+            nq = *reinterpret_cast<const float4*>(
+                a.state + (((int64_t)b * HALO + HALO + q) * nb + br) * d + c0);
+          }
+          ring[u] = nq;
+          if (q >= p0) {
+            float4 C = mul4(w0, ring[u]);
+            C = fma4(w1, ring[(u - DIL + R) % R], C);
+            C = fma4(w2, ring[(u - 2 * DIL + R) % R], C);
+            C = fma4(w3, ring[(u - 3 * DIL + R) % R], C);
+            const float g = FUSED ? s_alpha[i] : 1.0f;
+            float4 D = make_float4(fmaf(g, src.x, silu(C.x)), fmaf(g, src.y, silu(C.y)),
+                                   fmaf(g, src.z, silu(C.z)), fmaf(g, src.w, silu(C.w)));
+            const int64_t tok = seq0 + q;
+            if (FUSED && a.add_residual) {
+              const float4 h = Elem<T>::load4(H, tok * a.h_tok_stride + br * a.h_branch_stride + c0);
+              D = make_float4(D.x + h.x, D.y + h.y, D.z + h.z, D.w + h.w);
+            }
+            Elem<T>::store4(OUT, (tok * nb + br) * d + c0, D);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename T, bool FUSED>
+hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
+  const int tiles = (a.T + a.tile - 1) / a.tile;
+  dim3 grid((unsigned)((int64_t)a.B * tiles), (unsigned)a.nb);
+  switch (dil) {
+    case 1: conv_kernel<1, T, FUSED><<<grid, 256, 0, s>>>(a); break;
+    case 2: conv_kernel<2, T, FUSED><<<grid, 256, 0, s>>>(a); break;
+    case 3: conv_kernel<3, T, FUSED><<<grid, 256, 0, s>>>(a); break;
+    case 4: conv_kernel<4, T, FUSED><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_values(int dtype, const ConvArgs& a, int64_t M, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (dtype == NGRAM_BF16)
+    gate_values_kernel<bf16_bits><<<(unsigned)M, 256, 0, s>>>(a, M);
+  else
+    gate_values_kernel<float><<<(unsigned)M, 256, 0, s>>>(a, M);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.T == 0) return hipSuccess;
+  return dtype == NGRAM_BF16 ? launch_conv_t<bf16_bits, true>(dil, a, s)
+                             : launch_conv_t<float, true>(dil, a, s);
+}
+
+hipError_t launch_op_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.T == 0) return hipSuccess;
+  return dtype == NGRAM_BF16 ? launch_conv_t<bf16_bits, false>(dil, a, s)
+                             : launch_conv_t<float, false>(dil, a, s);
+}
+
+int conv_tile_for(int32_t T) { return T < kMaxTile ? T : kMaxTile; }
+
+}  // namespace ngram

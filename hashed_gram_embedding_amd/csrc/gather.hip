@@ -1,0 +1,74 @@
+// Gather + concatenation of the hashed rows into the memory vector E_t
+// ("Qwen3.8-Flash-Next 深度研究" §2.3: the row ids' rows are concatenated into
+// E_t; Engram's second component in "Qwen 4用上DeepSeek的Engram").
+//
+// HBM-bound random reads.  One wavefront owns one token: its n_tables rows
+// are split into 16-byte chunks, lane l takes chunks l, l+64, ..., so a
+// 640-byte row (320 bf16) is read as five aligned 128-byte lines by 40
+// consecutive lanes, and the concatenated E_t row is written with fully
+// coalesced 16-byte stores.  All of a token's loads are issued before its
+// stores (up to 8 chunks per lane in flight) to keep enough random row
+// fetches outstanding; the table base pointers sit in LDS because the lanes
+// of one wave touch different tables.
+#include "internal.h"
+
+namespace ngram {
+namespace {
+
+constexpr int kGatherUnroll = 8;
+
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ row_idx,
+                                                     int64_t n_tok, int32_t n_tables,
+                                                     int32_t row_chunks, TablePtrs tabs,
+                                                     uint4* __restrict__ mem) {
+  __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
+  if (threadIdx.x < NGRAM_MAX_TABLES)
+    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[threadIdx.x < n_tables ? threadIdx.x : 0]);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int waves_per_block = blockDim.x >> 6;
+  const int64_t wave0 = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6);
+  const int64_t wstride = (int64_t)gridDim.x * waves_per_block;
+  const int32_t chunks = n_tables * row_chunks;  // 16-byte chunks per token
+
+  for (int64_t tok = wave0; tok < n_tok; tok += wstride) {
+    const int32_t* rix = row_idx + tok * n_tables;
+    uint4* dst = mem + tok * chunks;
+    for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
+      uint4 v[kGatherUnroll];
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const int q = base + u * 64 + lane;
+        if (q < chunks) {
+          const int j = q / row_chunks;
+          const int c = q - j * row_chunks;
+          const int64_t r = rix[j];
+          v[u] = s_tab[j][r * row_chunks + c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const int q = base + u * 64 + lane;
+        if (q < chunks) dst[q] = v[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
+                         int32_t row_dim, const TablePtrs& t, void* mem, hipStream_t s) {
+  const int esize = dtype == NGRAM_BF16 ? 2 : 4;
+  const int32_t row_chunks = row_dim * esize / 16;
+  const int threads = 256;
+  int64_t blocks = (n_tok + 3) / 4;
+  if (blocks > 262144) blocks = 262144;
+  if (blocks < 1) blocks = 1;
+  gather_kernel<<<(unsigned)blocks, threads, 0, s>>>(row_idx, n_tok, n_tables, row_chunks, t,
+                                                     static_cast<uint4*>(mem));
+  return hipGetLastError();
+}
+
+}  // namespace ngram

@@ -1,0 +1,140 @@
+// Internal declarations shared by the kernel sources of libngram.so.
+// Not installed; the public interface is include/ngram.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ngram.h"
+
+namespace ngram {
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_bits;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) return (b >> 16) | 0x40u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static float4 load4(const float* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(p + i);
+  }
+  __device__ __forceinline__ static void store4(float* p, int64_t i, float4 v) {
+    *reinterpret_cast<float4*>(p + i) = v;
+  }
+};
+template <>
+struct Elem<bf16_bits> {
+  __device__ __forceinline__ static float load(const bf16_bits* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ __forceinline__ static float4 load4(const bf16_bits* p, int64_t i) {
+    uint2 r = *reinterpret_cast<const uint2*>(p + i);
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+  }
+  __device__ __forceinline__ static void store4(bf16_bits* p, int64_t i, float4 v) {
+    uint2 r;
+    r.x = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+    r.y = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+    *reinterpret_cast<uint2*>(p + i) = r;
+  }
+};
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// kernel argument blocks (passed by value)
+// ---------------------------------------------------------------------------
+struct HashArgs {
+  int32_t n_orders, heads, n_tables, max_order;
+  int32_t pad_id, vocab, vocab_c, hist_len;
+  int32_t orders[NGRAM_MAX_ORDER];
+  uint64_t rows[NGRAM_MAX_TABLES];
+  uint64_t mult[NGRAM_MAX_TABLES][NGRAM_MAX_ORDER];
+};
+
+struct TablePtrs {
+  const void* p[NGRAM_MAX_TABLES];
+};
+
+// Projection + gate-partials problem (one launch covers all segments: the
+// n_branches key projections, then the value projection).
+struct ProjArgs {
+  const void* e;          // [M, K] table dtype
+  const void* wk;         // [nb, K, d]
+  const void* wv;         // [K, d]
+  const void* hidden;     // act dtype
+  int64_t h_tok_stride;   // elements
+  int64_t h_branch_stride;
+  const void* gamma_q;    // [d] nullable
+  const void* gamma_k;    // [d] nullable
+  float* v;               // [M, d] fp32 (bf16 path) / [M, nb+1, d] (fp32 path)
+  float* parts;           // [M, 3*nb+1, np] fp32
+  int64_t M;
+  int32_t K, d, nb, np;
+};
+
+// Gate + gated value + conv block over a [B, T] token grid.
+struct ConvArgs {
+  // value source: fused path reads fp32 V and gate partials; the op path
+  // reads U rows of the act dtype.
+  const float* v;         // fused: [M, v_stride]
+  int64_t v_stride;
+  const float* parts;     // fused: [M, 3*nb+1, np]
+  int32_t np;
+  const void* u;          // op: [M, nb, d] act dtype
+  const void* conv_w;     // [4, d] act dtype
+  const void* gamma_u;    // [d] nullable
+  const float* state;     // [B, 3*dil, nb, d] nullable
+  const void* hidden;     // residual source (flag)
+  int64_t h_tok_stride, h_branch_stride;
+  void* out;              // [M, nb, d] act dtype
+  float* gates;           // [M, nb] nullable
+  int32_t B, T, nb, d, tile;
+  float eps;
+  int32_t add_residual;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_compress(const int32_t* raw, int64_t n, const int32_t* lut, int32_t vocab,
+                           int32_t vocab_c, int32_t pad_id, int32_t* comp, int32_t* err,
+                           hipStream_t s);
+hipError_t launch_hash(bool raw_input, const int32_t* ids, int32_t B, int32_t T,
+                       const int32_t* hist, const int32_t* lut, const HashArgs& a,
+                       int32_t* row_idx, int32_t* err, hipStream_t s);
+hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
+                         int32_t row_dim, const TablePtrs& t, void* mem, hipStream_t s);
+
+// Projection tile shape picked for M tokens (bf16 path); np = partials per row.
+struct ProjPlan {
+  int bm, bn, np;
+};
+ProjPlan plan_projection(int dtype, int64_t M, int32_t d);
+hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a, hipStream_t s);
+
+hipError_t launch_gate_values(int dtype, const ConvArgs& a, int64_t M, hipStream_t s);
+hipError_t launch_fused_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s);
+hipError_t launch_op_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s);
+int conv_tile_for(int32_t T);
+
+}  // namespace ngram

@@ -1,0 +1,239 @@
+"""Thin ctypes binding of ``libngram.so`` (declared in ``include/ngram.h``).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: torch CUDA tensors become device pointers, the current torch
+stream becomes the HIP stream, and a negative status raises ``NgramError``.
+Every step of the layer runs in the library's HIP kernels; there is no other
+code path.  If the library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+MAX_TABLES = 16
+MAX_ORDER = 4
+MAX_BRANCHES = 4
+ADD_RESIDUAL = 1
+F32, BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libngram.so")
+
+
+class NgramError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class NgramConfig(ctypes.Structure):
+    """Mirror of ``ngram_config`` (include/ngram.h)."""
+    _fields_ = [
+        ("n_orders", ctypes.c_int32),
+        ("orders", ctypes.c_int32 * MAX_ORDER),
+        ("heads_per_order", ctypes.c_int32),
+        ("n_tables", ctypes.c_int32),
+        ("rows", ctypes.c_int64 * MAX_TABLES),
+        ("hash_mult", (ctypes.c_uint64 * MAX_ORDER) * MAX_TABLES),
+        ("row_dim", ctypes.c_int32),
+        ("mem_dim", ctypes.c_int32),
+        ("hidden_dim", ctypes.c_int32),
+        ("n_branches", ctypes.c_int32),
+        ("conv_kernel", ctypes.c_int32),
+        ("conv_dilation", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("vocab_compressed", ctypes.c_int32),
+        ("pad_id", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("table_dtype", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+    ]
+
+
+def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_mult,
+                row_dim: int, hidden_dim: int, n_branches: int, vocab: int,
+                vocab_compressed: int, dtype: int, pad_id: int = 0, rms_eps: float = 1e-6,
+                conv_kernel: int = 4, conv_dilation: Optional[int] = None) -> NgramConfig:
+    """Fill an NgramConfig; ``hash_mult`` is indexable as [table][slot]."""
+    c = NgramConfig()
+    c.n_orders = len(orders)
+    for i, o in enumerate(orders):
+        c.orders[i] = int(o)
+    c.heads_per_order = heads
+    c.n_tables = len(orders) * heads
+    for j, r in enumerate(rows):
+        c.rows[j] = int(r)
+    for j in range(min(len(hash_mult), MAX_TABLES)):
+        for i in range(MAX_ORDER):
+            c.hash_mult[j][i] = int(hash_mult[j][i])
+    c.row_dim = row_dim
+    c.mem_dim = c.n_tables * row_dim
+    c.hidden_dim = hidden_dim
+    c.n_branches = n_branches
+    c.conv_kernel = conv_kernel
+    c.conv_dilation = max(orders) if conv_dilation is None else conv_dilation
+    c.vocab = vocab
+    c.vocab_compressed = vocab_compressed
+    c.pad_id = pad_id
+    c.rms_eps = rms_eps
+    c.table_dtype = dtype
+    c.act_dtype = dtype
+    return c
+
+
+_lib = None
+_p, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_cfgp = ctypes.POINTER(NgramConfig)
+
+_SIGS = {
+    "ngram_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "ngram_abi_version": (ctypes.c_int, []),
+    "ngram_config_validate": (ctypes.c_int, [_cfgp]),
+    "ngram_compress_ids": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p]),
+    "ngram_hash": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p]),
+    "ngram_gather": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p]),
+    "ngram_gate_workspace_size": (_sz, [_cfgp, _i64]),
+    "ngram_gate": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]),
+    "ngram_causal_conv": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _p]),
+    "ngram_forward_workspace_size": (_sz, [_cfgp, _i32, _i32]),
+    "ngram_forward": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p,
+                                     _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().ngram_status_str(status).decode()
+
+
+def abi_version() -> int:
+    return lib().ngram_abi_version()
+
+
+def ngram_config_validate(cfg: NgramConfig) -> int:
+    return lib().ngram_config_validate(ctypes.byref(cfg))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libngram must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise NgramError(status, where)
+
+
+def _table_array(tables):
+    arr = (ctypes.c_void_p * MAX_TABLES)()
+    for j, t in enumerate(tables):
+        arr[j] = t if isinstance(t, int) else (t.data_ptr() if t is not None else None)
+    return arr
+
+
+def _workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def ngram_compress_ids(cfg, raw_ids, lut, comp_ids, err_flag=None, stream=None):
+    _check(lib().ngram_compress_ids(ctypes.byref(cfg), _ptr(raw_ids), raw_ids.numel(), _ptr(lut),
+                                    _ptr(comp_ids), _ptr(err_flag), _stream(stream)),
+           "ngram_compress_ids")
+    return comp_ids
+
+
+def ngram_hash(cfg, comp_ids, row_idx, history=None, stream=None):
+    B, T = comp_ids.shape
+    _check(lib().ngram_hash(ctypes.byref(cfg), _ptr(comp_ids), B, T, _ptr(history),
+                            _ptr(row_idx), _stream(stream)), "ngram_hash")
+    return row_idx
+
+
+def ngram_gather(cfg, row_idx, tables, mem, stream=None):
+    n_tok = row_idx.numel() // cfg.n_tables
+    _check(lib().ngram_gather(ctypes.byref(cfg), _ptr(row_idx), n_tok, _table_array(tables),
+                              _ptr(mem), _stream(stream)), "ngram_gather")
+    return mem
+
+
+def ngram_gate_workspace_size(cfg, n_tok: int) -> int:
+    return int(lib().ngram_gate_workspace_size(ctypes.byref(cfg), n_tok))
+
+
+def ngram_gate(cfg, hidden, hidden_branch_stride, mem, w_k, w_v, gates, u=None, gamma_q=None,
+               gamma_k=None, workspace=None, stream=None):
+    n_tok = mem.shape[0]
+    need = ngram_gate_workspace_size(cfg, n_tok)
+    if workspace is None:
+        workspace = _workspace(need, mem.device)
+    _check(lib().ngram_gate(ctypes.byref(cfg), _ptr(hidden), hidden_branch_stride, _ptr(mem),
+                            _ptr(w_k), _ptr(w_v), _ptr(gamma_q), _ptr(gamma_k), n_tok,
+                            _ptr(gates), _ptr(u), _ptr(workspace), workspace.numel(),
+                            _stream(stream)), "ngram_gate")
+    return gates, u
+
+
+def ngram_causal_conv(cfg, u, B: int, T: int, conv_w, out, gamma_u=None, conv_state=None,
+                      stream=None):
+    _check(lib().ngram_causal_conv(ctypes.byref(cfg), _ptr(u), B, T, _ptr(conv_w), _ptr(gamma_u),
+                                   _ptr(conv_state), _ptr(out), _stream(stream)),
+           "ngram_causal_conv")
+    return out
+
+
+def ngram_forward_workspace_size(cfg, B: int, T: int) -> int:
+    return int(lib().ngram_forward_workspace_size(ctypes.byref(cfg), B, T))
+
+
+def ngram_forward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w, out,
+                  history=None, gamma_q=None, gamma_k=None, gamma_u=None, conv_state=None,
+                  flags: int = 0, gates=None, err_flag=None, workspace=None, stream=None):
+    B, T = raw_ids.shape
+    if workspace is None:
+        workspace = _workspace(ngram_forward_workspace_size(cfg, B, T), raw_ids.device)
+    _check(lib().ngram_forward(ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history), _ptr(lut),
+                               _table_array(tables), _ptr(hidden), hidden_branch_stride, _ptr(w_k),
+                               _ptr(w_v), _ptr(conv_w), _ptr(gamma_q), _ptr(gamma_k),
+                               _ptr(gamma_u), _ptr(conv_state), flags, _ptr(out), _ptr(gates),
+                               _ptr(err_flag), _ptr(workspace), workspace.numel(),
+                               _stream(stream)), "ngram_forward")
+    return out

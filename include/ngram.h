@@ -1,0 +1,226 @@
+/*
+ * ngram.h -- C-ABI of libngram.so, the hashed N-gram embedding layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (Engram-style "N-gram Embedding"), per token t of a sequence:
+ *   1. c_t = LUT[x_t]                                   tokenizer compression
+ *   2. 2-gram key (c_{t-1}, c_t), 3-gram key (c_{t-2}, c_{t-1}, c_t)
+ *   3. each key hashed by K independent heads into prime-sized tables
+ *   4. E_t = concatenation of the gathered rows         memory vector
+ *   5. K_t = E_t W_K (one per branch), V_t = E_t W_V (shared)
+ *   6. g_t = sigmoid( RMSNorm(h_t) . RMSNorm(K_t) / sqrt(d) )   one per branch
+ *   7. U_t = g_t V_t
+ *   8. Delta_t = U_t + SiLU( DWConv_{kernel 4, dilation = max order}( RMSNorm(U) )_t )
+ * Sources: "Qwen 4用上DeepSeek的Engram！125B MoE一张4090能跑不用量化"
+ * (yktysq.com), section "DeepSeek Engram 更复杂，Qwen 更精简" (the four
+ * components and multi-branch integration), and "Qwen3.8-Flash-Next 深度研究"
+ * (zhichai.net), §2.3 "Embedding：N-gram Embedding" (lookup rule and the
+ * layer formula E_t -> K_t, V_t; g_t; U_t; Delta_t).
+ *
+ * Conventions for every entry point
+ *  - Device pointers are borrowed for the stream-ordered duration of the call;
+ *    the caller owns every buffer.  The library allocates no device memory:
+ *    scratch comes from the caller's workspace.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream), never synchronises, keeps no state between calls and is
+ *    reentrant.
+ *  - All arrays are dense row-major.  Device pointers must be 16-byte aligned.
+ *  - Arguments are validated on the host before any launch; a failed check
+ *    returns a negative ngram_status and launches nothing.  A failed launch
+ *    returns NGRAM_EHIP.  Empty inputs (zero tokens) return NGRAM_OK at once.
+ *  - Invalid token ids (outside [0, vocab), or whose LUT entry lies outside
+ *    [0, vocab_compressed)) are data errors found on the device: the token is
+ *    treated as pad_id and, if err_flag is non-NULL, *err_flag is set to 1
+ *    (never cleared by the library).
+ *  - Floating point: storage is fp32 or bf16 (ngram_dtype); all arithmetic is
+ *    fp32 with fp32 accumulation (MFMA for bf16 projections); outputs are
+ *    rounded to the storage type to nearest-even.  Gates are always fp32.
+ */
+#ifndef NGRAM_H
+#define NGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NGRAM_MAX_TABLES 16
+#define NGRAM_MAX_ORDER 4
+#define NGRAM_MAX_BRANCHES 4
+
+/* flags for ngram_forward */
+#define NGRAM_ADD_RESIDUAL 1 /* out = hidden (the branch's query row) + Delta */
+
+typedef enum ngram_status {
+  NGRAM_OK = 0,
+  NGRAM_EINVAL = -1,     /* NULL pointer or inconsistent configuration */
+  NGRAM_ESHAPE = -2,     /* a size is out of range or not a supported multiple */
+  NGRAM_EDTYPE = -3,     /* unsupported dtype or dtype combination */
+  NGRAM_EALIGN = -4,     /* a device pointer is not 16-byte aligned */
+  NGRAM_ERANGE = -5,     /* a table row count is not prime / too large, ids out of range */
+  NGRAM_EHIP = -6,       /* a HIP launch failed */
+  NGRAM_EWORKSPACE = -7  /* workspace missing or smaller than required */
+} ngram_status;
+
+typedef enum ngram_dtype { NGRAM_F32 = 0, NGRAM_BF16 = 1 } ngram_dtype;
+
+/*
+ * Layer configuration (host memory, read during the call only).
+ *
+ * Tables: table j = o * heads_per_order + k holds the rows of head k of order
+ * orders[o] (orders ascending, so 2-gram tables come first).  For the token at
+ * position t its row is
+ *     key = XOR_{i=0}^{n-1} ( (uint64)c_{t-i} * hash_mult[j][i] )   (mod 2^64)
+ *     row = key mod rows[j]
+ * with n = orders[o]; c_{t-i} for t-i < 0 comes from the history if given,
+ * else pad_id.  The pages name only "deterministic hashing by K independent
+ * heads into prime-sized tables" and a "mod hash"; this multiply-xor-mod form
+ * is the library's reading, the multipliers being parameters of the model.
+ */
+typedef struct ngram_config {
+  int32_t n_orders;                                      /* 1..NGRAM_MAX_ORDER */
+  int32_t orders[NGRAM_MAX_ORDER];                       /* strictly ascending, 1..4 */
+  int32_t heads_per_order;                               /* K >= 1 */
+  int32_t n_tables;                                      /* == n_orders * K <= 16 */
+  int64_t rows[NGRAM_MAX_TABLES];                        /* prime, < 2^31 */
+  uint64_t hash_mult[NGRAM_MAX_TABLES][NGRAM_MAX_ORDER]; /* slot i used for i < order */
+  int32_t row_dim;                                       /* values per table row */
+  int32_t mem_dim;                                       /* == n_tables * row_dim */
+  int32_t hidden_dim;                                    /* d */
+  int32_t n_branches;                                    /* 1..NGRAM_MAX_BRANCHES */
+  int32_t conv_kernel;                                   /* 4 */
+  int32_t conv_dilation;                                 /* == orders[n_orders - 1] */
+  int32_t vocab;                                         /* raw ids in [0, vocab) */
+  int32_t vocab_compressed;                              /* LUT image in [0, vocab_compressed) */
+  int32_t pad_id;                                        /* in [0, vocab_compressed) */
+  float rms_eps;                                         /* >= 0, RMSNorm epsilon */
+  int32_t table_dtype;                                   /* ngram_dtype */
+  int32_t act_dtype;                                     /* ngram_dtype, == table_dtype */
+} ngram_config;
+
+/* Human-readable name of a status code (static string). */
+const char* ngram_status_str(int status);
+
+/* Library ABI version: increments whenever a signature or layout changes. */
+int ngram_abi_version(void);
+
+/*
+ * Check a configuration without touching the GPU.  Returns NGRAM_OK or the
+ * first failing status.  Shape rules: row_dim * sizeof(table dtype) must be a
+ * multiple of 16 bytes; for bf16, mem_dim % 64 == 0 and hidden_dim % 32 == 0;
+ * for fp32, hidden_dim % 4 == 0.  conv_kernel must be 4 (the pages' kernel)
+ * and conv_dilation the largest order.
+ */
+int ngram_config_validate(const ngram_config* cfg);
+
+/*
+ * Tokenizer compression -- Engram's first component ("Qwen 4用上DeepSeek的
+ * Engram", section "DeepSeek Engram 更复杂，Qwen 更精简"): comp_ids[i] =
+ * lut[raw_ids[i]].
+ *   raw_ids  device int32[n]
+ *   lut      device int32[vocab]
+ *   comp_ids device int32[n] (output)
+ *   err_flag device int32, nullable: set to 1 on an invalid id
+ */
+int ngram_compress_ids(const ngram_config* cfg, const int32_t* raw_ids, int64_t n,
+                       const int32_t* lut, int32_t* comp_ids, int32_t* err_flag, void* stream);
+
+/*
+ * N-gram keys and multi-head hashing -- Engram's second component and the
+ * lookup rule of "Qwen3.8-Flash-Next 深度研究" §2.3 (2-gram heads on
+ * (x_{t-1}, x_t), 3-gram heads on (x_{t-2}, x_{t-1}, x_t)).
+ *   comp_ids device int32[B, T] compressed ids (output of ngram_compress_ids)
+ *   history  device int32[B, max_order - 1] compressed ids before position 0,
+ *            oldest first; NULL = pad_id
+ *   row_idx  device int32[B, T, n_tables] (output): row of table j for token t
+ * Compressed ids are not range-checked here (ngram_compress_ids does that).
+ */
+int ngram_hash(const ngram_config* cfg, const int32_t* comp_ids, int32_t B, int32_t T,
+               const int32_t* history, int32_t* row_idx, void* stream);
+
+/*
+ * Gather and concatenation into the memory vector E_t (§2.3 "每行 160 个值，
+ * 拼接成 E_t"): mem[t, j*row_dim + c] = tables[j][row_idx[t, j], c].  An exact
+ * copy.
+ *   row_idx  device int32[n_tok, n_tables]; each entry must be < rows[j]
+ *   tables   HOST array of n_tables device pointers, table j is
+ *            [rows[j], row_dim] of table_dtype
+ *   mem      device [n_tok, mem_dim] of table_dtype (output)
+ */
+int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
+                 const void* const* tables, void* mem, void* stream);
+
+/*
+ * Context-aware gating -- Engram's third component and §2.3's
+ * g_t = Gate(Norm(Q_t), Norm(K_t)), U_t = g_t (.) V_t:
+ *   K^(b) = E W_K^(b), V = E W_V (fp32 accumulate), the query h^(b) is the
+ *   hidden state, g = sigmoid( sum(gamma_q h/rms(h) * gamma_k K/rms(K)) / sqrt(d) )
+ *   with rms(x) = sqrt(mean(x^2) + rms_eps); U^(b) = g^(b) V.
+ *   hidden   device [n_tok, nbh, d] act_dtype with hidden_branch_stride == 0
+ *            (nbh = 1: one query row shared by all branches) or == d
+ *            (nbh = n_branches: one query row per branch)
+ *   mem      device [n_tok, mem_dim] table_dtype (E)
+ *   w_k      device [n_branches, mem_dim, d] act_dtype; w_v [mem_dim, d]
+ *   gamma_q, gamma_k  device [d] act_dtype, nullable (= 1)
+ *   gates    device float[n_tok, n_branches] (output)
+ *   u        device [n_tok, n_branches, d] act_dtype (output), nullable
+ *   workspace device scratch of at least ngram_gate_workspace_size() bytes
+ */
+size_t ngram_gate_workspace_size(const ngram_config* cfg, int64_t n_tok);
+int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branch_stride,
+               const void* mem, const void* w_k, const void* w_v, const void* gamma_q,
+               const void* gamma_k, int64_t n_tok, float* gates, void* u, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/*
+ * Convolution block -- Engram's fourth component (kernel 4, dilation = the
+ * largest n-gram order, depthwise, causal) and §2.3's
+ * Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))):
+ *   N_t = gamma_u (.) U_t / rms(U_t) per branch;  C_t = sum_i conv_w[i] (.) N_{t - i*dil}
+ *   (zero before position 0 unless conv_state is given);  Delta_t = U_t + C_t sigmoid(C_t)
+ *   u          device [B, T, n_branches, d] act_dtype
+ *   conv_w     device [conv_kernel, d] act_dtype; tap i multiplies position t - i*dil
+ *   gamma_u    device [d] act_dtype, nullable (= 1)
+ *   conv_state device float[B, (conv_kernel-1)*dil, n_branches, d] normalised rows
+ *              N for positions -(k-1)*dil .. -1 (last row = position -1), nullable
+ *   out        device [B, T, n_branches, d] act_dtype (output)
+ */
+int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t T,
+                      const void* conv_w, const void* gamma_u, const float* conv_state,
+                      void* out, void* stream);
+
+/*
+ * The whole layer in one call (steps 1-8 above), intermediates in fp32: K is
+ * never materialised, V and U stay fp32.
+ *   raw_ids   device int32[B, T]
+ *   history   device int32[B, max_order - 1] RAW ids before position 0 (oldest
+ *             first), compressed here; NULL = pad_id (decode passes the last
+ *             tokens of each sequence)
+ *   lut       device int32[vocab]
+ *   tables    HOST array of n_tables device pointers (see ngram_gather)
+ *   hidden, hidden_branch_stride, w_k, w_v, gamma_q, gamma_k: as ngram_gate,
+ *             hidden indexed by token b*T + t
+ *   conv_w, gamma_u, conv_state: as ngram_causal_conv
+ *   flags     0 or NGRAM_ADD_RESIDUAL
+ *   out       device [B, T, n_branches, d] act_dtype (output): Delta_t, or
+ *             hidden + Delta_t with NGRAM_ADD_RESIDUAL
+ *   gates     device float[B, T, n_branches] (output), nullable
+ *   err_flag  device int32, nullable (see conventions)
+ *   workspace device scratch of at least ngram_forward_workspace_size() bytes
+ */
+size_t ngram_forward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T);
+int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                  const int32_t* history, const int32_t* lut, const void* const* tables,
+                  const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                  const void* w_v, const void* conv_w, const void* gamma_q,
+                  const void* gamma_k, const void* gamma_u, const float* conv_state,
+                  int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NGRAM_H */

@@ -1,0 +1,204 @@
+"""Fused ngram_forward against the oracle: every workload at its full size in
+the launch configuration the benchmark uses, outputs compared on sampled
+windows (each with its 11-token context) or in full where the oracle is
+quick, plus edge cases (ragged and short sequences, history, conv state,
+residual flag, other order sets, invalid ids, empty batches)."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_support as G
+from synth import device as SD
+from synth import rng
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _device_inputs(w, ids, hist, random_gamma=False):
+    n = ids.size
+    d = dict(
+        ids=torch.from_numpy(ids).cuda(),
+        hist=None if hist is None else torch.from_numpy(hist).cuda(),
+        lut=torch.from_numpy(W.make_lut(w)).cuda(),
+        tables=G.tables(w),
+        hidden=SD.make_hidden(w, n),
+        conv_w=G.conv_w(w),
+        gam=G.gammas(w, random_gamma),
+    )
+    d["wk"], d["wv"] = G.weights(w)
+    return d
+
+
+def _run(w, inp, flags=0, conv_state=None):
+    H = G.H()
+    B, T = inp["ids"].shape
+    cfg = G.config(w)
+    out = torch.empty((B, T, w.n_branches, w.hidden), dtype=G.tdtype(w), device="cuda")
+    gates = torch.empty((B, T, w.n_branches), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hbs = 0 if w.n_branches == 1 else w.hidden
+    g = inp["gam"]
+    H.ngram_forward(cfg, inp["ids"], inp["lut"], inp["tables"], inp["hidden"], hbs, inp["wk"],
+                    inp["wv"], inp["conv_w"], out, history=inp["hist"], gamma_q=g["q"],
+                    gamma_k=g["k"], gamma_u=g["u"], conv_state=conv_state, flags=flags,
+                    gates=gates, err_flag=err)
+    torch.cuda.synchronize()
+    return out, gates, err.item()
+
+
+def _host_params(w, inp):
+    return G.to_storage(inp["wk"]), G.to_storage(inp["wv"]), W.conv_weight_values(w), \
+        {k: G.to_storage(v) for k, v in inp["gam"].items()}
+
+
+def _check_windows(orc, w, ids, hist, inp, out, gates, windows, flags=0, state=None):
+    wk, wv, cw, gam = _host_params(w, inp)
+    T = ids.shape[1]
+    for b, start, length in windows:
+        st = None if state is None or start > 0 else state[b:b + 1]
+        ref = G.oracle_forward_window(orc, w, ids, hist, b, start, length,
+                                      lambda toks: W.hidden_values(w, toks), wk, wv, cw, gam,
+                                      conv_state=st)
+        toks = b * T + np.arange(start, start + length)
+        got = G.to_f64(out.reshape(-1, w.n_branches, w.hidden)[torch.from_numpy(toks).cuda()])
+        want = ref["delta"]
+        if flags:
+            want = want + W.to_f64(W.hidden_values(w, toks), w.dtype)
+        e_out = G.rel_err(got, want)
+        e_gate = G.rel_err(gates.reshape(-1, w.n_branches)[torch.from_numpy(toks).cuda()].cpu().numpy(),
+                           ref["gate"])
+        print(f"   window b={b} [{start},{start + length}) rel_err out={e_out:.3e} gate={e_gate:.3e}")
+        assert e_out < G.TOL and e_gate < G.TOL, (b, start, e_out, e_gate)
+
+
+@pytest.mark.parametrize("random_gamma,flags", [(False, 0), (True, 1)])
+def test_forward_tiny_full(orc, random_gamma, flags):
+    w = W.get("tiny")
+    print(f"[forward] tiny gamma={random_gamma} flags={flags}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, random_gamma)
+    out, gates, err = _run(w, inp, flags)
+    assert err == 0
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, w.seq_len)], flags)
+
+
+def test_forward_engram_small(orc):
+    w = W.get("engram_small")
+    print("[forward] engram_small", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, random_gamma=True)
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    T = w.seq_len
+    _check_windows(orc, w, ids, hist, inp, out, gates,
+                   [(0, 0, 40), (0, 1000, 40), (7, 2049, 40), (7, T - 40, 40)])
+
+
+def test_forward_qwen_decode_full(orc):
+    w = W.get("qwen_decode")
+    print("[forward] qwen_decode", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist)
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    wk, wv, cw, gam = _host_params(w, inp)
+    ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
+                      w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
+                      W.hidden_values(w, np.arange(ids.size)), wk, wv, cw, w.dtype,
+                      gamma_q=gam["q"], gamma_k=gam["k"], gamma_u=gam["u"], eps=w.rms_eps)
+    e_out = G.rel_err(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"])
+    e_gate = G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"])
+    print(f"   decode rel_err out={e_out:.3e} gate={e_gate:.3e}")
+    assert e_out < G.TOL and e_gate < G.TOL
+
+
+def test_forward_qwen_decode_conv_state_and_residual(orc):
+    """A populated conv state (the last 9 normalised rows of each sequence)."""
+    w = W.get("qwen_decode").replace(batch=16)
+    print("[forward] qwen_decode state+residual", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist)
+    halo = 3 * w.max_order
+    state = rng.normal_f32(4242, np.arange(w.batch * halo * w.hidden), 1.0).reshape(
+        w.batch, halo, 1, w.hidden)
+    out, gates, err = _run(w, inp, flags=1, conv_state=torch.from_numpy(state).cuda())
+    assert err == 0
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, 1) for b in range(w.batch)],
+                   flags=1, state=state.astype(np.float64))
+
+
+def test_forward_qwen_prefill(orc):
+    w = W.get("qwen_prefill")
+    print("[forward] qwen_prefill 262144 tokens", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist)
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    T = w.seq_len
+    _check_windows(orc, w, ids, hist, inp, out, gates,
+                   [(0, 0, 24), (0, 7, 24), (0, 131071, 24), (0, T - 24, 24)])
+    assert bool(((gates > 0) & (gates < 1)).all())
+
+
+@pytest.mark.parametrize("name", ["qwen_multibranch_uniform", "qwen_multibranch_zipf13"])
+def test_forward_multibranch(orc, name):
+    w = W.get(name)
+    print(f"[forward] {name}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist)
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    T = w.seq_len
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 16), (9, 4000, 16), (15, T - 16, 16)])
+
+
+@pytest.mark.parametrize("B,T", [(3, 77), (4, 5), (1, 1), (2, 64), (1, 65)])
+def test_forward_ragged_and_short(orc, B, T):
+    w = W.get("tiny").replace(batch=B, seq_len=T)
+    print(f"[forward] tiny B={B} T={T}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, random_gamma=True)
+    out, gates, err = _run(w, inp)
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, T) for b in range(B)])
+
+
+@pytest.mark.parametrize("variant", ["orders234", "orders12_bf16", "order2_only"])
+def test_forward_other_order_sets(orc, variant):
+    """Dilation follows the largest order (4, 2, 2)."""
+    if variant == "orders234":
+        w = W.get("tiny").replace(orders=(2, 3, 4), explicit_rows=(), batch=2, seq_len=90)
+    elif variant == "orders12_bf16":
+        w = W.get("engram_small").replace(orders=(1, 2), heads=4, batch=2, seq_len=300,
+                                          hidden=256)
+    else:
+        w = W.get("tiny").replace(orders=(2,), heads=3, explicit_rows=(), batch=2, seq_len=50)
+    print(f"[forward] {variant}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist)
+    out, gates, err = _run(w, inp)
+    _check_windows(orc, w, ids, hist, inp, out, gates,
+                   [(b, 0, w.seq_len) for b in range(w.batch)])
+
+
+def test_forward_invalid_ids_are_pad(orc):
+    w = W.get("tiny").replace(batch=2, seq_len=40)
+    ids, hist = W.make_ids(w)
+    ids[0, 5] = -7
+    ids[1, 30] = w.vocab + 3
+    inp = _device_inputs(w, ids, hist)
+    out, gates, err = _run(w, inp)
+    assert err == 1
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 40), (1, 0, 40)])
+
+
+def test_forward_empty_batch():
+    H = G.H()
+    w = W.get("tiny")
+    cfg = G.config(w)
+    ids = torch.empty((0, 16), dtype=torch.int32, device="cuda")
+    inp = _device_inputs(w, np.zeros((1, 16), dtype=np.int32), None)
+    out = torch.empty((0, 16, 1, w.hidden), dtype=torch.float32, device="cuda")
+    H.ngram_forward(cfg, ids, inp["lut"], inp["tables"], inp["hidden"], 0, inp["wk"], inp["wv"],
+                    inp["conv_w"], out, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
