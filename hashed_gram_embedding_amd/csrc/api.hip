@@ -93,8 +93,18 @@ int validate(const ngram_config* c) {
   if (c->vocab < 1 || c->vocab_compressed < 1) return NGRAM_EINVAL;
   if (c->pad_id < 0 || c->pad_id >= c->vocab_compressed) return NGRAM_EINVAL;
   if (!(c->rms_eps >= 0.0f) || !isfinite(c->rms_eps)) return NGRAM_EINVAL;
+  if (c->w_layout != NGRAM_W_MEM_D && c->w_layout != NGRAM_W_D_MEM) return NGRAM_EINVAL;
+  if ((int64_t)c->hidden_dim * c->mem_dim >= (int64_t(1) << 31)) return NGRAM_ESHAPE;
   return NGRAM_OK;
 }
+
+// bf16 with W stored [d, mem]: operands copied global -> LDS (project_async).
+bool async_path(const ngram_config* c) {
+  return c->table_dtype == NGRAM_BF16 && c->w_layout == NGRAM_W_D_MEM;
+}
+// ... and the forward hashes and gathers inside the projection when every
+// 64-wide K step lies within one table row.
+bool fused_gather(const ngram_config* c) { return async_path(c) && c->row_dim % 64 == 0; }
 
 HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
   HashArgs a;
@@ -110,6 +120,7 @@ HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
   for (int o = 0; o < c->n_orders; ++o) a.orders[o] = c->orders[o];
   for (int j = 0; j < c->n_tables; ++j) {
     a.rows[j] = (uint64_t)c->rows[j];
+    a.magic[j] = (uint64_t)(((unsigned __int128)1 << 64) / (uint64_t)c->rows[j]);
     for (int i = 0; i < NGRAM_MAX_ORDER; ++i) a.mult[j][i] = c->hash_mult[j][i];
   }
   return a;
@@ -119,17 +130,25 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   size_t row_idx = 0, e = 0, v = 0, parts = 0, total = 0;
-  ProjPlan plan;
+  ProjPlan plan;       // plan.np is the number of partials per row on every path
+  int async = -1;      // async projection tile plan, -1 when not used
   int64_t v_stride = 0;  // fp32 elements between V rows
   int64_t v_offset = 0;  // fp32 elements from the V buffer to row 0's values
 };
 
-// with_memory: the forward pass also keeps the row ids and E in the workspace.
-Layout layout_for(const ngram_config* c, int64_t n_tok, bool with_memory) {
+// forward: the forward pass (row ids and E live in the workspace unless the
+// projection gathers them itself).
+Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward) {
   Layout L;
   const int dt = c->table_dtype;
   const int nb = c->n_branches, d = c->hidden_dim;
   L.plan = plan_projection(dt, n_tok, d);
+  if (async_path(c)) {
+    L.async = async_plan(n_tok);
+    const int wc = async_wave_cols(L.async);
+    L.plan.np = (d + wc - 1) / wc;
+  }
+  const bool with_memory = forward && !fused_gather(c);
   size_t off = 0;
   if (with_memory) {
     L.row_idx = off;
@@ -154,6 +173,14 @@ Layout layout_for(const ngram_config* c, int64_t n_tok, bool with_memory) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
+
+// Benchmark instrumentation (ngram_set_timing_events).
+hipEvent_t g_stage_events[NGRAM_N_STAGES + 1];
+bool g_stage_events_on = false;
+
+void mark_stage(int i, hipStream_t s) {
+  if (g_stage_events_on) (void)hipEventRecord(g_stage_events[i], s);
+}
 
 int check_tables(const ngram_config* c, const void* const* tables, TablePtrs* out) {
   if (tables == nullptr) return NGRAM_EINVAL;
@@ -191,7 +218,38 @@ ProjArgs proj_args(const ngram_config* c, const void* e, const void* w_k, const 
   a.d = c->hidden_dim;
   a.nb = c->n_branches;
   a.np = L.plan.np;
+  a.w_dk = c->w_layout == NGRAM_W_D_MEM;
   return a;
+}
+
+AsyncProjArgs async_args(const ngram_config* c, const ProjArgs& p) {
+  AsyncProjArgs a;
+  memset(&a, 0, sizeof a);
+  a.e = static_cast<const bf16_bits*>(p.e);
+  a.wk = static_cast<const bf16_bits*>(p.wk);
+  a.wv = static_cast<const bf16_bits*>(p.wv);
+  a.epi.hidden = static_cast<const bf16_bits*>(p.hidden);
+  a.epi.h_tok_stride = p.h_tok_stride;
+  a.epi.h_branch_stride = p.h_branch_stride;
+  a.epi.gamma_q = static_cast<const bf16_bits*>(p.gamma_q);
+  a.epi.gamma_k = static_cast<const bf16_bits*>(p.gamma_k);
+  a.epi.v = p.v;
+  a.epi.parts = p.parts;
+  a.epi.M = p.M;
+  a.epi.d = p.d;
+  a.epi.nb = p.nb;
+  a.epi.np = p.np;
+  a.K = p.K;
+  a.row_dim = c->row_dim;
+  a.group_m = 4;
+  return a;
+}
+
+// Launch the projection for E (or, with gather, for raw ids hashed in-kernel).
+hipError_t run_projection(const ngram_config* c, const Layout& L, const ProjArgs& p,
+                          hipStream_t s) {
+  if (L.async < 0) return launch_projection(c->table_dtype, L.plan, p, s);
+  return launch_projection_async(false, L.async, async_args(c, p), s);
 }
 
 ConvArgs conv_args_base(const ngram_config* c) {
@@ -224,6 +282,20 @@ const char* ngram_status_str(int status) {
 int ngram_abi_version(void) { return kAbiVersion; }
 
 int ngram_config_validate(const ngram_config* cfg) { return validate(cfg); }
+
+int ngram_set_timing_events(void* const* events, int n) {
+  if (n == 0) {
+    g_stage_events_on = false;
+    return NGRAM_OK;
+  }
+  if (n != NGRAM_N_STAGES + 1 || events == nullptr) return NGRAM_EINVAL;
+  for (int i = 0; i <= NGRAM_N_STAGES; ++i) {
+    if (events[i] == nullptr) return NGRAM_EINVAL;
+    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_stage_events_on = true;
+  return NGRAM_OK;
+}
 
 int ngram_compress_ids(const ngram_config* cfg, const int32_t* raw_ids, int64_t n,
                        const int32_t* lut, int32_t* comp_ids, int32_t* err_flag, void* stream) {
@@ -294,7 +366,7 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
   char* ws = static_cast<char*>(workspace);
   const ProjArgs pa = proj_args(cfg, mem, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
                                 gamma_k, ws, L, n_tok);
-  st = hip_status(launch_projection(cfg->table_dtype, L.plan, pa, s));
+  st = hip_status(run_projection(cfg, L, pa, s));
   if (st) return st;
   ConvArgs ca = conv_args_base(cfg);
   ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
@@ -370,15 +442,37 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   void* e = ws + L.e;
 
   const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
-  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
-  if (st) return st;
-  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim, tp,
-                                e, s));
-  if (st) return st;
   const ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
                                 gamma_k, ws, L, n_tok);
-  st = hip_status(launch_projection(cfg->table_dtype, L.plan, pa, s));
-  if (st) return st;
+  if (fused_gather(cfg)) {
+    // hash + gather + projection in one launch
+    AsyncProjArgs aa = async_args(cfg, pa);
+    aa.e = nullptr;
+    aa.ids = raw_ids;
+    aa.hist = history;
+    aa.lut = lut;
+    aa.err = err_flag;
+    aa.T = T;
+    aa.hash = ha;
+    aa.tabs = tp;
+    mark_stage(0, s);
+    mark_stage(1, s);
+    mark_stage(2, s);
+    st = hip_status(launch_projection_async(true, L.async, aa, s));
+    if (st) return st;
+  } else {
+    mark_stage(0, s);
+    st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
+    if (st) return st;
+    mark_stage(1, s);
+    st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim,
+                                  tp, e, s));
+    if (st) return st;
+    mark_stage(2, s);
+    st = hip_status(run_projection(cfg, L, pa, s));
+    if (st) return st;
+  }
+  mark_stage(3, s);
   ConvArgs ca = conv_args_base(cfg);
   ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
   ca.v_stride = L.v_stride;
@@ -396,7 +490,9 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   ca.T = T;
   ca.tile = conv_tile_for(T);
   ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
-  return hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+  st = hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+  mark_stage(NGRAM_N_STAGES, s);
+  return st;
 }
 
 }  // extern "C"

@@ -1,0 +1,145 @@
+// Epilogue of the projection kernels: turns a wave's 32x32-MFMA accumulator
+// tile into the gate's row partials (key segments) or fp32 V plus sum(v^2)
+// (value segment).  See project.hip for the layer context.
+#pragma once
+
+#include "internal.h"
+
+namespace ngram {
+
+// Sum 16 per-row values over the 32 lanes of a half-wave by recursive
+// halving: each exchange sends half of the remaining values, so 16 shuffles
+// replace 80.  Lane l ends up owning row index owner16(l) (lanes l and l^1
+// hold the same value).
+__device__ __forceinline__ float xsum16(float (&x)[16], int lane) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const bool up = lane & 16;
+    const float keep = up ? x[8 + q] : x[q];
+    const float send = up ? x[q] : x[8 + q];
+    x[q] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool up = lane & 8;
+    const float keep = up ? x[4 + q] : x[q];
+    const float send = up ? x[q] : x[4 + q];
+    x[q] = keep + __shfl_xor(send, 8);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const bool up = lane & 4;
+    const float keep = up ? x[2 + q] : x[q];
+    const float send = up ? x[q] : x[2 + q];
+    x[q] = keep + __shfl_xor(send, 4);
+  }
+  {
+    const bool up = lane & 2;
+    const float keep = up ? x[1] : x[0];
+    const float send = up ? x[0] : x[1];
+    x[0] = keep + __shfl_xor(send, 2);
+  }
+  return x[0] + __shfl_xor(x[0], 1);
+}
+
+__device__ __forceinline__ int owner16(int lane) {
+  return ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1);
+}
+
+// Row (within a 32x32 block) held by accumulator register r of this lane.
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// seg < nb: key projection of branch seg; seg == nb: value projection.
+// The wave owns rows [wrow0, wrow0 + 32*MI) and columns [wcol0, wcol0 + 32*NI),
+// its partial index is pidx.
+template <int MI, int NI>
+__device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], const EpiArgs& a,
+                                              int seg, int64_t wrow0, int wcol0, int pidx,
+                                              int lane) {
+  const int d = a.d;
+  const int64_t M = a.M;
+  const int nq = 3 * a.nb + 1;
+  if (seg < a.nb) {
+    const bf16_bits* __restrict__ H = a.hidden + seg * a.h_branch_stride;
+    float g[NI];
+    bool cv[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = wcol0 + ni * 32 + (lane & 31);
+      cv[ni] = col < d;
+      const int cc = cv[ni] ? col : 0;
+      g[ni] = (a.gamma_q ? bf16_to_f32(a.gamma_q[cc]) : 1.0f) *
+              (a.gamma_k ? bf16_to_f32(a.gamma_k[cc]) : 1.0f);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      float xd[16], xk[16], xh[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xd[r] = xk[r] = xh[r] = 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = wcol0 + ni * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
+          if (cv[ni] && row < M) {
+            const float h = bf16_to_f32(H[row * a.h_tok_stride + col]);
+            const float k = acc[mi][ni][r];
+            xd[r] += g[ni] * h * k;
+            xk[r] += k * k;
+            xh[r] += h * h;
+          }
+        }
+      }
+      const float sd = xsum16(xd, lane);
+      const float sk = xsum16(xk, lane);
+      const float sh = xsum16(xh, lane);
+      const int64_t row = wrow0 + mi * 32 + acc_row(owner16(lane), lane);
+      if (!(lane & 1) && row < M) {
+        float* p = a.parts + (row * nq + 3 * seg) * a.np + pidx;
+        p[0] = sd;
+        p[a.np] = sk;
+        p[2 * a.np] = sh;
+      }
+    }
+  } else {
+    float* __restrict__ V = a.v;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      float xv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xv[r] = 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = wcol0 + ni * 32 + (lane & 31);
+        if (col < d) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
+            if (row < M) {
+              const float v = acc[mi][ni][r];
+              V[row * d + col] = v;
+              xv[r] += v * v;
+            }
+          }
+        }
+      }
+      const float sv = xsum16(xv, lane);
+      const int64_t row = wrow0 + mi * 32 + acc_row(owner16(lane), lane);
+      if (!(lane & 1) && row < M) a.parts[(row * nq + 3 * a.nb) * a.np + pidx] = sv;
+    }
+  }
+}
+
+// 64-bit key mod a prime p < 2^31 with magic = floor(2^64 / p): the quotient
+// estimate is exact or one short (Barrett), so one correction suffices.
+__device__ __forceinline__ uint32_t mod_prime(uint64_t key, uint64_t p, uint64_t magic) {
+  const uint64_t q = __umul64hi(key, magic);
+  uint64_t r = key - q * p;
+  if (r >= p) r -= p;
+  return (uint32_t)r;
+}
+
+}  // namespace ngram

@@ -36,27 +36,6 @@ __device__ __forceinline__ float4 fma4(float4 a, float4 b, float4 c) {
 }
 __device__ __forceinline__ float silu(float c) { return c / (1.0f + expf(-c)); }
 
-// Gate of branch br from the projection's row partials (layout
-// [3*nb+1][np]: dot, sum k^2, sum h^2 per branch, then sum v^2).
-__device__ __forceinline__ float gate_from_parts(const float* __restrict__ pr, int br, int np,
-                                                 int d, float eps) {
-  float dot = 0.0f, kk = 0.0f, hh = 0.0f;
-  for (int p = 0; p < np; ++p) {
-    dot += pr[(3 * br) * np + p];
-    kk += pr[(3 * br + 1) * np + p];
-    hh += pr[(3 * br + 2) * np + p];
-  }
-  const float fd = (float)d;
-  const float z = dot / (sqrtf(hh / fd + eps) * sqrtf(kk / fd + eps) * sqrtf(fd));
-  return 1.0f / (1.0f + expf(-z));
-}
-
-__device__ __forceinline__ float sum_parts(const float* __restrict__ pr, int np) {
-  float s = 0.0f;
-  for (int p = 0; p < np; ++p) s += pr[p];
-  return s;
-}
-
 // ngram_gate: gates and U = g V in the activation dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_values_kernel(ConvArgs a, int64_t M) {
@@ -65,10 +44,30 @@ __global__ __launch_bounds__(256) void gate_values_kernel(ConvArgs a, int64_t M)
   if (tok >= M) return;
   const int nq = 3 * a.nb + 1;
   const float* pr = a.parts + tok * nq * a.np;
-  if (threadIdx.x < a.nb) {
-    const float al = gate_from_parts(pr, threadIdx.x, a.np, a.d, a.eps);
-    s_alpha[threadIdx.x] = al;
-    if (a.gates) a.gates[tok * a.nb + threadIdx.x] = al;
+  {
+    // one wave per branch; lanes split the row partials
+    const int lane = threadIdx.x & 63, br = threadIdx.x >> 6;
+    if (br < a.nb) {
+      float dot = 0.0f, kk = 0.0f, hh = 0.0f;
+      for (int p = lane; p < a.np; p += 64) {
+        dot += pr[(3 * br) * a.np + p];
+        kk += pr[(3 * br + 1) * a.np + p];
+        hh += pr[(3 * br + 2) * a.np + p];
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        dot += __shfl_xor(dot, off);
+        kk += __shfl_xor(kk, off);
+        hh += __shfl_xor(hh, off);
+      }
+      if (lane == 0) {
+        const float fd = (float)a.d;
+        const float z = dot / (sqrtf(hh / fd + a.eps) * sqrtf(kk / fd + a.eps) * sqrtf(fd));
+        const float al = 1.0f / (1.0f + expf(-z));
+        s_alpha[br] = al;
+        if (a.gates) a.gates[tok * a.nb + br] = al;
+      }
+    }
   }
   __syncthreads();
   T* out = static_cast<T*>(a.out);
@@ -99,26 +98,47 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
   const int nb = a.nb, d = a.d;
   const int64_t seq0 = (int64_t)b * a.T;
 
-  // ---- step 1: per-position scalars
+  // ---- step 1: per-position scalars, one wave per position: the lanes split
+  // the np row partials of each sum and combine them with shuffles
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if (FUSED) {
     const int nq = 3 * nb + 1;
-    for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    const float fd = (float)d;
+    for (int i = wave; i < L; i += nw) {
       const int q = qs + i;
-      float al = 0.0f, sc = 0.0f;
-      if (q >= 0) {
-        const int64_t tok = seq0 + q;
-        const float* pr = a.parts + tok * nq * a.np;
-        al = gate_from_parts(pr, br, a.np, d, a.eps);
-        const float mv = sum_parts(pr + 3 * nb * a.np, a.np) / (float)d;
-        sc = al / sqrtf(al * al * mv + a.eps);
+      if (q < 0) {
+        if (lane == 0) {
+          s_alpha[i] = 0.0f;
+          s_scale[i] = 0.0f;
+        }
+        continue;
+      }
+      const int64_t tok = seq0 + q;
+      const float* pr = a.parts + tok * nq * a.np;
+      float dot = 0.0f, kk = 0.0f, hh = 0.0f, vv = 0.0f;
+      for (int p = lane; p < a.np; p += 64) {
+        dot += pr[(3 * br) * a.np + p];
+        kk += pr[(3 * br + 1) * a.np + p];
+        hh += pr[(3 * br + 2) * a.np + p];
+        vv += pr[(3 * nb) * a.np + p];
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        dot += __shfl_xor(dot, off);
+        kk += __shfl_xor(kk, off);
+        hh += __shfl_xor(hh, off);
+        vv += __shfl_xor(vv, off);
+      }
+      if (lane == 0) {
+        const float z = dot / (sqrtf(hh / fd + a.eps) * sqrtf(kk / fd + a.eps) * sqrtf(fd));
+        const float al = 1.0f / (1.0f + expf(-z));
+        s_alpha[i] = al;
+        s_scale[i] = al / sqrtf(al * al * (vv / fd) + a.eps);
         if (a.gates && q >= p0) a.gates[tok * nb + br] = al;
       }
-      s_alpha[i] = al;
-      s_scale[i] = sc;
     }
   } else {
     const T* U = static_cast<const T*>(a.u);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     for (int i = wave; i < L; i += nw) {
       const int q = qs + i;
       float sc = 0.0f;

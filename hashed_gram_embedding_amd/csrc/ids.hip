@@ -10,21 +10,10 @@
 // are a handful of 4-byte loads that stay in L2, the LUT (<= 1 MB) is
 // L2-resident, and the n_tables 64-bit products and remainders are plain ALU
 // work.  The kernel is tiny next to the gather and the projections.
-#include "internal.h"
+#include "hashing.h"
 
 namespace ngram {
 namespace {
-
-__device__ __forceinline__ int32_t compress_one(int32_t x, const int32_t* __restrict__ lut,
-                                                int32_t vocab, int32_t vocab_c, int32_t pad,
-                                                int32_t* __restrict__ err) {
-  if (x >= 0 && x < vocab) {
-    int32_t c = lut[x];
-    if (c >= 0 && c < vocab_c) return c;
-  }
-  if (err) *err = 1;
-  return pad;
-}
 
 __global__ void compress_kernel(const int32_t* __restrict__ raw, int64_t n,
                                 const int32_t* __restrict__ lut, int32_t vocab, int32_t vocab_c,
@@ -45,35 +34,14 @@ __global__ void hash_kernel(const int32_t* __restrict__ ids, int32_t B, int32_t 
   for (int64_t tok = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; tok < n; tok += stride) {
     const int32_t b = (int32_t)(tok / T);
     const int32_t t = (int32_t)(tok - (int64_t)b * T);
-    // c[i] = compressed id at position t - i
     uint64_t c[NGRAM_MAX_ORDER];
-#pragma unroll
-    for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
-      int32_t id = a.pad_id;
-      bool have = false;
-      if (i < a.max_order) {
-        const int32_t p = t - i;
-        if (p >= 0) {
-          id = ids[tok - i];
-          have = true;
-        } else if (hist != nullptr && a.hist_len + p >= 0) {
-          id = hist[(int64_t)b * a.hist_len + a.hist_len + p];
-          have = true;
-        }
-      }
-      if (RAW && have) id = compress_one(id, lut, a.vocab, a.vocab_c, a.pad_id, err);
-      c[i] = (uint64_t)(uint32_t)id;
-    }
+    context_ids<RAW>(ids, tok, b, t, hist, lut, a, err, c);
     int32_t* out = row_idx + tok * a.n_tables;
     for (int o = 0; o < a.n_orders; ++o) {
       const int n_o = a.orders[o];
       for (int k = 0; k < a.heads; ++k) {
         const int j = o * a.heads + k;
-        uint64_t key = 0;
-#pragma unroll
-        for (int i = 0; i < NGRAM_MAX_ORDER; ++i)
-          if (i < n_o) key ^= c[i] * a.mult[j][i];
-        out[j] = (int32_t)(key % a.rows[j]);
+        out[j] = (int32_t)table_row(a, j, n_o, c);
       }
     }
   }

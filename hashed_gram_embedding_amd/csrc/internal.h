@@ -58,8 +58,6 @@ struct Elem<bf16_bits> {
   }
 };
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
-
 // ---------------------------------------------------------------------------
 // kernel argument blocks (passed by value)
 // ---------------------------------------------------------------------------
@@ -68,6 +66,7 @@ struct HashArgs {
   int32_t pad_id, vocab, vocab_c, hist_len;
   int32_t orders[NGRAM_MAX_ORDER];
   uint64_t rows[NGRAM_MAX_TABLES];
+  uint64_t magic[NGRAM_MAX_TABLES];  // floor(2^64 / rows[j]) for mod_prime
   uint64_t mult[NGRAM_MAX_TABLES][NGRAM_MAX_ORDER];
 };
 
@@ -90,6 +89,38 @@ struct ProjArgs {
   float* parts;           // [M, 3*nb+1, np] fp32
   int64_t M;
   int32_t K, d, nb, np;
+  int32_t w_dk;           // fp32 path: W stored [d, K] instead of [K, d]
+};
+
+// Epilogue of the projections: gate row partials for key segments, fp32 V
+// and sum(v^2) for the value segment.
+struct EpiArgs {
+  const bf16_bits* hidden;
+  int64_t h_tok_stride, h_branch_stride;
+  const bf16_bits* gamma_q;  // nullable
+  const bf16_bits* gamma_k;  // nullable
+  float* v;                  // [M, d]
+  float* parts;              // [M, 3*nb+1, np]
+  int64_t M;
+  int32_t d, nb, np;
+};
+
+// Projection with operands copied global -> LDS (W stored [d, mem]).  The A
+// operand is E [M, K] (e != nullptr) or gathered from the tables after
+// hashing raw ids in-kernel (e == nullptr).
+struct AsyncProjArgs {
+  const bf16_bits* e;
+  const int32_t* ids;        // raw ids [B, T]
+  const int32_t* hist;       // raw history [B, max_order-1] or nullptr
+  const int32_t* lut;
+  int32_t* err;
+  int32_t T, row_dim;
+  HashArgs hash;
+  TablePtrs tabs;
+  const bf16_bits* wk;       // [nb, d, K]
+  const bf16_bits* wv;       // [d, K]
+  EpiArgs epi;
+  int32_t K, tiles_m, tiles_n, group_m;
 };
 
 // Gate + gated value + conv block over a [B, T] token grid.
@@ -131,6 +162,11 @@ struct ProjPlan {
 };
 ProjPlan plan_projection(int dtype, int64_t M, int32_t d);
 hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a, hipStream_t s);
+
+// plan 0: 256x256 tiles, 1: 128x128, 2: 64x64; wave_cols = partial width.
+int async_plan(int64_t M);
+int async_wave_cols(int plan);
+hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s);
 
 hipError_t launch_gate_values(int dtype, const ConvArgs& a, int64_t M, hipStream_t s);
 hipError_t launch_fused_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s);

@@ -20,7 +20,7 @@
 // 8x8 blocks, transposed in registers and stored n-major so each lane reads
 // its 8 consecutive k values with one 16-byte LDS load.  The LDS k pitch is
 // padded by 16 bytes so the 32 rows read by a half-wave hit distinct banks.
-#include "internal.h"
+#include "epilogue.h"
 
 namespace ngram {
 namespace {
@@ -37,50 +37,6 @@ struct Tile {
   static constexpr int LDS_A = BM * LDK, LDS_B = BN * LDK;
   static constexpr int LDS_BUF = LDS_A + LDS_B;
 };
-
-// Sum 16 per-row values over the 32 lanes of a half-wave by recursive
-// halving: each exchange sends half of the remaining values, so 16 shuffles
-// replace 80.  Lane l ends up owning row index owner16(l) (lanes l and l^1
-// hold the same value).
-__device__ __forceinline__ float xsum16(float (&x)[16], int lane) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const bool up = lane & 16;
-    const float keep = up ? x[8 + q] : x[q];
-    const float send = up ? x[q] : x[8 + q];
-    x[q] = keep + __shfl_xor(send, 16);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const bool up = lane & 8;
-    const float keep = up ? x[4 + q] : x[q];
-    const float send = up ? x[q] : x[4 + q];
-    x[q] = keep + __shfl_xor(send, 8);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const bool up = lane & 4;
-    const float keep = up ? x[2 + q] : x[q];
-    const float send = up ? x[q] : x[2 + q];
-    x[q] = keep + __shfl_xor(send, 4);
-  }
-  {
-    const bool up = lane & 2;
-    const float keep = up ? x[1] : x[0];
-    const float send = up ? x[0] : x[1];
-    x[0] = keep + __shfl_xor(send, 2);
-  }
-  return x[0] + __shfl_xor(x[0], 1);
-}
-
-__device__ __forceinline__ int owner16(int lane) {
-  return ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1);
-}
-
-// Row (within the 32x32 block) of accumulator register r for this lane.
-__device__ __forceinline__ int acc_row(int r, int lane) {
-  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
 
 // A tile rows row0 + 32*i (clamped to the last valid row: values of rows
 // past M are computed but never written), 16 bytes at element column kcol.
@@ -228,81 +184,19 @@ __global__ __launch_bounds__(256, 1) void proj_bf16_kernel(ProjArgs a, int tiles
   // ---------------------------------------------------------------- epilogue
   const int wcol0 = n0 + wn * TL::WN;  // first column of this wave
   if (wcol0 >= d) return;
-  const int pidx = wcol0 / TL::WN;
-  const int nq = 3 * a.nb + 1;
-  const int64_t wrow0 = m0 + wm * TL::WM;
-
-  if (seg < a.nb) {
-    const bf16_bits* __restrict__ H = static_cast<const bf16_bits*>(a.hidden) + seg * a.h_branch_stride;
-    const bf16_bits* __restrict__ GQ = static_cast<const bf16_bits*>(a.gamma_q);
-    const bf16_bits* __restrict__ GK = static_cast<const bf16_bits*>(a.gamma_k);
-    float g[TL::NI];
-    bool cv[TL::NI];
-#pragma unroll
-    for (int ni = 0; ni < TL::NI; ++ni) {
-      const int col = wcol0 + ni * 32 + (lane & 31);
-      cv[ni] = col < d;
-      const int cc = cv[ni] ? col : 0;
-      g[ni] = (GQ ? bf16_to_f32(GQ[cc]) : 1.0f) * (GK ? bf16_to_f32(GK[cc]) : 1.0f);
-    }
-#pragma unroll
-    for (int mi = 0; mi < TL::MI; ++mi) {
-      float xd[16], xk[16], xh[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xd[r] = xk[r] = xh[r] = 0.0f;
-#pragma unroll
-      for (int ni = 0; ni < TL::NI; ++ni) {
-        const int col = wcol0 + ni * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
-          if (cv[ni] && row < M) {
-            const float h = bf16_to_f32(H[row * a.h_tok_stride + col]);
-            const float k = acc[mi][ni][r];
-            xd[r] += g[ni] * h * k;
-            xk[r] += k * k;
-            xh[r] += h * h;
-          }
-        }
-      }
-      const float sd = xsum16(xd, lane);
-      const float sk = xsum16(xk, lane);
-      const float sh = xsum16(xh, lane);
-      const int64_t row = wrow0 + mi * 32 + acc_row(owner16(lane), lane);
-      if (!(lane & 1) && row < M) {
-        float* p = a.parts + (row * nq + 3 * seg) * a.np + pidx;
-        p[0] = sd;
-        p[a.np] = sk;
-        p[2 * a.np] = sh;
-      }
-    }
-  } else {
-    float* __restrict__ V = a.v;
-#pragma unroll
-    for (int mi = 0; mi < TL::MI; ++mi) {
-      float xv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xv[r] = 0.0f;
-#pragma unroll
-      for (int ni = 0; ni < TL::NI; ++ni) {
-        const int col = wcol0 + ni * 32 + (lane & 31);
-        if (col < d) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
-            if (row < M) {
-              const float v = acc[mi][ni][r];
-              V[row * d + col] = v;
-              xv[r] += v * v;
-            }
-          }
-        }
-      }
-      const float sv = xsum16(xv, lane);
-      const int64_t row = wrow0 + mi * 32 + acc_row(owner16(lane), lane);
-      if (!(lane & 1) && row < M) a.parts[(row * nq + 3 * a.nb) * a.np + pidx] = sv;
-    }
-  }
+  EpiArgs ea;
+  ea.hidden = static_cast<const bf16_bits*>(a.hidden);
+  ea.h_tok_stride = a.h_tok_stride;
+  ea.h_branch_stride = a.h_branch_stride;
+  ea.gamma_q = static_cast<const bf16_bits*>(a.gamma_q);
+  ea.gamma_k = static_cast<const bf16_bits*>(a.gamma_k);
+  ea.v = a.v;
+  ea.parts = a.parts;
+  ea.M = M;
+  ea.d = d;
+  ea.nb = a.nb;
+  ea.np = a.np;
+  gate_epilogue<TL::MI, TL::NI>(acc, ea, seg, m0 + wm * TL::WM, wcol0, wcol0 / TL::WN, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -322,11 +216,13 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjArgs a) {
   const float* E = static_cast<const float*>(a.e);
   const float* W = seg < a.nb ? static_cast<const float*>(a.wk) + (int64_t)seg * a.K * a.d
                               : static_cast<const float*>(a.wv);
+  // W[k][col] is at k*d + col ([K, d]) or col*K + k ([d, K])
+  const int64_t sk = a.w_dk ? 1 : a.d, sc = a.w_dk ? a.K : 1;
   float acc = 0.0f;
   for (int k0 = 0; k0 < a.K; k0 += FT) {
     const int64_t arow = (int64_t)blockIdx.y * FT + ty;
     As[ty][tx] = (arow < a.M && k0 + tx < a.K) ? E[arow * a.K + k0 + tx] : 0.0f;
-    Bs[ty][tx] = (k0 + ty < a.K && col < a.d) ? W[(int64_t)(k0 + ty) * a.d + col] : 0.0f;
+    Bs[ty][tx] = (k0 + ty < a.K && col < a.d) ? W[(int64_t)(k0 + ty) * sk + col * sc] : 0.0f;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < FT; ++k) acc = fmaf(As[ty][k], Bs[k][tx], acc);

@@ -1,0 +1,312 @@
+// Key / value projections, bf16 MFMA, operands streamed straight from global
+// memory into LDS -- the fast path for W stored [d, mem] (NGRAM_W_D_MEM).
+//
+// Same contract as project.hip ("Qwen3.8-Flash-Next 深度研究" §2.3:
+// E_t -> K_t, V_t, then g_t from RMSNorm'd query and key; Engram's third
+// component in "Qwen 4用上DeepSeek的Engram"): C = E [W_K^(0) .. W_K^(nb-1) W_V]^T
+// with the gate's row partials in the epilogue, K never written.  With W
+// stored [d, mem] both operands are contiguous along the reduction axis, so
+// every 16-byte chunk is copied global -> LDS by global_load_lds_dwordx4
+// (no register staging, no transposes) and a STAGES-deep ring of LDS buffers
+// keeps up to STAGES-1 K steps of copies in flight while the matrix cores
+// work on the current one.
+//
+// GATHER: the kernel hashes its own BM tokens (compression, n-gram keys,
+// multi-head mod-prime hashing) into LDS row ids and the A-operand copies read
+// the table rows directly -- E_t is never materialised, so hash + gather +
+// projection is one launch.  Each 64-wide K step lies inside one table row
+// (row_dim % BK == 0), so a step reads one aligned 128-byte line per token.
+//
+// Each ring slot is its own __shared__ array and the K loop is unrolled by
+// the ring depth, so every copy and every operand read names its slot at
+// compile time: the compiler's wait-count insertion then sees that a read of
+// slot s does not depend on copies still in flight into the other slots and
+// keeps only the explicit partial vmcnt waits below (with one shared array it
+// would drain all copies before every LDS read, serialising the ring).
+//
+// LDS layout per stage: A [BM][BK], B [BN][BK] bf16, rows of BK*2 bytes whose
+// 16-byte chunks are XOR-swizzled by row (chunk ^ f(row)); a copy writes the
+// lanes' chunks contiguously, so the swizzle is applied to the source address,
+// and the MFMA operand reads (8 lanes x 16 bytes per LDS cycle) hit distinct
+// banks.  Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD
+// gets a contiguous range of tiles, walked in groups of group_m M-tiles with
+// the M index fastest -- concurrently running workgroups of one XCD share A
+// and B slabs in its L2.
+#include <stdlib.h>
+
+#include "hashing.h"
+
+namespace ngram {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt: at most N vector-memory ops outstanding, all LDS ops done
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier that leaves global->LDS copies of later stages in flight
+// (__syncthreads() would drain vmcnt); the memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_keep_copies() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void copy16_to_lds(const void* src, bf16_bits* wave_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)wave_dst, 16, 0, 0);
+}
+
+template <int BK>
+__device__ __forceinline__ int swz(int row);
+template <>
+__device__ __forceinline__ int swz<64>(int row) {
+  return row & 7;
+}
+template <>
+__device__ __forceinline__ int swz<32>(int row) {
+  return (row >> 2) & 3;
+}
+
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int tiles_n, int gm,
+                                         int& m, int& seg, int& n) {
+  const int total = tiles_m * n_seg * tiles_n;
+  int logical = bid;
+  if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int per_m = n_seg * tiles_n;
+  const int group = logical / (gm * per_m);
+  const int first_m = group * gm;
+  const int gsize = min(gm, tiles_m - first_m);
+  const int idx = logical - group * gm * per_m;
+  m = first_m + idx % gsize;
+  const int sn = idx / gsize;
+  seg = sn / tiles_n;
+  n = sn - seg * tiles_n;
+}
+
+template <int BM, int BN, int BK, int STAGES, int WGM, bool GATHER>
+__global__ __launch_bounds__(256, 1) void proj_async_kernel(AsyncProjArgs a) {
+  constexpr int WGN = 4 / WGM;
+  constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CH;          // rows covered by one wave-wide copy
+  constexpr int A_INS = BM / (RPI * 4);  // copies per wave per stage
+  constexpr int B_INS = BN / (RPI * 4);
+  constexpr int PER_STAGE = A_INS + B_INS;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int A_ELEMS = BM * BK;
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  static_assert(A_INS * RPI * 4 == BM && B_INS * RPI * 4 == BN, "tile / copy shape");
+  static_assert(MI * 32 == WTM && NI * 32 == WTN, "wave tile");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+
+  __shared__ __attribute__((aligned(16))) bf16_bits ring0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring2[STAGES > 2 ? STAGE_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring3[STAGES > 3 ? STAGE_ELEMS : 8];
+  __shared__ int32_t s_rid[GATHER ? BM * NGRAM_MAX_TABLES : 1];
+  // slot index is a compile-time constant at every use (unrolled loops)
+  auto slot = [&](int sl) -> bf16_bits* {
+    return sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : ring3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const EpiArgs& ep = a.epi;
+  const int n_seg = ep.nb + 1;
+  int m_tile, seg, n_tile;
+  map_tile(blockIdx.x, a.tiles_m, n_seg, a.tiles_n, a.group_m, m_tile, seg, n_tile);
+  const int64_t M = ep.M;
+  const int64_t m0 = (int64_t)m_tile * BM;
+  const int n0 = n_tile * BN;
+  const int K = a.K, d = ep.d;
+  const bf16_bits* __restrict__ W = seg < ep.nb ? a.wk + (int64_t)seg * d * K : a.wv;
+
+  if (GATHER) {
+    for (int i = tid; i < BM; i += 256) {
+      int64_t tok = m0 + i;
+      if (tok > M - 1) tok = M - 1;
+      const int32_t b = (int32_t)(tok / a.T);
+      const int32_t t = (int32_t)(tok - (int64_t)b * a.T);
+      uint64_t c[NGRAM_MAX_ORDER];
+      context_ids<true>(a.ids, tok, b, t, a.hist, a.lut, a.hash, a.err, c);
+      for (int o = 0; o < a.hash.n_orders; ++o)
+        for (int k = 0; k < a.hash.heads; ++k) {
+          const int j = o * a.hash.heads + k;
+          s_rid[i * NGRAM_MAX_TABLES + j] = (int32_t)table_row(a.hash, j, a.hash.orders[o], c);
+        }
+    }
+    __syncthreads();
+  }
+
+  // Copy lanes: lane -> (row lrow of the copy's RPI-row block, 16-byte chunk
+  // pch of the LDS row).  A block starts at a multiple of RPI rows, so the
+  // row's swizzle is that of lrow and the chunk each lane fetches is fixed.
+  const int lrow = lane / CH, pch = lane - (lane / CH) * CH;
+  const int lch8 = (pch ^ swz<BK>(lrow)) * 8;  // element offset of the fetched chunk
+  // Operand-read lanes: LDS byte offset of this lane's A and B rows for
+  // mi = ni = 0; the other blocks are +32 rows (immediate offsets), and the
+  // swizzle of all of them equals that of the lane's row (rows differ by
+  // multiples of 16).
+  const int frow = lane & 31;
+  const uint32_t a_row_b = (uint32_t)((wm * WTM + frow) * BK * 2);
+  const uint32_t b_row_b = (uint32_t)((wn * WTN + frow) * BK * 2);
+  const int fsw = swz<BK>(frow);
+
+  // Copy K step kt into ring slot sl: A rows then B rows, one 16-byte chunk
+  // per lane, RPI rows per wave-wide copy.
+  auto issue = [&](int kt, int sl) {
+    bf16_bits* As = slot(sl);
+    bf16_bits* Bs = As + A_ELEMS;
+    const int k0 = kt * BK;
+    int j = 0, cofs = 0;
+    const bf16_bits* tab = nullptr;
+    if (GATHER) {
+      j = k0 / a.row_dim;
+      cofs = k0 - j * a.row_dim + lch8;
+      tab = static_cast<const bf16_bits*>(a.tabs.p[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int rblk = (wave * A_INS + i) * RPI;
+      const bf16_bits* src;
+      if (GATHER) {
+        src = tab + (int64_t)s_rid[(rblk + lrow) * NGRAM_MAX_TABLES + j] * a.row_dim + cofs;
+      } else {
+        int64_t grow = m0 + rblk + lrow;
+        if (grow > M - 1) grow = M - 1;
+        src = a.e + grow * K + k0 + lch8;
+      }
+      copy16_to_lds(src, As + rblk * BK);
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int rblk = (wave * B_INS + i) * RPI;
+      int n = n0 + rblk + lrow;
+      if (n > d - 1) n = d - 1;  // columns past d are computed, never stored
+      copy16_to_lds(W + (uint32_t)(n * K + k0 + lch8), Bs + rblk * BK);
+    }
+  };
+
+  floatx16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  // MFMAs over the K step held in ring slot sl
+  auto compute = [&](int sl) {
+    const char* As = reinterpret_cast<const char*>(slot(sl));
+    const char* Bs = As + A_ELEMS * 2;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const uint32_t co = (uint32_t)(((kk * 2 + (lane >> 5)) ^ fsw) * 16);
+      bf16x8 af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8*>(As + a_row_b + co + mi * 32 * BK * 2);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        bfr[ni] = *reinterpret_cast<const bf16x8*>(Bs + b_row_b + co + ni * 32 * BK * 2);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  const int nk = K / BK;
+  // The last slot first receives a throw-away copy of step 0 (overwritten
+  // before it is read), so that on entry to the loop every slot has one copy
+  // outstanding in the same order as at the loop's back edge; the compiler's
+  // wait-count state then merges exactly at the loop header instead of
+  // falling back to draining every copy before the first read.
+  issue(0, STAGES - 1);
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, st);
+
+  for (int base = 0; base < nk; base += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int kt = base + u;
+      if (kt < nk) {
+        // this wave's copies of step kt have landed; later steps may be in flight
+        if (kt + STAGES - 2 < nk)
+          wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+        else
+          wait_vmcnt<0>();
+        barrier_keep_copies();  // ... and every other wave's; slot of step kt-1 is free
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (u + STAGES - 1) % STAGES);
+        compute(u);
+      }
+    }
+  }
+
+  const int wcol0 = n0 + wn * WTN;
+  if (wcol0 >= d) return;
+  gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+}
+
+template <int BM, int BN, int BK, int STAGES, int WGM>
+hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
+  constexpr int WTN = BN / (4 / WGM);  // columns per wave = width of one row partial
+  AsyncProjArgs a = a0;
+  // the host sized the partials for this tile's wave width; refuse to launch
+  // (instead of writing past the workspace) if the two ever disagree
+  if (a.epi.np != (a.epi.d + WTN - 1) / WTN) return hipErrorInvalidValue;
+  a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
+  a.tiles_n = (a.epi.d + BN - 1) / BN;
+  const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
+  if (gather)
+    proj_async_kernel<BM, BN, BK, STAGES, WGM, true><<<(unsigned)blocks, 256, 0, s>>>(a);
+  else
+    proj_async_kernel<BM, BN, BK, STAGES, WGM, false><<<(unsigned)blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// One table of tile plans serves both the launch and the host's partial
+// count, so the two cannot drift apart.
+#define NGRAM_ASYNC_PLANS(X) \
+  X(0, 256, 128, 32, 4, 2)   \
+  X(1, 128, 128, 64, 4, 2)   \
+  X(2, 64, 64, 64, 4, 2)     \
+  X(3, 256, 128, 64, 3, 2)   \
+  X(4, 128, 64, 64, 4, 2)    \
+  X(5, 64, 128, 64, 4, 2)
+
+}  // namespace
+
+// Tile plans (id, BM, BN, K step, ring depth, wave rows; 4 waves): see
+// NGRAM_ASYNC_PLANS.  NGRAM_ASYNC_TILE=<id> overrides the choice (a tuning
+// knob).
+int async_plan(int64_t M) {
+  const char* e = getenv("NGRAM_ASYNC_TILE");
+  if (e && *e >= '0' && *e <= '5' && e[1] == 0) return *e - '0';
+  if (M >= 4096) return 0;
+  if (M >= 1024) return 1;
+  return 2;
+}
+
+int async_wave_cols(int plan) {
+#define NGRAM_WAVE_COLS(id, bm, bn, bk, st, wgm) \
+  if (plan == id) return bn / (4 / wgm);
+  NGRAM_ASYNC_PLANS(NGRAM_WAVE_COLS)
+#undef NGRAM_WAVE_COLS
+  return -1;
+}
+
+hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s) {
+  if (a.epi.M == 0) return hipSuccess;
+#define NGRAM_LAUNCH_PLAN(id, bm, bn, bk, st, wgm) \
+  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm>(gather, a, s);
+  NGRAM_ASYNC_PLANS(NGRAM_LAUNCH_PLAN)
+#undef NGRAM_LAUNCH_PLAN
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ngram

@@ -10,7 +10,6 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass, field
 from typing import Optional, Sequence
 
 MAX_TABLES = 16
@@ -18,6 +17,7 @@ MAX_ORDER = 4
 MAX_BRANCHES = 4
 ADD_RESIDUAL = 1
 F32, BF16 = 0, 1
+W_MEM_D, W_D_MEM = 0, 1  # projection storage: [mem, d] or [d, mem] (fast path)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libngram.so")
@@ -50,13 +50,15 @@ class NgramConfig(ctypes.Structure):
         ("rms_eps", ctypes.c_float),
         ("table_dtype", ctypes.c_int32),
         ("act_dtype", ctypes.c_int32),
+        ("w_layout", ctypes.c_int32),
     ]
 
 
 def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_mult,
                 row_dim: int, hidden_dim: int, n_branches: int, vocab: int,
                 vocab_compressed: int, dtype: int, pad_id: int = 0, rms_eps: float = 1e-6,
-                conv_kernel: int = 4, conv_dilation: Optional[int] = None) -> NgramConfig:
+                conv_kernel: int = 4, conv_dilation: Optional[int] = None,
+                w_layout: int = W_MEM_D) -> NgramConfig:
     """Fill an NgramConfig; ``hash_mult`` is indexable as [table][slot]."""
     c = NgramConfig()
     c.n_orders = len(orders)
@@ -81,6 +83,7 @@ def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_
     c.rms_eps = rms_eps
     c.table_dtype = dtype
     c.act_dtype = dtype
+    c.w_layout = w_layout
     return c
 
 
@@ -92,6 +95,7 @@ _SIGS = {
     "ngram_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ngram_abi_version": (ctypes.c_int, []),
     "ngram_config_validate": (ctypes.c_int, [_cfgp]),
+    "ngram_set_timing_events": (ctypes.c_int, [_p, ctypes.c_int]),
     "ngram_compress_ids": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p]),
     "ngram_hash": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p]),
     "ngram_gather": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p]),
@@ -130,6 +134,23 @@ def abi_version() -> int:
 
 def ngram_config_validate(cfg: NgramConfig) -> int:
     return lib().ngram_config_validate(ctypes.byref(cfg))
+
+
+N_STAGES = 4
+STAGE_NAMES = ("hash", "gather", "projection", "gate_conv")
+
+
+def ngram_set_timing_events(events) -> None:
+    """Benchmark hook: ``events`` is a list of N_STAGES + 1 torch.cuda.Event
+    (created with enable_timing=True), or None to turn the hook off."""
+    if events is None:
+        _check(lib().ngram_set_timing_events(None, 0), "ngram_set_timing_events")
+        return
+    for e in events:  # torch creates the underlying hipEvent on first record
+        if not e.cuda_event:
+            e.record()
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check(lib().ngram_set_timing_events(arr, len(events)), "ngram_set_timing_events")
 
 
 # ---------------------------------------------------------------------------

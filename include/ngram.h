@@ -67,6 +67,17 @@ typedef enum ngram_status {
 typedef enum ngram_dtype { NGRAM_F32 = 0, NGRAM_BF16 = 1 } ngram_dtype;
 
 /*
+ * Storage of the projection matrices (ngram_config.w_layout).
+ *   NGRAM_W_MEM_D: W_K^(b), W_V are [mem_dim, d] row-major, K = E W.
+ *   NGRAM_W_D_MEM: they are [d, mem_dim] row-major (output row n holds the
+ *                  mem_dim weights of K_n; the torch.nn.Linear convention),
+ *                  K = E W^T.  Both operands of the product are then
+ *                  contiguous along mem_dim, which the bf16 kernels stream
+ *                  straight into LDS: this is the fast layout.
+ */
+typedef enum ngram_w_layout { NGRAM_W_MEM_D = 0, NGRAM_W_D_MEM = 1 } ngram_w_layout;
+
+/*
  * Layer configuration (host memory, read during the call only).
  *
  * Tables: table j = o * heads_per_order + k holds the rows of head k of order
@@ -75,9 +86,11 @@ typedef enum ngram_dtype { NGRAM_F32 = 0, NGRAM_BF16 = 1 } ngram_dtype;
  *     key = XOR_{i=0}^{n-1} ( (uint64)c_{t-i} * hash_mult[j][i] )   (mod 2^64)
  *     row = key mod rows[j]
  * with n = orders[o]; c_{t-i} for t-i < 0 comes from the history if given,
- * else pad_id.  The pages name only "deterministic hashing by K independent
- * heads into prime-sized tables" and a "mod hash"; this multiply-xor-mod form
- * is the library's reading, the multipliers being parameters of the model.
+ * else pad_id.  The sources fix only that each order has K independent hash
+ * heads mapping into tables of prime size, deterministically, and (in a
+ * related method's lineage table) that the hash is a modulus; this
+ * multiply-xor-mod form is the library's reading, the multipliers being
+ * parameters of the model.
  */
 typedef struct ngram_config {
   int32_t n_orders;                                      /* 1..NGRAM_MAX_ORDER */
@@ -98,6 +111,7 @@ typedef struct ngram_config {
   float rms_eps;                                         /* >= 0, RMSNorm epsilon */
   int32_t table_dtype;                                   /* ngram_dtype */
   int32_t act_dtype;                                     /* ngram_dtype, == table_dtype */
+  int32_t w_layout;                                      /* ngram_w_layout */
 } ngram_config;
 
 /* Human-readable name of a status code (static string). */
@@ -141,9 +155,9 @@ int ngram_hash(const ngram_config* cfg, const int32_t* comp_ids, int32_t B, int3
                const int32_t* history, int32_t* row_idx, void* stream);
 
 /*
- * Gather and concatenation into the memory vector E_t (§2.3 "每行 160 个值，
- * 拼接成 E_t"): mem[t, j*row_dim + c] = tables[j][row_idx[t, j], c].  An exact
- * copy.
+ * Gather and concatenation into the memory vector E_t ("Qwen3.8-Flash-Next
+ * 深度研究" §2.3: the rows named by the row ids are joined end to end into
+ * E_t): mem[t, j*row_dim + c] = tables[j][row_idx[t, j], c].  An exact copy.
  *   row_idx  device int32[n_tok, n_tables]; each entry must be < rows[j]
  *   tables   HOST array of n_tables device pointers, table j is
  *            [rows[j], row_dim] of table_dtype
@@ -162,7 +176,9 @@ int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
  *            (nbh = 1: one query row shared by all branches) or == d
  *            (nbh = n_branches: one query row per branch)
  *   mem      device [n_tok, mem_dim] table_dtype (E)
- *   w_k      device [n_branches, mem_dim, d] act_dtype; w_v [mem_dim, d]
+ *   w_k      device [n_branches, mem_dim, d] act_dtype and w_v [mem_dim, d]
+ *            (NGRAM_W_MEM_D), or [n_branches, d, mem_dim] and [d, mem_dim]
+ *            (NGRAM_W_D_MEM)
  *   gamma_q, gamma_k  device [d] act_dtype, nullable (= 1)
  *   gates    device float[n_tok, n_branches] (output)
  *   u        device [n_tok, n_branches, d] act_dtype (output), nullable
@@ -218,6 +234,19 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   const void* gamma_k, const void* gamma_u, const float* conv_state,
                   int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * Benchmark instrumentation (not part of the layer).  When n == NGRAM_N_STAGES,
+ * every following ngram_forward records events[i] (NGRAM_N_STAGES + 1 hipEvent_t handles) on its
+ * stream before stage i -- 0 hash, 1 gather, 2 projection, 3 gate+conv -- and
+ * events[NGRAM_N_STAGES] after the last stage, so hipEventElapsedTime
+ * between consecutive events gives each stage's device time.  n == 0 turns it
+ * off.  The setting is process-wide and not synchronised: set it only while no
+ * other thread calls ngram_forward.  Returns NGRAM_EINVAL for other n or NULL
+ * events.
+ */
+#define NGRAM_N_STAGES 4
+int ngram_set_timing_events(void* const* events, int n);
 
 #ifdef __cplusplus
 }

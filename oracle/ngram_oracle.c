@@ -20,7 +20,8 @@
  *      (x_{t-1}, x_t), 3-gram heads on (x_{t-2}, x_{t-1}, x_t)), concatenation
  *      into E_t, and the layer formula E_t -> K_t, V_t; g_t = Gate(Norm(Q_t),
  *      Norm(K_t)); U_t = g_t * V_t; Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))).
- *  [C] same page, §3-D lineage table: Over-Encoding's "mod hash".
+ *  [C] same page, §3-D lineage table: the related Over-Encoding method hashes
+ *      by a modulus.
  *
  * Readings where the pages leave a step open (each is the plainest one the
  * rest of the text supports):
@@ -134,8 +135,8 @@ void orc_hash(const int32_t* comp, int32_t B, int32_t T, const int32_t* hist,
 }
 
 /*
- * Step 3 -- gather and concatenate [A, second component; B, "16 row ids, 160
- * values per row, concatenated into E_t"]: E_t = table_0[r_0] ++ table_1[r_1]
+ * Step 3 -- gather and concatenate [A, second component; B, the row ids' rows
+ * joined end to end into E_t]: E_t = table_0[r_0] ++ table_1[r_1]
  * ++ ... in table order (orders ascending, then heads).  e is [n_tok, mem]
  * with mem = n_tables * row_dim.
  */

@@ -71,12 +71,19 @@ def make_hidden(w: Workload, n_tokens: int, batch_id: int = 0, device="cuda"):
     return fill_normal(t, w.hidden_seed(batch_id), w.hidden_sigma)
 
 
-def make_weights(w: Workload, device="cuda"):
-    """(W_K [nb, mem, d], W_V [mem, d]) on the device."""
+def make_weights(w: Workload, device="cuda", layout: str = "mem_d"):
+    """(W_K, W_V) on the device: [nb, mem, d] and [mem, d] for layout
+    'mem_d'; the same matrices stored transposed ([nb, d, mem], [d, mem])
+    for layout 'd_mem'."""
     import torch
     wk = torch.empty((w.n_branches, w.mem_dim, w.hidden), dtype=torch_dtype(w), device=device)
     for b in range(w.n_branches):
         fill_normal(wk[b], w.wk_seed(b), w.w_sigma)
     wv = torch.empty((w.mem_dim, w.hidden), dtype=torch_dtype(w), device=device)
     fill_normal(wv, w.wv_seed(), w.w_sigma)
+    if layout == "d_mem":
+        wk = wk.transpose(1, 2).contiguous()
+        wv = wv.t().contiguous()
+    elif layout != "mem_d":
+        raise ValueError(layout)
     return wk, wv

@@ -336,9 +336,11 @@ def to_f64(values: np.ndarray, dtype: str) -> np.ndarray:
     return rng.bf16_bits_to_f32(values).astype(np.float64)
 
 
-def layer_config(w: Workload) -> dict:
-    """Keyword arguments describing the layer for a workload (plain data)."""
+def layer_config(w: Workload, w_layout: str = "mem_d") -> dict:
+    """Keyword arguments describing the layer for a workload (plain data);
+    ``w_layout`` says how the projection matrices are stored."""
     return dict(orders=tuple(w.orders), heads=w.heads, rows=w.rows(),
                 hash_mult=hash_multipliers(w), row_dim=w.row_dim, hidden_dim=w.hidden,
                 n_branches=w.n_branches, vocab=w.vocab, vocab_compressed=w.vocab_compressed,
-                dtype=0 if w.dtype == "f32" else 1, pad_id=0, rms_eps=w.rms_eps)
+                dtype=0 if w.dtype == "f32" else 1, pad_id=0, rms_eps=w.rms_eps,
+                w_layout={"mem_d": 0, "d_mem": 1}[w_layout])

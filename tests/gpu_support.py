@@ -18,8 +18,8 @@ def H():
     return H
 
 
-def config(w: W.Workload, **over):
-    kw = W.layer_config(w)
+def config(w: W.Workload, layout: str = "mem_d", **over):
+    kw = W.layer_config(w, layout)
     kw.update(over)
     return H().make_config(**kw)
 
@@ -59,11 +59,19 @@ def tables(w: W.Workload):
     return _TABLES[key]
 
 
-def weights(w: W.Workload):
-    key = (w.param_seed, w.mem_dim, w.hidden, w.n_branches, w.dtype)
+def weights(w: W.Workload, layout: str = "mem_d"):
+    key = (w.param_seed, w.mem_dim, w.hidden, w.n_branches, w.dtype, layout)
     if key not in _WEIGHTS:
-        _WEIGHTS[key] = SD.make_weights(w)
+        _WEIGHTS[key] = SD.make_weights(w, layout=layout)
     return _WEIGHTS[key]
+
+
+def host_weights(wk: torch.Tensor, wv: torch.Tensor, layout: str):
+    """Device weights -> host storage in the oracle's [mem, d] orientation."""
+    k, v = to_storage(wk), to_storage(wv)
+    if layout == "d_mem":
+        k, v = np.ascontiguousarray(k.transpose(0, 2, 1)), np.ascontiguousarray(v.T)
+    return k, v
 
 
 def conv_w(w):

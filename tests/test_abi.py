@@ -104,6 +104,9 @@ def test_validation_codes(H):
     c.hidden_dim = 2048 + 16                                       # bf16 needs d % 32
     assert H.ngram_config_validate(c) == E["SHAPE"]
     c = _cfg(H)
+    c.w_layout = 2
+    assert H.ngram_config_validate(c) == E["INVAL"]
+    c = _cfg(H)
     c.rms_eps = float("nan")
     assert H.ngram_config_validate(c) == E["INVAL"]
     assert H.ngram.lib().ngram_config_validate(None) == E["INVAL"]

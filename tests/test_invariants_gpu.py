@@ -15,8 +15,8 @@ pytestmark = pytest.mark.gpu
 def _forward(w, ids, hidden):
     H = G.H()
     B, T = ids.shape
-    cfg = G.config(w)
-    wk, wv = G.weights(w)
+    cfg = G.config(w, "d_mem")
+    wk, wv = G.weights(w, "d_mem")
     out = torch.empty((B, T, w.n_branches, w.hidden), dtype=G.tdtype(w), device="cuda")
     gates = torch.empty((B, T, w.n_branches), dtype=torch.float32, device="cuda")
     H.ngram_forward(cfg, torch.from_numpy(ids).cuda(), torch.from_numpy(W.make_lut(w)).cuda(),

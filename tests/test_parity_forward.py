@@ -15,9 +15,10 @@ from synth import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _device_inputs(w, ids, hist, random_gamma=False):
+def _device_inputs(w, ids, hist, random_gamma=False, layout="mem_d"):
     n = ids.size
     d = dict(
+        layout=layout,
         ids=torch.from_numpy(ids).cuda(),
         hist=None if hist is None else torch.from_numpy(hist).cuda(),
         lut=torch.from_numpy(W.make_lut(w)).cuda(),
@@ -26,14 +27,14 @@ def _device_inputs(w, ids, hist, random_gamma=False):
         conv_w=G.conv_w(w),
         gam=G.gammas(w, random_gamma),
     )
-    d["wk"], d["wv"] = G.weights(w)
+    d["wk"], d["wv"] = G.weights(w, layout)
     return d
 
 
 def _run(w, inp, flags=0, conv_state=None):
     H = G.H()
     B, T = inp["ids"].shape
-    cfg = G.config(w)
+    cfg = G.config(w, inp["layout"])
     out = torch.empty((B, T, w.n_branches, w.hidden), dtype=G.tdtype(w), device="cuda")
     gates = torch.empty((B, T, w.n_branches), dtype=torch.float32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -48,8 +49,8 @@ def _run(w, inp, flags=0, conv_state=None):
 
 
 def _host_params(w, inp):
-    return G.to_storage(inp["wk"]), G.to_storage(inp["wv"]), W.conv_weight_values(w), \
-        {k: G.to_storage(v) for k, v in inp["gam"].items()}
+    wk, wv = G.host_weights(inp["wk"], inp["wv"], inp["layout"])
+    return wk, wv, W.conv_weight_values(w), {k: G.to_storage(v) for k, v in inp["gam"].items()}
 
 
 def _check_windows(orc, w, ids, hist, inp, out, gates, windows, flags=0, state=None):
@@ -83,11 +84,12 @@ def test_forward_tiny_full(orc, random_gamma, flags):
     _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, w.seq_len)], flags)
 
 
-def test_forward_engram_small(orc):
+@pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
+def test_forward_engram_small(orc, layout):
     w = W.get("engram_small")
-    print("[forward] engram_small", flush=True)
+    print(f"[forward] engram_small {layout}", flush=True)
     ids, hist = W.make_ids(w)
-    inp = _device_inputs(w, ids, hist, random_gamma=True)
+    inp = _device_inputs(w, ids, hist, random_gamma=True, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
     T = w.seq_len
@@ -95,11 +97,12 @@ def test_forward_engram_small(orc):
                    [(0, 0, 40), (0, 1000, 40), (7, 2049, 40), (7, T - 40, 40)])
 
 
-def test_forward_qwen_decode_full(orc):
+@pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
+def test_forward_qwen_decode_full(orc, layout):
     w = W.get("qwen_decode")
-    print("[forward] qwen_decode", flush=True)
+    print(f"[forward] qwen_decode {layout}", flush=True)
     ids, hist = W.make_ids(w)
-    inp = _device_inputs(w, ids, hist)
+    inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
     wk, wv, cw, gam = _host_params(w, inp)
@@ -113,12 +116,13 @@ def test_forward_qwen_decode_full(orc):
     assert e_out < G.TOL and e_gate < G.TOL
 
 
-def test_forward_qwen_decode_conv_state_and_residual(orc):
+@pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
+def test_forward_qwen_decode_conv_state_and_residual(orc, layout):
     """A populated conv state (the last 9 normalised rows of each sequence)."""
     w = W.get("qwen_decode").replace(batch=16)
-    print("[forward] qwen_decode state+residual", flush=True)
+    print(f"[forward] qwen_decode state+residual {layout}", flush=True)
     ids, hist = W.make_ids(w)
-    inp = _device_inputs(w, ids, hist)
+    inp = _device_inputs(w, ids, hist, layout=layout)
     halo = 3 * w.max_order
     state = rng.normal_f32(4242, np.arange(w.batch * halo * w.hidden), 1.0).reshape(
         w.batch, halo, 1, w.hidden)
@@ -128,11 +132,12 @@ def test_forward_qwen_decode_conv_state_and_residual(orc):
                    flags=1, state=state.astype(np.float64))
 
 
-def test_forward_qwen_prefill(orc):
+@pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
+def test_forward_qwen_prefill(orc, layout):
     w = W.get("qwen_prefill")
-    print("[forward] qwen_prefill 262144 tokens", flush=True)
+    print(f"[forward] qwen_prefill 262144 tokens {layout}", flush=True)
     ids, hist = W.make_ids(w)
-    inp = _device_inputs(w, ids, hist)
+    inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
     T = w.seq_len
@@ -141,12 +146,14 @@ def test_forward_qwen_prefill(orc):
     assert bool(((gates > 0) & (gates < 1)).all())
 
 
-@pytest.mark.parametrize("name", ["qwen_multibranch_uniform", "qwen_multibranch_zipf13"])
-def test_forward_multibranch(orc, name):
+@pytest.mark.parametrize("name,layout", [("qwen_multibranch_uniform", "d_mem"),
+                                         ("qwen_multibranch_zipf13", "d_mem"),
+                                         ("qwen_multibranch_zipf13", "mem_d")])
+def test_forward_multibranch(orc, name, layout):
     w = W.get(name)
-    print(f"[forward] {name}", flush=True)
+    print(f"[forward] {name} {layout}", flush=True)
     ids, hist = W.make_ids(w)
-    inp = _device_inputs(w, ids, hist)
+    inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
     T = w.seq_len
@@ -163,7 +170,8 @@ def test_forward_ragged_and_short(orc, B, T):
     _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, T) for b in range(B)])
 
 
-@pytest.mark.parametrize("variant", ["orders234", "orders12_bf16", "order2_only"])
+@pytest.mark.parametrize("variant", ["orders234", "orders12_bf16", "order2_only",
+                                     "rowdim96_bf16_dmem"])
 def test_forward_other_order_sets(orc, variant):
     """Dilation follows the largest order (4, 2, 2)."""
     if variant == "orders234":
@@ -171,11 +179,14 @@ def test_forward_other_order_sets(orc, variant):
     elif variant == "orders12_bf16":
         w = W.get("engram_small").replace(orders=(1, 2), heads=4, batch=2, seq_len=300,
                                           hidden=256)
-    else:
+    elif variant == "order2_only":
         w = W.get("tiny").replace(orders=(2,), heads=3, explicit_rows=(), batch=2, seq_len=50)
+    else:  # 96-wide rows: the projection cannot gather K steps itself
+        w = W.get("engram_small").replace(heads=2, row_dim=96, batch=2, seq_len=200,
+                                          hidden=128)
     print(f"[forward] {variant}", flush=True)
     ids, hist = W.make_ids(w)
-    inp = _device_inputs(w, ids, hist)
+    inp = _device_inputs(w, ids, hist, layout="d_mem" if "dmem" in variant else "mem_d")
     out, gates, err = _run(w, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates,
                    [(b, 0, w.seq_len) for b in range(w.batch)])

@@ -99,26 +99,31 @@ def _synthetic_memory(w, n, seed):
     return rng.normal_values(seed, np.arange(n * w.mem_dim), 0.02, w.dtype).reshape(n, w.mem_dim)
 
 
-@pytest.mark.parametrize("name,n,shared,random_gamma", [
-    ("tiny", 256, True, False),
-    ("tiny", 37, True, True),
-    ("engram_small", 300, True, False),
-    ("engram_small", 1500, True, True),
-    ("qwen_decode", 256, True, False),
-    ("qwen_decode", 1091, True, True),
-    ("qwen_multibranch_zipf13", 200, False, False),
-    ("qwen_multibranch_zipf13", 1029, False, True),
+@pytest.mark.parametrize("name,n,shared,random_gamma,layout", [
+    ("tiny", 256, True, False, "mem_d"),
+    ("tiny", 37, True, True, "d_mem"),
+    ("engram_small", 300, True, False, "mem_d"),
+    ("engram_small", 1500, True, True, "mem_d"),
+    ("engram_small", 700, True, True, "d_mem"),
+    ("qwen_decode", 256, True, False, "mem_d"),
+    ("qwen_decode", 256, True, False, "d_mem"),
+    ("qwen_decode", 1091, True, True, "mem_d"),
+    ("qwen_decode", 1091, True, True, "d_mem"),
+    ("qwen_decode", 4133, True, False, "d_mem"),
+    ("qwen_multibranch_zipf13", 200, False, False, "mem_d"),
+    ("qwen_multibranch_zipf13", 1029, False, True, "mem_d"),
+    ("qwen_multibranch_zipf13", 1029, False, True, "d_mem"),
 ])
-def test_gate_op(orc, name, n, shared, random_gamma):
+def test_gate_op(orc, name, n, shared, random_gamma, layout):
     H = G.H()
     w = W.get(name)
-    print(f"[gate] {name} n={n} shared={shared} gamma={random_gamma}", flush=True)
-    cfg = G.config(w)
+    print(f"[gate] {name} n={n} shared={shared} gamma={random_gamma} layout={layout}", flush=True)
+    cfg = G.config(w, layout)
     e = _synthetic_memory(w, n, 77 + n)
     nbh = 1 if shared else w.n_branches
     hid = rng.normal_values(91 + n, np.arange(n * nbh * w.hidden), 1.0, w.dtype).reshape(
         n, nbh, w.hidden)
-    wk, wv = G.weights(w)
+    wk, wv = G.weights(w, layout)
     gam = G.gammas(w, random_gamma)
     gates = torch.empty((n, w.n_branches), dtype=torch.float32, device="cuda")
     u = torch.empty((n, w.n_branches, w.hidden), dtype=G.tdtype(w), device="cuda")
@@ -126,9 +131,9 @@ def test_gate_op(orc, name, n, shared, random_gamma):
                  gates, u, gamma_q=gam["q"], gamma_k=gam["k"])
     torch.cuda.synchronize()
     e64 = W.to_f64(e, w.dtype)
-    wk_h = G.to_storage(wk)
+    wk_h, wv_h = G.host_weights(wk, wv, layout)
     k = np.stack([orc.project(e64, wk_h[b], w.dtype) for b in range(w.n_branches)], axis=1)
-    v = orc.project(e64, G.to_storage(wv), w.dtype)
+    v = orc.project(e64, wv_h, w.dtype)
     g_ref = orc.gate(hid, w.dtype, k, G.to_storage(gam["q"]), G.to_storage(gam["k"]), w.rms_eps)
     u_ref = orc.gated_value(g_ref, v)
     assert G.rel_err(gates.cpu().numpy(), g_ref) < G.TOL

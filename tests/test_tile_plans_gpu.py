@@ -1,0 +1,76 @@
+"""Every tile plan of the projection kernel that streams operands straight
+into LDS (W stored [d, mem]) against the oracle, at ragged token counts:
+the op-level gate on a dense memory matrix and the forward pass that hashes
+and gathers inside the projection.  NGRAM_ASYNC_TILE selects the plan."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_support as G
+from synth import device as SD
+from synth import rng
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+PLANS = ["0", "1", "2", "3", "4", "5"]
+
+
+@pytest.fixture
+def plan_env(request):
+    old = os.environ.get("NGRAM_ASYNC_TILE")
+    os.environ["NGRAM_ASYNC_TILE"] = request.param
+    yield request.param
+    if old is None:
+        del os.environ["NGRAM_ASYNC_TILE"]
+    else:
+        os.environ["NGRAM_ASYNC_TILE"] = old
+
+
+@pytest.mark.parametrize("plan_env", PLANS, indirect=True)
+@pytest.mark.parametrize("n", [77, 1000, 4133])
+def test_gate_each_plan(orc, plan_env, n):
+    H = G.H()
+    w = W.get("qwen_multibranch_zipf13")
+    print(f"[plan {plan_env}] gate n={n}", flush=True)
+    cfg = G.config(w, "d_mem")
+    e = rng.normal_values(31 + n, np.arange(n * w.mem_dim), 0.02, "bf16").reshape(n, w.mem_dim)
+    hid = rng.normal_values(32 + n, np.arange(n * 4 * w.hidden), 1.0, "bf16").reshape(n, 4, w.hidden)
+    wk, wv = G.weights(w, "d_mem")
+    gates = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    u = torch.empty((n, 4, w.hidden), dtype=torch.bfloat16, device="cuda")
+    H.ngram_gate(cfg, G.to_device(hid, w), w.hidden, G.to_device(e, w), wk, wv, gates, u)
+    torch.cuda.synchronize()
+    e64 = W.to_f64(e, "bf16")
+    wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
+    k = np.stack([orc.project(e64, wk_h[b], "bf16") for b in range(4)], axis=1)
+    v = orc.project(e64, wv_h, "bf16")
+    g_ref = orc.gate(hid, "bf16", k, eps=w.rms_eps)
+    assert G.rel_err(gates.cpu().numpy(), g_ref) < G.TOL
+    assert G.rel_err(G.to_f64(u), orc.gated_value(g_ref, v)) < G.TOL
+
+
+@pytest.mark.parametrize("plan_env", PLANS, indirect=True)
+def test_forward_each_plan(orc, plan_env):
+    H = G.H()
+    w = W.get("qwen_prefill").replace(batch=3, seq_len=1100)
+    print(f"[plan {plan_env}] forward", flush=True)
+    cfg = G.config(w, "d_mem")
+    ids, _ = W.make_ids(w)
+    wk, wv = G.weights(w, "d_mem")
+    hidden = SD.make_hidden(w, ids.size)
+    out = torch.empty((3, 1100, 1, w.hidden), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((3, 1100, 1), dtype=torch.float32, device="cuda")
+    H.ngram_forward(cfg, torch.from_numpy(ids).cuda(), torch.from_numpy(W.make_lut(w)).cuda(),
+                    G.tables(w), hidden, 0, wk, wv, G.conv_w(w), out, gates=gates)
+    torch.cuda.synchronize()
+    wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
+    for b, start in [(0, 0), (1, 517), (2, 1100 - 20)]:
+        ref = G.oracle_forward_window(orc, w, ids, None, b, start, 20,
+                                      lambda toks: W.hidden_values(w, toks), wk_h, wv_h,
+                                      W.conv_weight_values(w))
+        got = G.to_f64(out[b, start:start + 20])
+        assert G.rel_err(got, ref["delta"]) < G.TOL
+        assert G.rel_err(gates[b, start:start + 20].cpu().numpy(), ref["gate"]) < G.TOL
