@@ -140,7 +140,10 @@ def source_sha(paths):
 STAGE_SOURCES = {
     "hash": ["hashed_gram_embedding_amd/csrc/ids.hip"],
     "gather": ["hashed_gram_embedding_amd/csrc/gather.hip"],
-    "projection": ["hashed_gram_embedding_amd/csrc/project.hip"],
+    "projection": ["hashed_gram_embedding_amd/csrc/project.hip",
+                   "hashed_gram_embedding_amd/csrc/project_async.hip",
+                   "hashed_gram_embedding_amd/csrc/epilogue.h",
+                   "hashed_gram_embedding_amd/csrc/hashing.h"],
     "gate_conv": ["hashed_gram_embedding_amd/csrc/finalize.hip"],
 }
 

@@ -3,6 +3,7 @@
 // of the layer runs in the kernels of ids.hip, gather.hip, project.hip and
 // finalize.hip; this file launches them on the caller's stream.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "internal.h"
@@ -106,6 +107,30 @@ bool async_path(const ngram_config* c) {
 // 64-wide K step lies within one table row.
 bool fused_gather(const ngram_config* c) { return async_path(c) && c->row_dim % 64 == 0; }
 
+// Decode (one new token per sequence): E is materialised once and the
+// projection is split along K into raw fp32 partial tiles, so many more
+// workgroups stream the weights; the decode finalize sums the splits.
+bool decode_path(const ngram_config* c, int32_t T) { return async_path(c) && T == 1; }
+
+// Split factor and tile plan of the decode projection (NGRAM_DECODE_SPLIT
+// and NGRAM_DECODE_TILE override them: tuning knobs).
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  if (!e || !*e) return dflt;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  return (*end == 0 && v >= 0 && v < 1000) ? (int)v : dflt;
+}
+int decode_tile(void) { return env_int("NGRAM_DECODE_TILE", 2); }
+int decode_split(const ngram_config* c, int tile) {
+  const int bk = tile == 0 ? 32 : 64;
+  const int nk = c->mem_dim / bk;
+  int s = env_int("NGRAM_DECODE_SPLIT", 1);
+  if (s < 1) s = 1;
+  while (s > 1 && nk % s != 0) --s;  // must divide the number of K steps
+  return s;
+}
+
 HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
   HashArgs a;
   memset(&a, 0, sizeof a);
@@ -129,17 +154,31 @@ HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t row_idx = 0, e = 0, v = 0, parts = 0, total = 0;
+  size_t row_idx = 0, e = 0, v = 0, parts = 0, split = 0, total = 0;
   ProjPlan plan;       // plan.np is the number of partials per row on every path
   int async = -1;      // async projection tile plan, -1 when not used
+  int k_split = 0;     // decode path: K splits (0: not the decode path)
   int64_t v_stride = 0;  // fp32 elements between V rows
   int64_t v_offset = 0;  // fp32 elements from the V buffer to row 0's values
 };
 
 // forward: the forward pass (row ids and E live in the workspace unless the
-// projection gathers them itself).
-Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward) {
+// projection gathers them itself).  T: tokens per sequence (decode when 1).
+Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward, int32_t T = 0) {
   Layout L;
+  if (forward && decode_path(c, T)) {
+    L.async = decode_tile();
+    L.k_split = decode_split(c, L.async);
+    L.plan.np = 1;
+    size_t off = 0;
+    L.e = off;
+    off = align_up(off + (size_t)n_tok * c->mem_dim * esize_of(c->table_dtype));
+    L.split = off;
+    off = align_up(off + (size_t)L.k_split * n_tok * (c->n_branches + 1) * c->hidden_dim *
+                             sizeof(float));
+    L.total = off;
+    return L;
+  }
   const int dt = c->table_dtype;
   const int nb = c->n_branches, d = c->hidden_dim;
   L.plan = plan_projection(dt, n_tok, d);
@@ -403,7 +442,7 @@ int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t
 
 size_t ngram_forward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T) {
   if (validate(cfg) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
-  return layout_for(cfg, (int64_t)B * T, true).total;
+  return layout_for(cfg, (int64_t)B * T, true, T).total;
 }
 
 int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
@@ -431,13 +470,52 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u,
                         (const void*)conv_state, (const void*)out, (const void*)gates})
     if (!aligned16(p)) return NGRAM_EALIGN;
-  const Layout L = layout_for(cfg, n_tok, true);
+  const Layout L = layout_for(cfg, n_tok, true, T);
   if (!workspace) return NGRAM_EWORKSPACE;
   if (workspace_bytes < L.total) return NGRAM_EWORKSPACE;
   if (!aligned16(workspace)) return NGRAM_EALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if (L.k_split > 0) {
+    // decode: hash + gather -> E, split-K projection, decode finalize
+    const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+    void* e = ws + L.e;
+    float* split = reinterpret_cast<float*>(ws + L.split);
+    mark_stage(0, s);
+    st = hip_status(launch_hash_gather(cfg->table_dtype, raw_ids, B, T, history, lut, ha,
+                                       cfg->n_tables, cfg->row_dim, tp, e, err_flag, s));
+    if (st) return st;
+    mark_stage(1, s);
+    mark_stage(2, s);
+    ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
+                            gamma_k, ws, L, n_tok);
+    AsyncProjArgs aa = async_args(cfg, pa);
+    aa.epi.np = 1;
+    aa.k_split = L.k_split;
+    aa.split_out = split;
+    st = hip_status(launch_projection_split(L.async, aa, s));
+    if (st) return st;
+    mark_stage(3, s);
+    ConvArgs ca = conv_args_base(cfg);
+    ca.conv_w = conv_w;
+    ca.gamma_u = gamma_u;
+    ca.gamma_q = gamma_q;
+    ca.gamma_k = gamma_k;
+    ca.state = conv_state;
+    ca.hidden = hidden;
+    ca.h_tok_stride = h_tok;
+    ca.h_branch_stride = hidden_branch_stride;
+    ca.out = out;
+    ca.gates = gates;
+    ca.B = B;
+    ca.T = T;
+    ca.dil = cfg->conv_dilation;
+    ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
+    st = hip_status(launch_decode_finalize(cfg->act_dtype, L.k_split, split, ca, s));
+    mark_stage(NGRAM_N_STAGES, s);
+    return st;
+  }
   int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
   void* e = ws + L.e;
 

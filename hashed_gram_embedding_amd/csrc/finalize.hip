@@ -213,6 +213,104 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
   }
 }
 
+// Decode (one new token per sequence): sum the K splits of the projection,
+// then gate, U, RMSNorm(U), the conv taps (the current position's and the
+// caller's state rows, or zeros, for the earlier ones) and the output.  One
+// workgroup per token; the token's (nb+1)*d columns are read twice from L2,
+// once for the row reductions and once for the outputs.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const float* __restrict__ split,
+                                                              int32_t k_split, int32_t dil) {
+  __shared__ float s_red[4][3 * NGRAM_MAX_BRANCHES + 1];
+  __shared__ float s_tot[3 * NGRAM_MAX_BRANCHES + 1];
+  const int64_t tok = blockIdx.x;  // T == 1: token = sequence
+  const int nb = a.nb, d = a.d;
+  const int64_t ntot = (int64_t)(nb + 1) * d;
+  const int64_t sstride = (int64_t)a.B * ntot;
+  const float* __restrict__ P = split + tok * ntot;
+  const T* __restrict__ H = static_cast<const T*>(a.hidden);
+  const T* __restrict__ GQ = static_cast<const T*>(a.gamma_q);
+  const T* __restrict__ GK = static_cast<const T*>(a.gamma_k);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  auto col4 = [&](int64_t off, int c) {  // sum of the splits, 4 columns
+    float4 x = *reinterpret_cast<const float4*>(P + off + c);
+    for (int s = 1; s < k_split; ++s) {
+      const float4 y = *reinterpret_cast<const float4*>(P + s * sstride + off + c);
+      x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+    }
+    return x;
+  };
+
+  // pass 1: row reductions (dot, sum k^2, sum h^2 per branch; sum v^2)
+  float acc[3 * NGRAM_MAX_BRANCHES + 1];
+#pragma unroll
+  for (int q = 0; q < 3 * NGRAM_MAX_BRANCHES + 1; ++q) acc[q] = 0.0f;
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    const float4 gq = GQ ? Elem<T>::load4(GQ, c) : f4(1.0f);
+    const float4 gk = GK ? Elem<T>::load4(GK, c) : f4(1.0f);
+#pragma unroll
+    for (int br = 0; br < NGRAM_MAX_BRANCHES; ++br) {
+      if (br < nb) {
+        const float4 k = col4((int64_t)br * d, c);
+        const float4 h = Elem<T>::load4(H, tok * a.h_tok_stride + br * a.h_branch_stride + c);
+        acc[3 * br] += gq.x * gk.x * h.x * k.x + gq.y * gk.y * h.y * k.y + gq.z * gk.z * h.z * k.z +
+                       gq.w * gk.w * h.w * k.w;
+        acc[3 * br + 1] += k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w;
+        acc[3 * br + 2] += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
+      }
+    }
+    const float4 v = col4((int64_t)nb * d, c);
+    acc[3 * NGRAM_MAX_BRANCHES] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+#pragma unroll
+  for (int q = 0; q < 3 * NGRAM_MAX_BRANCHES + 1; ++q) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off);
+    if (lane == 0) s_red[wave][q] = acc[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < 3 * NGRAM_MAX_BRANCHES + 1)
+    s_tot[threadIdx.x] = s_red[0][threadIdx.x] + s_red[1][threadIdx.x] + s_red[2][threadIdx.x] +
+                         s_red[3][threadIdx.x];
+  __syncthreads();
+
+  const float fd = (float)d;
+  const float mv = s_tot[3 * NGRAM_MAX_BRANCHES] / fd;
+  const T* __restrict__ CW = static_cast<const T*>(a.conv_w);
+  const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
+  T* __restrict__ OUT = static_cast<T*>(a.out);
+  const int halo = 3 * dil;
+  for (int br = 0; br < nb; ++br) {
+    const float z = s_tot[3 * br] /
+                    (sqrtf(s_tot[3 * br + 2] / fd + a.eps) * sqrtf(s_tot[3 * br + 1] / fd + a.eps) *
+                     sqrtf(fd));
+    const float al = 1.0f / (1.0f + expf(-z));
+    const float sc = al / sqrtf(al * al * mv + a.eps);
+    if (a.gates && threadIdx.x == 0) a.gates[tok * nb + br] = al;
+    // pass 2: outputs
+    for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+      const float4 v = col4((int64_t)nb * d, c);
+      const float4 gu = GU ? Elem<T>::load4(GU, c) : f4(1.0f);
+      float4 C = mul4(Elem<T>::load4(CW, c), mul4(mul4(gu, v), f4(sc)));
+      if (a.state) {
+        for (int i = 1; i < 4; ++i) {
+          const float4 st = *reinterpret_cast<const float4*>(
+              a.state + ((tok * halo + halo - i * dil) * nb + br) * d + c);
+          C = fma4(Elem<T>::load4(CW, (int64_t)i * d + c), st, C);
+        }
+      }
+      float4 D = make_float4(fmaf(al, v.x, silu(C.x)), fmaf(al, v.y, silu(C.y)),
+                             fmaf(al, v.z, silu(C.z)), fmaf(al, v.w, silu(C.w)));
+      if (a.add_residual) {
+        const float4 h = Elem<T>::load4(H, tok * a.h_tok_stride + br * a.h_branch_stride + c);
+        D = make_float4(D.x + h.x, D.y + h.y, D.z + h.z, D.w + h.w);
+      }
+      Elem<T>::store4(OUT, (tok * nb + br) * d + c, D);
+    }
+  }
+}
+
 template <typename T, bool FUSED>
 hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
   const int tiles = (a.T + a.tile - 1) / a.tile;
@@ -248,6 +346,16 @@ hipError_t launch_op_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t
   if (a.B == 0 || a.T == 0) return hipSuccess;
   return dtype == NGRAM_BF16 ? launch_conv_t<bf16_bits, false>(dil, a, s)
                              : launch_conv_t<float, false>(dil, a, s);
+}
+
+hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split, const ConvArgs& a,
+                                  hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  if (dtype == NGRAM_BF16)
+    decode_finalize_kernel<bf16_bits><<<(unsigned)a.B, 256, 0, s>>>(a, split, k_split, a.dil);
+  else
+    decode_finalize_kernel<float><<<(unsigned)a.B, 256, 0, s>>>(a, split, k_split, a.dil);
+  return hipGetLastError();
 }
 
 int conv_tile_for(int32_t T) { return T < kMaxTile ? T : kMaxTile; }

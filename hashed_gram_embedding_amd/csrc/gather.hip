@@ -10,7 +10,7 @@
 // stores (up to 8 chunks per lane in flight) to keep enough random row
 // fetches outstanding; the table base pointers sit in LDS because the lanes
 // of one wave touch different tables.
-#include "internal.h"
+#include "hashing.h"
 
 namespace ngram {
 namespace {
@@ -56,7 +56,71 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   }
 }
 
+// Hash + gather in one pass, one wavefront per token: every lane reads the
+// token's context ids (the same few words, served by the cache), lane j
+// hashes table j, and each 16-byte chunk's lane fetches its table's row id
+// from lane j with a cross-lane read before the loads above.
+__global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restrict__ ids,
+                                                          int32_t B, int32_t T,
+                                                          const int32_t* __restrict__ hist,
+                                                          const int32_t* __restrict__ lut, HashArgs h,
+                                                          int32_t row_chunks, TablePtrs tabs,
+                                                          uint4* __restrict__ mem,
+                                                          int32_t* __restrict__ err) {
+  __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
+  if (threadIdx.x < NGRAM_MAX_TABLES)
+    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[threadIdx.x < h.n_tables ? threadIdx.x : 0]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int waves_per_block = blockDim.x >> 6;
+  const int64_t n_tok = (int64_t)B * T;
+  const int64_t wstride = (int64_t)gridDim.x * waves_per_block;
+  const int32_t chunks = h.n_tables * row_chunks;
+  const int jl = lane < h.n_tables ? lane : 0;
+  const int order_l = h.orders[jl / h.heads];
+  for (int64_t tok = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6); tok < n_tok;
+       tok += wstride) {
+    const int32_t b = (int32_t)(tok / T);
+    const int32_t t = (int32_t)(tok - (int64_t)b * T);
+    uint64_t c[NGRAM_MAX_ORDER];
+    context_ids<true>(ids, tok, b, t, hist, lut, h, err, c);
+    const int32_t my_row = (int32_t)table_row(h, jl, order_l, c);
+    uint4* dst = mem + tok * chunks;
+    for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
+      uint4 v[kGatherUnroll];
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const int q = base + u * 64 + lane;
+        const int j = q / row_chunks;
+        const int64_t r = __shfl(my_row, j < h.n_tables ? j : 0);
+        if (q < chunks) v[u] = s_tab[j][r * row_chunks + (q - j * row_chunks)];
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const int q = base + u * 64 + lane;
+        if (q < chunks) dst[q] = v[u];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t T,
+                              const int32_t* hist, const int32_t* lut, const HashArgs& h,
+                              int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,
+                              int32_t* err, hipStream_t s) {
+  const int esize = dtype == NGRAM_BF16 ? 2 : 4;
+  const int32_t row_chunks = row_dim * esize / 16;
+  (void)n_tables;
+  const int64_t n_tok = (int64_t)B * T;
+  int64_t blocks = (n_tok + 3) / 4;
+  if (blocks > 262144) blocks = 262144;
+  if (blocks < 1) blocks = 1;
+  hash_gather_kernel<<<(unsigned)blocks, 256, 0, s>>>(ids, B, T, hist, lut, h, row_chunks, t,
+                                                      static_cast<uint4*>(mem), err);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
                          int32_t row_dim, const TablePtrs& t, void* mem, hipStream_t s) {

@@ -121,6 +121,11 @@ struct AsyncProjArgs {
   const bf16_bits* wv;       // [d, K]
   EpiArgs epi;
   int32_t K, tiles_m, tiles_n, group_m;
+  // split-K (k_split > 1): workgroup ks covers K steps [ks*K/k_split, ...)
+  // and stores its raw fp32 tile into split_out[ks][M][(nb+1)*d]; no
+  // epilogue math (the decode finalize sums the splits)
+  int32_t k_split;
+  float* split_out;
 };
 
 // Gate + gated value + conv block over a [B, T] token grid.
@@ -142,6 +147,9 @@ struct ConvArgs {
   int32_t B, T, nb, d, tile;
   float eps;
   int32_t add_residual;
+  int32_t dil;                // conv dilation (decode finalize)
+  const void* gamma_q;        // decode finalize: the gate's gains
+  const void* gamma_k;
 };
 
 // ---------------------------------------------------------------------------
@@ -167,6 +175,14 @@ hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a,
 int async_plan(int64_t M);
 int async_wave_cols(int plan);
 hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s);
+// split-K raw-tile variant for small M (decode); E given densely
+hipError_t launch_projection_split(int plan, const AsyncProjArgs& a, hipStream_t s);
+hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t T,
+                              const int32_t* hist, const int32_t* lut, const HashArgs& h,
+                              int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,
+                              int32_t* err, hipStream_t s);
+hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split, const ConvArgs& a,
+                                  hipStream_t s);
 
 hipError_t launch_gate_values(int dtype, const ConvArgs& a, int64_t M, hipStream_t s);
 hipError_t launch_fused_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s);

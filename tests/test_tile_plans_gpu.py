@@ -74,3 +74,56 @@ def test_forward_each_plan(orc, plan_env):
         got = G.to_f64(out[b, start:start + 20])
         assert G.rel_err(got, ref["delta"]) < G.TOL
         assert G.rel_err(gates[b, start:start + 20].cpu().numpy(), ref["gate"]) < G.TOL
+
+
+@pytest.fixture
+def decode_env(request):
+    tile, split = request.param
+    old = {k: os.environ.get(k) for k in ("NGRAM_DECODE_TILE", "NGRAM_DECODE_SPLIT")}
+    os.environ["NGRAM_DECODE_TILE"] = tile
+    os.environ["NGRAM_DECODE_SPLIT"] = split
+    yield request.param
+    for k, v in old.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+@pytest.mark.parametrize("decode_env", [("2", "1"), ("2", "4"), ("2", "8"), ("5", "2"),
+                                        ("0", "16"), ("1", "5")], indirect=True)
+@pytest.mark.parametrize("name", ["qwen_decode", "qwen_multibranch_zipf13"])
+def test_decode_path_splits(orc, decode_env, name):
+    """One new token per sequence (T = 1): hash+gather, split-K projection and
+    the decode finalize, with a populated conv state, the residual flag and
+    random RMSNorm gains."""
+    H = G.H()
+    w = W.get(name).replace(batch=64, seq_len=1, history_len=2)
+    print(f"[decode tile/split {decode_env}] {name}", flush=True)
+    cfg = G.config(w, "d_mem")
+    ids, hist = W.make_ids(w)
+    wk, wv = G.weights(w, "d_mem")
+    nb, d, halo = w.n_branches, w.hidden, 3 * w.max_order
+    hidden = SD.make_hidden(w, ids.size)
+    gam = G.gammas(w, True)
+    state = rng.normal_f32(77, np.arange(w.batch * halo * nb * d), 1.0).reshape(w.batch, halo, nb, d)
+    out = torch.empty((w.batch, 1, nb, d), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((w.batch, 1, nb), dtype=torch.float32, device="cuda")
+    H.ngram_forward(cfg, torch.from_numpy(ids).cuda(), torch.from_numpy(W.make_lut(w)).cuda(),
+                    G.tables(w), hidden, 0 if nb == 1 else d, wk, wv, G.conv_w(w), out,
+                    history=torch.from_numpy(hist).cuda(), gamma_q=gam["q"], gamma_k=gam["k"],
+                    gamma_u=gam["u"], conv_state=torch.from_numpy(state).cuda(), flags=1,
+                    gates=gates)
+    torch.cuda.synchronize()
+    wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
+    gh = {k: G.to_storage(v) for k, v in gam.items()}
+    ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
+                      w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
+                      W.hidden_values(w, np.arange(ids.size)), wk_h, wv_h,
+                      W.conv_weight_values(w), "bf16", gamma_q=gh["q"], gamma_k=gh["k"],
+                      gamma_u=gh["u"], eps=w.rms_eps, conv_state=state.astype(np.float64))
+    want = ref["delta"] + W.to_f64(W.hidden_values(w, np.arange(ids.size)), "bf16").reshape(
+        w.batch, -1, d)[:, :1 if nb == 1 else nb]
+    got = G.to_f64(out).reshape(want.shape)
+    assert G.rel_err(got, want) < G.TOL
+    assert G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"]) < G.TOL
