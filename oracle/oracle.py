@@ -11,6 +11,7 @@ uint16 bit patterns for bf16 tensors (``dtype`` says which).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Callable, Optional, Sequence
@@ -32,20 +33,37 @@ def lib():
         if not os.path.exists(LIB_PATH):
             from . import build as _b
             _b.build()
-        L = ctypes.CDLL(LIB_PATH)
-        L.orc_num_threads.restype = ctypes.c_int
-        L.orc_set_num_threads.argtypes = [ctypes.c_int]
-        L.orc_compress.restype = _i64
-        L.orc_compress.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _p]
-        L.orc_hash.argtypes = [_p, _i32, _i32, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p]
-        L.orc_gather.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p]
-        L.orc_project.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p]
-        L.orc_gate.argtypes = [_p, _i32, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _f64, _p]
-        L.orc_gated_value.argtypes = [_p, _p, _i64, _i32, _i32, _p]
-        L.orc_conv_block.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _i32, _p,
-                                     _f64, _p, _p]
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Temporarily route every step through another build of the oracle
+    source (the mutation tests plant mistakes in a copy)."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_num_threads.argtypes = [ctypes.c_int]
+    L.orc_compress.restype = _i64
+    L.orc_compress.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _p]
+    L.orc_hash.argtypes = [_p, _i32, _i32, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p]
+    L.orc_gather.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p]
+    L.orc_project.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p]
+    L.orc_gate.argtypes = [_p, _i32, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _f64, _p]
+    L.orc_gated_value.argtypes = [_p, _p, _i64, _i32, _i32, _p]
+    L.orc_conv_block.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _i32, _p,
+                                 _f64, _p, _p]
+    return L
 
 
 def _ptr(a: Optional[np.ndarray]):

@@ -330,6 +330,13 @@ def test_gate_gammas_enter_the_dot(orc):
     # only one coordinate survives: q.k^ = 1*1 (both rms = 1 with eps 0) -> z = 1/sqrt(d)
     got = orc.gate(h, "f32", k, gamma_q=gq, eps=0.0)[0, 0]
     assert abs(got - 1 / (1 + math.exp(-1 / math.sqrt(d)))) < 1e-15
+    # the same through the key's gain
+    got = orc.gate(h, "f32", k, gamma_k=gq, eps=0.0)[0, 0]
+    assert abs(got - 1 / (1 + math.exp(-1 / math.sqrt(d)))) < 1e-15
+    # both gains 2: q^ = k^ = 2 (all ones, rms 1) -> dot = 4d -> z = 4 sqrt(d)
+    two = np.full(d, 2.0, dtype=np.float32)
+    got = orc.gate(h, "f32", k, gamma_q=two, gamma_k=two, eps=0.0)[0, 0]
+    assert abs(got - 1 / (1 + math.exp(-4 * math.sqrt(d)))) < 1e-15
 
 
 def test_gated_value(orc):
@@ -472,3 +479,14 @@ def test_forward_decode_with_history_equals_prefill(orc):
         assert np.array_equal(step[key].reshape(5, -1), full[key].reshape(5, 3, -1)[:, 2]), key
     # Delta at position 2 uses only tap 0 (positions -1, -4, -7 are outside)
     assert np.array_equal(step["delta"].reshape(5, -1), full["delta"].reshape(5, 3, -1)[:, 2])
+
+
+def test_hash_hand_worked_examples(orc):
+    g = _golden("hash_worked_example.json")
+    for case in g["cases"]:
+        mult = np.zeros((16, 4), dtype=np.uint64)
+        mult[0, 0] = np.uint64(int(case["A"][0]))
+        mult[0, 1] = np.uint64(int(case["A"][1]))
+        comp = np.array([case["ids"]], dtype=np.int32)
+        r = orc.hash_rows(comp, None, (2,), 1, [case["p"]], mult)
+        assert r[:, 0].tolist() == case["rows"], case["work"]
