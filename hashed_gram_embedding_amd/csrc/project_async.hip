@@ -85,19 +85,19 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int ti
   n = sn - seg * tiles_n;
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, bool GATHER, bool SPLIT = false>
-__global__ __launch_bounds__(256, 1) void proj_async_kernel(AsyncProjArgs a) {
-  constexpr int WGN = 4 / WGM;
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool GATHER, bool SPLIT = false>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProjArgs a) {
+  constexpr int NW = WGM * WGN;          // waves per workgroup
   constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
   constexpr int RPI = 64 / CH;          // rows covered by one wave-wide copy
-  constexpr int A_INS = BM / (RPI * 4);  // copies per wave per stage
-  constexpr int B_INS = BN / (RPI * 4);
+  constexpr int A_INS = BM / (RPI * NW);  // copies per wave per stage
+  constexpr int B_INS = BN / (RPI * NW);
   constexpr int PER_STAGE = A_INS + B_INS;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
   constexpr int A_ELEMS = BM * BK;
   constexpr int STAGE_ELEMS = (BM + BN) * BK;
-  static_assert(A_INS * RPI * 4 == BM && B_INS * RPI * 4 == BN, "tile / copy shape");
+  static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "tile / copy shape");
   static_assert(MI * 32 == WTM && NI * 32 == WTN, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void proj_async_kernel(AsyncProjArgs a) {
   const bf16_bits* __restrict__ W = seg < ep.nb ? a.wk + (int64_t)seg * d * K : a.wv;
 
   if (GATHER) {
-    for (int i = tid; i < BM; i += 256) {
+    for (int i = tid; i < BM; i += 64 * NW) {
       int64_t tok = m0 + i;
       if (tok > M - 1) tok = M - 1;
       const int32_t b = (int32_t)(tok / a.T);
@@ -286,9 +286,9 @@ __global__ __launch_bounds__(256, 1) void proj_async_kernel(AsyncProjArgs a) {
   gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
-  constexpr int WTN = BN / (4 / WGM);  // columns per wave = width of one row partial
+  constexpr int WTN = BN / WGN;  // columns per wave = width of one row partial
   AsyncProjArgs a = a0;
   // the host sized the partials for this tile's wave width; refuse to launch
   // (instead of writing past the workspace) if the two ever disagree
@@ -297,13 +297,15 @@ hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
   a.tiles_n = (a.epi.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
   if (gather)
-    proj_async_kernel<BM, BN, BK, STAGES, WGM, true><<<(unsigned)blocks, 256, 0, s>>>(a);
+    proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>
+        <<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
   else
-    proj_async_kernel<BM, BN, BK, STAGES, WGM, false><<<(unsigned)blocks, 256, 0, s>>>(a);
+    proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false>
+        <<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 hipError_t launch_split_t(const AsyncProjArgs& a0, hipStream_t s) {
   AsyncProjArgs a = a0;
   if (a.k_split < 1 || (a.K / BK) % a.k_split != 0 || a.split_out == nullptr)
@@ -311,36 +313,47 @@ hipError_t launch_split_t(const AsyncProjArgs& a0, hipStream_t s) {
   a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
   a.tiles_n = (a.epi.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n * a.k_split;
-  proj_async_kernel<BM, BN, BK, STAGES, WGM, false, true><<<(unsigned)blocks, 256, 0, s>>>(a);
+  proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>
+      <<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // One table of tile plans serves both the launch and the host's partial
 // count, so the two cannot drift apart.
-#define NGRAM_ASYNC_PLANS(X) \
-  X(0, 256, 128, 32, 4, 2)   \
-  X(1, 128, 128, 64, 4, 2)   \
-  X(2, 64, 64, 64, 4, 2)     \
-  X(3, 256, 128, 64, 3, 2)   \
-  X(4, 128, 64, 64, 4, 2)    \
-  X(5, 64, 128, 64, 4, 2)
+#define NGRAM_ASYNC_PLANS(X)  \
+  X(0, 256, 128, 32, 4, 2, 2) \
+  X(1, 128, 128, 64, 4, 2, 2) \
+  X(2, 64, 64, 64, 4, 2, 2)   \
+  X(3, 256, 128, 64, 3, 2, 2) \
+  X(4, 128, 64, 64, 4, 2, 2)  \
+  X(5, 64, 128, 64, 4, 2, 2)  \
+  X(6, 256, 256, 32, 2, 2, 4) \
+  X(7, 256, 256, 64, 2, 2, 4) \
+  X(8, 128, 128, 64, 2, 2, 2) \
+  X(9, 256, 128, 32, 2, 2, 2) \
+  X(10, 256, 256, 32, 4, 2, 4) \
+  X(11, 256, 256, 64, 2, 4, 2)
 
 }  // namespace
 
-// Tile plans (id, BM, BN, K step, ring depth, wave rows; 4 waves): see
+// Tile plans (id, BM, BN, K step, ring depth, wave rows, wave columns): see
 // NGRAM_ASYNC_PLANS.  NGRAM_ASYNC_TILE=<id> overrides the choice (a tuning
 // knob).
 int async_plan(int64_t M) {
   const char* e = getenv("NGRAM_ASYNC_TILE");
-  if (e && *e >= '0' && *e <= '5' && e[1] == 0) return *e - '0';
-  if (M >= 4096) return 0;
-  if (M >= 1024) return 1;
+  if (e && *e) {
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (*end == 0 && v >= 0 && v <= 11) return (int)v;
+  }
+  if (M >= 8192) return 7;
+  if (M >= 1024) return 8;
   return 2;
 }
 
 int async_wave_cols(int plan) {
-#define NGRAM_WAVE_COLS(id, bm, bn, bk, st, wgm) \
-  if (plan == id) return bn / (4 / wgm);
+#define NGRAM_WAVE_COLS(id, bm, bn, bk, st, wgm, wgn) \
+  if (plan == id) return bn / wgn;
   NGRAM_ASYNC_PLANS(NGRAM_WAVE_COLS)
 #undef NGRAM_WAVE_COLS
   return -1;
@@ -348,8 +361,8 @@ int async_wave_cols(int plan) {
 
 hipError_t launch_projection_split(int plan, const AsyncProjArgs& a, hipStream_t s) {
   if (a.epi.M == 0) return hipSuccess;
-#define NGRAM_LAUNCH_SPLIT(id, bm, bn, bk, st, wgm) \
-  if (plan == id) return launch_split_t<bm, bn, bk, st, wgm>(a, s);
+#define NGRAM_LAUNCH_SPLIT(id, bm, bn, bk, st, wgm, wgn) \
+  if (plan == id) return launch_split_t<bm, bn, bk, st, wgm, wgn>(a, s);
   NGRAM_ASYNC_PLANS(NGRAM_LAUNCH_SPLIT)
 #undef NGRAM_LAUNCH_SPLIT
   return hipErrorInvalidValue;
@@ -357,8 +370,8 @@ hipError_t launch_projection_split(int plan, const AsyncProjArgs& a, hipStream_t
 
 hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s) {
   if (a.epi.M == 0) return hipSuccess;
-#define NGRAM_LAUNCH_PLAN(id, bm, bn, bk, st, wgm) \
-  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm>(gather, a, s);
+#define NGRAM_LAUNCH_PLAN(id, bm, bn, bk, st, wgm, wgn) \
+  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm, wgn>(gather, a, s);
   NGRAM_ASYNC_PLANS(NGRAM_LAUNCH_PLAN)
 #undef NGRAM_LAUNCH_PLAN
   return hipErrorInvalidValue;

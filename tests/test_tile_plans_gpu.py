@@ -15,7 +15,7 @@ from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-PLANS = ["0", "1", "2", "3", "4", "5"]
+PLANS = ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"]
 
 
 @pytest.fixture
