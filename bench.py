@@ -137,26 +137,46 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
+_CS = "hashed_gram_embedding_amd/csrc/"
+# kernel sources of each stage, per route: decode (one new token per
+# sequence) and the fused route of every other workload
 STAGE_SOURCES = {
-    "hash": ["hashed_gram_embedding_amd/csrc/ids.hip"],
-    "gather": ["hashed_gram_embedding_amd/csrc/gather.hip"],
-    "projection": ["hashed_gram_embedding_amd/csrc/project.hip",
-                   "hashed_gram_embedding_amd/csrc/project_async.hip",
-                   "hashed_gram_embedding_amd/csrc/epilogue.h",
-                   "hashed_gram_embedding_amd/csrc/hashing.h"],
-    "gate_conv": ["hashed_gram_embedding_amd/csrc/finalize.hip"],
+    ("gather", "decode"): [_CS + "gather.hip", _CS + "hashing.h"],
+    ("projection", "decode"): [_CS + "project_async.hip"],
+    ("gate_conv", "decode"): [_CS + "finalize.hip"],
+    ("projection", "fused"): [_CS + "project_async.hip", _CS + "epilogue.h",
+                              _CS + "hashing.h"],
+    ("gate_conv", "fused"): [_CS + "finalize.hip"],
+    ("hash", "f32"): [_CS + "ids.hip", _CS + "hashing.h"],
+    ("gather", "f32"): [_CS + "gather.hip"],
+    ("projection", "f32"): [_CS + "project.hip"],
+    ("gate_conv", "f32"): [_CS + "finalize.hip"],
 }
 
 
-def counter_traffic(stage: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when none were taken for this kernel source and workload."""
+def route(w) -> str:
+    if w.dtype == "f32":
+        return "f32"
+    return "decode" if w.seq_len == 1 else "fused"
+
+
+def stage_source_sha(stage: str, w):
+    srcs = STAGE_SOURCES.get((stage, route(w)))
+    return None if srcs is None else source_sha(srcs)
+
+
+def counter_traffic(stage: str, w):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for
+    a plain copy of known size), or None when none were taken for this kernel
+    source and workload."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as f:
         data = json.load(f)
-    rec = data.get(f"{stage}:{workload}")
-    if not rec or rec.get("source_sha") != source_sha(STAGE_SOURCES[stage]):
+    rec = data.get(f"{stage}:{w.name}")
+    sha = stage_source_sha(stage, w)
+    if not rec or sha is None or rec.get("source_sha") != sha:
         return None
     return float(rec["traffic_bytes"])
 
@@ -280,21 +300,36 @@ def main():
     ms_per_step = ms / args.steps
     tokens_per_s = w.n_tokens / (ms_per_step * 1e-3)
 
-    # ---- stage region: per-stage HIP events recorded by the library on the
-    # stream the kernels run on
+    # ---- stage region: each stage's kernels stamp their own begin / end times
+    # into a HIP event pair on the stream they run on (hipExtLaunchKernel), and
+    # a plain event pair brackets the whole step
     print(f"[bench] stage timing {args.stage_steps} steps", file=sys.stderr, flush=True)
     ns = setup.H.ngram.N_STAGES
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)]
+    # a spin kernel holds the GPU while the host enqueues the region (the
+    # hook costs host time per step), so the steps then run back to back and
+    # host submission gaps stay out of the event pairs
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(min(0.2, 3e-4 * args.stage_steps) * 2.5e9))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)]
            for _ in range(args.stage_steps)]
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.stage_steps)]
     for i in range(args.stage_steps):
         setup.H.ngram.ngram_set_timing_events(evs[i])
+        step_evs[i][0].record(stream)
         setup.step(i % setup.pool)
+        step_evs[i][1].record(stream)
+    mask = setup.H.ngram.ngram_timing_stage_mask()
     setup.H.ngram.ngram_set_timing_events(None)
     torch.cuda.synchronize()
-    stage_ms = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(ns)] for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[ns]) for e in evs])
     names = setup.H.ngram.STAGE_NAMES
-    stage_avg = {names[k]: float(stage_ms[:, k].mean()) for k in range(ns)}
+    stage_avg = {}
+    for k in range(ns):
+        if mask >> k & 1:
+            stage_avg[names[k]] = float(np.mean([e[2 * k].elapsed_time(e[2 * k + 1]) for e in evs]))
+        else:
+            stage_avg[names[k]] = 0.0  # absorbed into a later stage's kernel
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_evs])
     dom = max(stage_avg, key=stage_avg.get)
     dom_s = stage_avg[dom] * 1e-3
     a = stages_alg[dom]
@@ -307,7 +342,7 @@ def main():
         roof = {"bound": "hbm", "achieved": a["bytes"] / dom_s / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic(dom, w.name)
+    roof["traffic"] = counter_traffic(dom, w)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = a["bytes"]
     roof["algorithmic_flops"] = a["flops"]

@@ -10,9 +10,11 @@
 
 using namespace ngram;
 
+ngram::StageClock* ngram::g_open_stage = nullptr;
+
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 
 int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : 4; }
@@ -213,13 +215,34 @@ Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward, int32_t T 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 
-// Benchmark instrumentation (ngram_set_timing_events).
-hipEvent_t g_stage_events[NGRAM_N_STAGES + 1];
+// Benchmark instrumentation (ngram_set_timing_events): stage(i) closes the
+// open stage and opens stage i; the kernels launched while it is open stamp
+// the stage's event pair (launch() in internal.h).
+hipEvent_t g_stage_events[2 * NGRAM_N_STAGES];
 bool g_stage_events_on = false;
+int g_stage_mask = 0;
+int g_stage_index = -1;
+StageClock g_clock;
 
-void mark_stage(int i, hipStream_t s) {
-  if (g_stage_events_on) (void)hipEventRecord(g_stage_events[i], s);
+void close_stage() {
+  if (g_open_stage != nullptr && g_clock.launches > 0) g_stage_mask |= 1 << g_stage_index;
+  g_open_stage = nullptr;
+  g_stage_index = -1;
 }
+
+void stage(int i) {
+  close_stage();
+  if (!g_stage_events_on) return;
+  g_clock = StageClock{g_stage_events[2 * i], g_stage_events[2 * i + 1], 0};
+  g_stage_index = i;
+  g_open_stage = &g_clock;
+}
+
+// Closes the last stage when a timed forward call returns, on every path.
+struct TimedCall {
+  TimedCall() { g_stage_mask = 0; }
+  ~TimedCall() { close_stage(); }
+};
 
 int check_tables(const ngram_config* c, const void* const* tables, TablePtrs* out) {
   if (tables == nullptr) return NGRAM_EINVAL;
@@ -327,14 +350,16 @@ int ngram_set_timing_events(void* const* events, int n) {
     g_stage_events_on = false;
     return NGRAM_OK;
   }
-  if (n != NGRAM_N_STAGES + 1 || events == nullptr) return NGRAM_EINVAL;
-  for (int i = 0; i <= NGRAM_N_STAGES; ++i) {
+  if (n != 2 * NGRAM_N_STAGES || events == nullptr) return NGRAM_EINVAL;
+  for (int i = 0; i < 2 * NGRAM_N_STAGES; ++i) {
     if (events[i] == nullptr) return NGRAM_EINVAL;
     g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
   }
   g_stage_events_on = true;
   return NGRAM_OK;
 }
+
+int ngram_timing_stage_mask(void) { return g_stage_mask; }
 
 int ngram_compress_ids(const ngram_config* cfg, const int32_t* raw_ids, int64_t n,
                        const int32_t* lut, int32_t* comp_ids, int32_t* err_flag, void* stream) {
@@ -452,6 +477,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   const void* gamma_k, const void* gamma_u, const float* conv_state,
                   int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
                   size_t workspace_bytes, void* stream) {
+  const TimedCall timed;
   int st = validate(cfg);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
@@ -482,12 +508,11 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
     const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
     void* e = ws + L.e;
     float* split = reinterpret_cast<float*>(ws + L.split);
-    mark_stage(0, s);
+    stage(1);
     st = hip_status(launch_hash_gather(cfg->table_dtype, raw_ids, B, T, history, lut, ha,
                                        cfg->n_tables, cfg->row_dim, tp, e, err_flag, s));
     if (st) return st;
-    mark_stage(1, s);
-    mark_stage(2, s);
+    stage(2);
     ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
                             gamma_k, ws, L, n_tok);
     AsyncProjArgs aa = async_args(cfg, pa);
@@ -496,7 +521,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
     aa.split_out = split;
     st = hip_status(launch_projection_split(L.async, aa, s));
     if (st) return st;
-    mark_stage(3, s);
+    stage(3);
     ConvArgs ca = conv_args_base(cfg);
     ca.conv_w = conv_w;
     ca.gamma_u = gamma_u;
@@ -512,9 +537,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
     ca.T = T;
     ca.dil = cfg->conv_dilation;
     ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
-    st = hip_status(launch_decode_finalize(cfg->act_dtype, L.k_split, split, ca, s));
-    mark_stage(NGRAM_N_STAGES, s);
-    return st;
+    return hip_status(launch_decode_finalize(cfg->act_dtype, L.k_split, split, ca, s));
   }
   int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
   void* e = ws + L.e;
@@ -533,24 +556,22 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
     aa.T = T;
     aa.hash = ha;
     aa.tabs = tp;
-    mark_stage(0, s);
-    mark_stage(1, s);
-    mark_stage(2, s);
+    stage(2);
     st = hip_status(launch_projection_async(true, L.async, aa, s));
     if (st) return st;
   } else {
-    mark_stage(0, s);
+    stage(0);
     st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
     if (st) return st;
-    mark_stage(1, s);
+    stage(1);
     st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim,
                                   tp, e, s));
     if (st) return st;
-    mark_stage(2, s);
+    stage(2);
     st = hip_status(run_projection(cfg, L, pa, s));
     if (st) return st;
   }
-  mark_stage(3, s);
+  stage(3);
   ConvArgs ca = conv_args_base(cfg);
   ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
   ca.v_stride = L.v_stride;
@@ -568,9 +589,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   ca.T = T;
   ca.tile = conv_tile_for(T);
   ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
-  st = hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
-  mark_stage(NGRAM_N_STAGES, s);
-  return st;
+  return hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
 }
 
 }  // extern "C"

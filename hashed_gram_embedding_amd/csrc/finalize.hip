@@ -35,6 +35,12 @@ __device__ __forceinline__ float4 fma4(float4 a, float4 b, float4 c) {
   return make_float4(fmaf(a.x, b.x, c.x), fmaf(a.y, b.y, c.y), fmaf(a.z, b.z, c.z), fmaf(a.w, b.w, c.w));
 }
 __device__ __forceinline__ float silu(float c) { return c / (1.0f + expf(-c)); }
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
 
 // ngram_gate: gates and U = g V in the activation dtype.
 template <typename T>
@@ -311,29 +317,190 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
   }
 }
 
+// The same for d <= 1024 * ITEMS and NB branches, in registers: thread x owns
+// the 4-column groups c = 4 * (x + 256 * i), i < ITEMS.  Every load the token
+// needs before its row reductions is issued up front (addresses past d are
+// clamped to a valid column and their contribution dropped, so the code is
+// branch-free and the loads go out together), V and h stay in registers for
+// the outputs, and one block reduction separates the two memory round trips.
+template <typename T, int NB, int ITEMS, bool SPLITS>
+__global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
+                                                                  const float* __restrict__ split,
+                                                                  int32_t k_split, int32_t dil) {
+  constexpr int NQ = 3 * NB + 1;
+  __shared__ float s_red[4][NQ];
+  __shared__ float s_tot[NQ];
+  const int64_t tok = blockIdx.x;  // T == 1: token = sequence
+  const int d = a.d;
+  const int64_t ntot = (int64_t)(NB + 1) * d;
+  const int64_t sstride = (int64_t)a.B * ntot;
+  const float* __restrict__ P = split + tok * ntot;
+  const T* __restrict__ H = static_cast<const T*>(a.hidden);
+  const T* __restrict__ GQ = static_cast<const T*>(a.gamma_q);
+  const T* __restrict__ GK = static_cast<const T*>(a.gamma_k);
+  const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
+  const T* __restrict__ CW = static_cast<const T*>(a.conv_w);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  int col[ITEMS];
+  bool ok[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int c = 4 * ((int)threadIdx.x + 256 * i);
+    ok[i] = c < d;
+    col[i] = ok[i] ? c : d - 4;
+  }
+  auto splits = [&](int64_t off) {  // sum of the K splits, 4 columns
+    float4 x = *reinterpret_cast<const float4*>(P + off);
+    if (SPLITS)
+      for (int s = 1; s < k_split; ++s)
+        x = add4(x, *reinterpret_cast<const float4*>(P + s * sstride + off));
+    return x;
+  };
+  // absent gains read the conv taps (always there) and are replaced by 1 as
+  // 1 + (x - 1) * 0, so every load is unconditional and none sits behind a
+  // branch (a select would let the compiler move the load under one)
+  const bool has_gq = GQ != nullptr, has_gk = GK != nullptr, has_gu = GU != nullptr;
+  auto gain = [](float4 x, bool on) {
+    const float s = on ? 1.0f : 0.0f;
+    return make_float4(fmaf(x.x - 1.0f, s, 1.0f), fmaf(x.y - 1.0f, s, 1.0f),
+                       fmaf(x.z - 1.0f, s, 1.0f), fmaf(x.w - 1.0f, s, 1.0f));
+  };
+  const T* __restrict__ gq_p = has_gq ? GQ : CW;
+  const T* __restrict__ gk_p = has_gk ? GK : CW;
+  const T* __restrict__ gu_p = has_gu ? GU : CW;
+
+  float4 v[ITEMS], h[NB][ITEMS], k[NB][ITEMS], gq[ITEMS], gk[ITEMS], cw0[ITEMS], gu[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+#pragma unroll
+    for (int br = 0; br < NB; ++br) {
+      k[br][i] = splits((int64_t)br * d + col[i]);
+      h[br][i] = Elem<T>::load4(H, tok * a.h_tok_stride + br * a.h_branch_stride + col[i]);
+    }
+    v[i] = splits((int64_t)NB * d + col[i]);
+    gq[i] = Elem<T>::load4(gq_p, col[i]);
+    gk[i] = Elem<T>::load4(gk_p, col[i]);
+    cw0[i] = Elem<T>::load4(CW, col[i]);
+    gu[i] = Elem<T>::load4(gu_p, col[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above issued before the first wait
+  float acc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] = 0.0f;
+  float4 g[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    g[i] = mul4(gain(gq[i], has_gq), gain(gk[i], has_gk));
+    const float m = ok[i] ? 1.0f : 0.0f;
+    acc[3 * NB] += m * dot4(v[i], v[i]);
+#pragma unroll
+    for (int br = 0; br < NB; ++br) {
+      acc[3 * br] += m * dot4(mul4(g[i], h[br][i]), k[br][i]);
+      acc[3 * br + 1] += m * dot4(k[br][i], k[br][i]);
+      acc[3 * br + 2] += m * dot4(h[br][i], h[br][i]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off);
+    if (lane == 0) s_red[wave][q] = acc[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < NQ)
+    s_tot[threadIdx.x] = s_red[0][threadIdx.x] + s_red[1][threadIdx.x] + s_red[2][threadIdx.x] +
+                         s_red[3][threadIdx.x];
+  __syncthreads();
+
+  const float fd = (float)d;
+  const float mv = s_tot[3 * NB] / fd;
+  T* __restrict__ OUT = static_cast<T*>(a.out);
+  const int halo = 3 * dil;
+  float4 w0[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    w0[i] = mul4(cw0[i], gain(gu[i], has_gu));
+  }
+#pragma unroll
+  for (int br = 0; br < NB; ++br) {
+    const float z = s_tot[3 * br] /
+                    (sqrtf(s_tot[3 * br + 2] / fd + a.eps) * sqrtf(s_tot[3 * br + 1] / fd + a.eps) *
+                     sqrtf(fd));
+    const float al = 1.0f / (1.0f + expf(-z));
+    const float sc = al / sqrtf(al * al * mv + a.eps);
+    if (a.gates && threadIdx.x == 0) a.gates[tok * NB + br] = al;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      float4 C = mul4(w0[i], mul4(v[i], f4(sc)));
+      if (a.state) {
+        for (int t = 1; t < 4; ++t) {
+          const float4 st = *reinterpret_cast<const float4*>(
+              a.state + ((tok * halo + halo - t * dil) * NB + br) * d + col[i]);
+          C = fma4(Elem<T>::load4(CW, (int64_t)t * d + col[i]), st, C);
+        }
+      }
+      float4 D = make_float4(fmaf(al, v[i].x, silu(C.x)), fmaf(al, v[i].y, silu(C.y)),
+                             fmaf(al, v[i].z, silu(C.z)), fmaf(al, v[i].w, silu(C.w)));
+      if (a.add_residual) D = add4(D, h[br][i]);
+      if (ok[i]) Elem<T>::store4(OUT, (tok * NB + br) * d + col[i], D);
+    }
+  }
+}
+
 template <typename T, bool FUSED>
 hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
   const int tiles = (a.T + a.tile - 1) / a.tile;
   dim3 grid((unsigned)((int64_t)a.B * tiles), (unsigned)a.nb);
   switch (dil) {
-    case 1: conv_kernel<1, T, FUSED><<<grid, 256, 0, s>>>(a); break;
-    case 2: conv_kernel<2, T, FUSED><<<grid, 256, 0, s>>>(a); break;
-    case 3: conv_kernel<3, T, FUSED><<<grid, 256, 0, s>>>(a); break;
-    case 4: conv_kernel<4, T, FUSED><<<grid, 256, 0, s>>>(a); break;
+    case 1: return launch(conv_kernel<1, T, FUSED>, grid, 256, 0, s, a);
+    case 2: return launch(conv_kernel<2, T, FUSED>, grid, 256, 0, s, a);
+    case 3: return launch(conv_kernel<3, T, FUSED>, grid, 256, 0, s, a);
+    case 4: return launch(conv_kernel<4, T, FUSED>, grid, 256, 0, s, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+template <typename T, int NB, int ITEMS>
+hipError_t launch_finalize_reg_items(int32_t k_split, const float* split, const ConvArgs& a,
+                                     hipStream_t s) {
+  if (k_split == 1)
+    return launch(decode_finalize_reg_kernel<T, NB, ITEMS, false>, (unsigned)a.B, 256, 0, s, a,
+                  split, k_split, a.dil);
+  return launch(decode_finalize_reg_kernel<T, NB, ITEMS, true>, (unsigned)a.B, 256, 0, s, a, split,
+                k_split, a.dil);
+}
+
+template <typename T, int NB>
+hipError_t launch_finalize_reg_nb(int items, int32_t k_split, const float* split, const ConvArgs& a,
+                                  hipStream_t s) {
+  switch (items) {
+    case 1: return launch_finalize_reg_items<T, NB, 1>(k_split, split, a, s);
+    case 2: return launch_finalize_reg_items<T, NB, 2>(k_split, split, a, s);
+    case 3: return launch_finalize_reg_items<T, NB, 3>(k_split, split, a, s);
+    case 4: return launch_finalize_reg_items<T, NB, 4>(k_split, split, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_finalize_reg(int nb, int items, int32_t k_split, const float* split,
+                               const ConvArgs& a, hipStream_t s) {
+  switch (nb) {
+    case 1: return launch_finalize_reg_nb<T, 1>(items, k_split, split, a, s);
+    case 2: return launch_finalize_reg_nb<T, 2>(items, k_split, split, a, s);
+    case 3: return launch_finalize_reg_nb<T, 3>(items, k_split, split, a, s);
+    case 4: return launch_finalize_reg_nb<T, 4>(items, k_split, split, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gate_values(int dtype, const ConvArgs& a, int64_t M, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (dtype == NGRAM_BF16)
-    gate_values_kernel<bf16_bits><<<(unsigned)M, 256, 0, s>>>(a, M);
-  else
-    gate_values_kernel<float><<<(unsigned)M, 256, 0, s>>>(a, M);
-  return hipGetLastError();
+  if (dtype == NGRAM_BF16) return launch(gate_values_kernel<bf16_bits>, (unsigned)M, 256, 0, s, a, M);
+  return launch(gate_values_kernel<float>, (unsigned)M, 256, 0, s, a, M);
 }
 
 hipError_t launch_fused_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s) {
@@ -351,11 +518,15 @@ hipError_t launch_op_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t
 hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split, const ConvArgs& a,
                                   hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  const int items = (a.d + 1023) / 1024;
+  if (items <= 4) {
+    return dtype == NGRAM_BF16 ? launch_finalize_reg<bf16_bits>(a.nb, items, k_split, split, a, s)
+                               : launch_finalize_reg<float>(a.nb, items, k_split, split, a, s);
+  }
   if (dtype == NGRAM_BF16)
-    decode_finalize_kernel<bf16_bits><<<(unsigned)a.B, 256, 0, s>>>(a, split, k_split, a.dil);
-  else
-    decode_finalize_kernel<float><<<(unsigned)a.B, 256, 0, s>>>(a, split, k_split, a.dil);
-  return hipGetLastError();
+    return launch(decode_finalize_kernel<bf16_bits>, (unsigned)a.B, 256, 0, s, a, split, k_split,
+                  a.dil);
+  return launch(decode_finalize_kernel<float>, (unsigned)a.B, 256, 0, s, a, split, k_split, a.dil);
 }
 
 int conv_tile_for(int32_t T) { return T < kMaxTile ? T : kMaxTile; }

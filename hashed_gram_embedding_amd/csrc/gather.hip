@@ -117,9 +117,8 @@ hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t 
   int64_t blocks = (n_tok + 3) / 4;
   if (blocks > 262144) blocks = 262144;
   if (blocks < 1) blocks = 1;
-  hash_gather_kernel<<<(unsigned)blocks, 256, 0, s>>>(ids, B, T, hist, lut, h, row_chunks, t,
-                                                      static_cast<uint4*>(mem), err);
-  return hipGetLastError();
+  return launch(hash_gather_kernel, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h,
+                row_chunks, t, static_cast<uint4*>(mem), err);
 }
 
 hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
@@ -130,9 +129,8 @@ hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32
   int64_t blocks = (n_tok + 3) / 4;
   if (blocks > 262144) blocks = 262144;
   if (blocks < 1) blocks = 1;
-  gather_kernel<<<(unsigned)blocks, threads, 0, s>>>(row_idx, n_tok, n_tables, row_chunks, t,
-                                                     static_cast<uint4*>(mem));
-  return hipGetLastError();
+  return launch(gather_kernel, (unsigned)blocks, threads, 0, s, row_idx, n_tok, n_tables,
+                row_chunks, t, static_cast<uint4*>(mem));
 }
 
 }  // namespace ngram

@@ -59,8 +59,8 @@ int grid_for(int64_t n, int threads) {
 hipError_t launch_compress(const int32_t* raw, int64_t n, const int32_t* lut, int32_t vocab,
                            int32_t vocab_c, int32_t pad_id, int32_t* comp, int32_t* err,
                            hipStream_t s) {
-  compress_kernel<<<grid_for(n, 256), 256, 0, s>>>(raw, n, lut, vocab, vocab_c, pad_id, comp, err);
-  return hipGetLastError();
+  return launch(compress_kernel, grid_for(n, 256), 256, 0, s, raw, n, lut, vocab, vocab_c, pad_id,
+                comp, err);
 }
 
 hipError_t launch_hash(bool raw_input, const int32_t* ids, int32_t B, int32_t T,
@@ -68,10 +68,10 @@ hipError_t launch_hash(bool raw_input, const int32_t* ids, int32_t B, int32_t T,
                        int32_t* row_idx, int32_t* err, hipStream_t s) {
   const int64_t n = (int64_t)B * T;
   if (raw_input)
-    hash_kernel<true><<<grid_for(n, 256), 256, 0, s>>>(ids, B, T, hist, lut, a, row_idx, err);
-  else
-    hash_kernel<false><<<grid_for(n, 256), 256, 0, s>>>(ids, B, T, hist, lut, a, row_idx, err);
-  return hipGetLastError();
+    return launch(hash_kernel<true>, grid_for(n, 256), 256, 0, s, ids, B, T, hist, lut, a, row_idx,
+                  err);
+  return launch(hash_kernel<false>, grid_for(n, 256), 256, 0, s, ids, B, T, hist, lut, a, row_idx,
+                err);
 }
 
 }  // namespace ngram

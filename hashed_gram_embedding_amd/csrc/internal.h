@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/ngram.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -151,6 +152,39 @@ struct ConvArgs {
   const void* gamma_q;        // decode finalize: the gate's gains
   const void* gamma_k;
 };
+
+// ---------------------------------------------------------------------------
+// kernel launch
+// ---------------------------------------------------------------------------
+// Every kernel goes through launch(): a plain launch unless a timed stage is
+// open (benchmark instrumentation, ngram_set_timing_events), in which case
+// the stage's first kernel stamps its begin time into the stage's start event
+// and each of its kernels stamps its end time into the stop event, so the
+// event pair spans exactly the stage's kernels.
+struct StageClock {
+  hipEvent_t start, stop;
+  int launches;
+};
+extern StageClock* g_open_stage;
+
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
+template <typename... P>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem,
+                         hipStream_t s, typename same_type<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (StageClock* c = g_open_stage) {
+    e0 = c->launches == 0 ? c->start : nullptr;
+    e1 = c->stop;
+    ++c->launches;
+  }
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, s,
+                            e0, e1, 0);
+}
 
 // ---------------------------------------------------------------------------
 // launchers (return hipError_t of the launch)

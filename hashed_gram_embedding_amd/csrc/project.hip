@@ -280,8 +280,7 @@ hipError_t launch_bf16(const ProjArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const int tiles_n = (a.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)tiles_m * (a.nb + 1) * tiles_n;
-  proj_bf16_kernel<BM, BN><<<(unsigned)blocks, 256, 0, s>>>(a, tiles_m, tiles_n);
-  return hipGetLastError();
+  return launch(proj_bf16_kernel<BM, BN>, (unsigned)blocks, 256, 0, s, a, tiles_m, tiles_n);
 }
 
 }  // namespace
@@ -310,12 +309,10 @@ hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a,
   if (a.M == 0) return hipSuccess;
   if (dtype != NGRAM_BF16) {
     dim3 grid((a.d + FT - 1) / FT, (unsigned)((a.M + FT - 1) / FT), a.nb + 1);
-    proj_f32_kernel<<<grid, 256, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch(proj_f32_kernel, grid, 256, 0, s, a);
     if (e != hipSuccess) return e;
     const int64_t items = a.M * (a.nb + 1);
-    partials_f32_kernel<<<(unsigned)((items + 3) / 4), 256, 0, s>>>(a);
-    return hipGetLastError();
+    return launch(partials_f32_kernel, (unsigned)((items + 3) / 4), 256, 0, s, a);
   }
   if (plan.bm == 128) return launch_bf16<128, 128>(a, s);
   return launch_bf16<64, 64>(a, s);

@@ -297,12 +297,10 @@ hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
   a.tiles_n = (a.epi.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
   if (gather)
-    proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>
-        <<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
-  else
-    proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false>
-        <<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
-  return hipGetLastError();
+    return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>, (unsigned)blocks,
+                  64 * WGM * WGN, 0, s, a);
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false>, (unsigned)blocks,
+                64 * WGM * WGN, 0, s, a);
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
@@ -313,9 +311,8 @@ hipError_t launch_split_t(const AsyncProjArgs& a0, hipStream_t s) {
   a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
   a.tiles_n = (a.epi.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n * a.k_split;
-  proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>
-      <<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
-  return hipGetLastError();
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>, (unsigned)blocks,
+                64 * WGM * WGN, 0, s, a);
 }
 
 // One table of tile plans serves both the launch and the host's partial

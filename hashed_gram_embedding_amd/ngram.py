@@ -96,6 +96,7 @@ _SIGS = {
     "ngram_abi_version": (ctypes.c_int, []),
     "ngram_config_validate": (ctypes.c_int, [_cfgp]),
     "ngram_set_timing_events": (ctypes.c_int, [_p, ctypes.c_int]),
+    "ngram_timing_stage_mask": (ctypes.c_int, []),
     "ngram_compress_ids": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p]),
     "ngram_hash": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p]),
     "ngram_gather": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p]),
@@ -141,8 +142,9 @@ STAGE_NAMES = ("hash", "gather", "projection", "gate_conv")
 
 
 def ngram_set_timing_events(events) -> None:
-    """Benchmark hook: ``events`` is a list of N_STAGES + 1 torch.cuda.Event
-    (created with enable_timing=True), or None to turn the hook off."""
+    """Benchmark hook: ``events`` is a list of 2 * N_STAGES torch.cuda.Event
+    (created with enable_timing=True) -- the (start, stop) pair of each stage --
+    or None to turn the hook off."""
     if events is None:
         _check(lib().ngram_set_timing_events(None, 0), "ngram_set_timing_events")
         return
@@ -151,6 +153,11 @@ def ngram_set_timing_events(events) -> None:
             e.record()
     arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _check(lib().ngram_set_timing_events(arr, len(events)), "ngram_set_timing_events")
+
+
+def ngram_timing_stage_mask() -> int:
+    """Bit i set: stage i launched a kernel in the last timed ngram_forward."""
+    return int(lib().ngram_timing_stage_mask())
 
 
 # ---------------------------------------------------------------------------

@@ -236,17 +236,22 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   size_t workspace_bytes, void* stream);
 
 /*
- * Benchmark instrumentation (not part of the layer).  When n == NGRAM_N_STAGES,
- * every following ngram_forward records events[i] (NGRAM_N_STAGES + 1 hipEvent_t handles) on its
- * stream before stage i -- 0 hash, 1 gather, 2 projection, 3 gate+conv -- and
- * events[NGRAM_N_STAGES] after the last stage, so hipEventElapsedTime
- * between consecutive events gives each stage's device time.  n == 0 turns it
- * off.  The setting is process-wide and not synchronised: set it only while no
- * other thread calls ngram_forward.  Returns NGRAM_EINVAL for other n or NULL
- * events.
+ * Benchmark instrumentation (not part of the layer).  With n == 2 * NGRAM_N_STAGES, every
+ * following ngram_forward times its stages on the device -- 0 hash, 1 gather, 2 projection,
+ * 3 gate + conv: the first kernel of stage i stamps its begin time into events[2i] and every
+ * kernel of the stage stamps its end time into events[2i + 1] (hipExtLaunchKernel), so
+ * hipEventElapsedTime(events[2i], events[2i + 1]) is the stage's kernel time, with no event
+ * packet between the kernels.  A kernel that covers several stages counts in the last of them
+ * (the decode path hashes and gathers in one kernel; the fused path hashes, gathers and
+ * projects in one); the stages it absorbs launch nothing and leave their events untouched.
+ * ngram_timing_stage_mask() returns the bit mask (bit i = stage i) of the stages that launched
+ * a kernel in the last ngram_forward call.  n == 0 turns timing off.  The setting is
+ * process-wide and not synchronised: set it only while no other thread calls ngram_forward.
+ * Returns NGRAM_EINVAL for other n or NULL events.
  */
 #define NGRAM_N_STAGES 4
 int ngram_set_timing_events(void* const* events, int n);
+int ngram_timing_stage_mask(void);
 
 #ifdef __cplusplus
 }

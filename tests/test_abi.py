@@ -59,7 +59,7 @@ def test_config_layout_matches_c(H):
 
 
 def test_status_strings_and_version(H):
-    assert H.ngram.abi_version() == 1
+    assert H.ngram.abi_version() == 2
     for code in range(-7, 1):
         assert H.ngram.status_str(code).startswith("NGRAM_")
 

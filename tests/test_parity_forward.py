@@ -171,7 +171,7 @@ def test_forward_ragged_and_short(orc, B, T):
 
 
 @pytest.mark.parametrize("variant", ["orders234", "orders12_bf16", "order2_only",
-                                     "rowdim96_bf16_dmem"])
+                                     "rowdim96_bf16_dmem", "tables16x160_bf16_dmem"])
 def test_forward_other_order_sets(orc, variant):
     """Dilation follows the largest order (4, 2, 2)."""
     if variant == "orders234":
@@ -181,9 +181,12 @@ def test_forward_other_order_sets(orc, variant):
                                           hidden=256)
     elif variant == "order2_only":
         w = W.get("tiny").replace(orders=(2,), heads=3, explicit_rows=(), batch=2, seq_len=50)
-    else:  # 96-wide rows: the projection cannot gather K steps itself
+    elif variant == "rowdim96_bf16_dmem":  # the projection cannot gather K steps itself
         w = W.get("engram_small").replace(heads=2, row_dim=96, batch=2, seq_len=200,
                                           hidden=128)
+    else:  # 16 tables x 160 values: 8 heads per order, E of 2560 (320-byte rows)
+        w = W.get("engram_small").replace(heads=8, row_dim=160, row_start=10007, batch=2,
+                                          seq_len=200, hidden=256)
     print(f"[forward] {variant}", flush=True)
     ids, hist = W.make_ids(w)
     inp = _device_inputs(w, ids, hist, layout="d_mem" if "dmem" in variant else "mem_d")
