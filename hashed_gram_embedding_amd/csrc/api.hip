@@ -3,6 +3,7 @@
 // of the layer runs in the kernels of ids.hip, gather.hip, project.hip and
 // finalize.hip; this file launches them on the caller's stream.
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -109,28 +110,26 @@ bool async_path(const ngram_config* c) {
 // 64-wide K step lies within one table row.
 bool fused_gather(const ngram_config* c) { return async_path(c) && c->row_dim % 64 == 0; }
 
-// Decode (one new token per sequence): E is materialised once and the
-// projection is split along K into raw fp32 partial tiles, so many more
-// workgroups stream the weights; the decode finalize sums the splits.
-bool decode_path(const ngram_config* c, int32_t T) { return async_path(c) && T == 1; }
+// Decode (one new token per sequence, up to kDecodeMaxRows sequences): E is
+// materialised once by the hash + gather kernel, the weight-stationary
+// projection writes one fp32 partial per K slice, and the decode finalize
+// sums them.  Larger batches take the fused route, where the weights are
+// reused across many more rows.
+constexpr int64_t kDecodeMaxRows = 2048;
 
-// Split factor and tile plan of the decode projection (NGRAM_DECODE_SPLIT
-// and NGRAM_DECODE_TILE override them: tuning knobs).
-int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  if (!e || !*e) return dflt;
-  char* end = nullptr;
-  const long v = strtol(e, &end, 10);
-  return (*end == 0 && v >= 0 && v < 1000) ? (int)v : dflt;
+// Tile plan of the decode projection; NGRAM_DECODE_PLAN="ni,split,ring"
+// overrides it (a tuning knob; the launch rejects shapes it cannot run).
+WstatPlan decode_plan(const ngram_config* c, int64_t n_tok) {
+  WstatPlan p = wstat_plan(n_tok, (c->n_branches + 1) * c->hidden_dim, c->mem_dim);
+  const char* e = getenv("NGRAM_DECODE_PLAN");
+  int ni = 0, split = 0, ring = 0;
+  if (e && sscanf(e, "%d,%d,%d", &ni, &split, &ring) == 3 && ni > 0 && split > 0 && ring > 0)
+    p = WstatPlan{ni, split, ring};
+  return p;
 }
-int decode_tile(void) { return env_int("NGRAM_DECODE_TILE", 2); }
-int decode_split(const ngram_config* c, int tile) {
-  const int bk = tile == 0 ? 32 : 64;
-  const int nk = c->mem_dim / bk;
-  int s = env_int("NGRAM_DECODE_SPLIT", 1);
-  if (s < 1) s = 1;
-  while (s > 1 && nk % s != 0) --s;  // must divide the number of K steps
-  return s;
+
+bool decode_path(const ngram_config* c, int32_t T, int64_t n_tok) {
+  return async_path(c) && T == 1 && n_tok <= kDecodeMaxRows && decode_plan(c, n_tok).ni > 0;
 }
 
 HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
@@ -159,7 +158,8 @@ struct Layout {
   size_t row_idx = 0, e = 0, v = 0, parts = 0, split = 0, total = 0;
   ProjPlan plan;       // plan.np is the number of partials per row on every path
   int async = -1;      // async projection tile plan, -1 when not used
-  int k_split = 0;     // decode path: K splits (0: not the decode path)
+  int k_split = 0;     // decode path: K slices (0: not the decode path)
+  WstatPlan wplan{0, 0, 0};  // decode path: projection plan
   int64_t v_stride = 0;  // fp32 elements between V rows
   int64_t v_offset = 0;  // fp32 elements from the V buffer to row 0's values
 };
@@ -168,13 +168,13 @@ struct Layout {
 // projection gathers them itself).  T: tokens per sequence (decode when 1).
 Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward, int32_t T = 0) {
   Layout L;
-  if (forward && decode_path(c, T)) {
-    L.async = decode_tile();
-    L.k_split = decode_split(c, L.async);
+  if (forward && decode_path(c, T, n_tok)) {
+    L.wplan = decode_plan(c, n_tok);
+    L.k_split = L.wplan.split;
     L.plan.np = 1;
     size_t off = 0;
-    L.e = off;
-    off = align_up(off + (size_t)n_tok * c->mem_dim * esize_of(c->table_dtype));
+    L.e = off;  // decode E tiles: whole 16-token blocks
+    off = align_up(off + (size_t)((n_tok + 15) / 16 * 16) * c->mem_dim * esize_of(c->table_dtype));
     L.split = off;
     off = align_up(off + (size_t)L.k_split * n_tok * (c->n_branches + 1) * c->hidden_dim *
                              sizeof(float));
@@ -504,7 +504,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (L.k_split > 0) {
-    // decode: hash + gather -> E, split-K projection, decode finalize
+    // decode: hash + gather -> E, weight-stationary projection, decode finalize
     const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
     void* e = ws + L.e;
     float* split = reinterpret_cast<float*>(ws + L.split);
@@ -513,13 +513,16 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                                        cfg->n_tables, cfg->row_dim, tp, e, err_flag, s));
     if (st) return st;
     stage(2);
-    ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
-                            gamma_k, ws, L, n_tok);
-    AsyncProjArgs aa = async_args(cfg, pa);
-    aa.epi.np = 1;
-    aa.k_split = L.k_split;
-    aa.split_out = split;
-    st = hip_status(launch_projection_split(L.async, aa, s));
+    WstatArgs wa{};
+    wa.e = static_cast<const bf16_bits*>(e);
+    wa.wk = static_cast<const bf16_bits*>(w_k);
+    wa.wv = static_cast<const bf16_bits*>(w_v);
+    wa.M = n_tok;
+    wa.K = cfg->mem_dim;
+    wa.nb = cfg->n_branches;
+    wa.d = cfg->hidden_dim;
+    wa.split_out = split;
+    st = hip_status(launch_projection_wstat(L.wplan, wa, s));
     if (st) return st;
     stage(3);
     ConvArgs ca = conv_args_base(cfg);

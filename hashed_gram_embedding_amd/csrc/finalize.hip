@@ -323,7 +323,9 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
 // clamped to a valid column and their contribution dropped, so the code is
 // branch-free and the loads go out together), V and h stay in registers for
 // the outputs, and one block reduction separates the two memory round trips.
-template <typename T, int NB, int ITEMS, bool SPLITS>
+// KS > 0: exactly KS K slices, summed with every load issued up front;
+// KS == 0: k_split slices in a loop.
+template <typename T, int NB, int ITEMS, int KS>
 __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
                                                                   const float* __restrict__ split,
                                                                   int32_t k_split, int32_t dil) {
@@ -350,11 +352,16 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
     ok[i] = c < d;
     col[i] = ok[i] ? c : d - 4;
   }
-  auto splits = [&](int64_t off) {  // sum of the K splits, 4 columns
+  auto splits = [&](int64_t off) {  // sum of the K slices, 4 columns, in slice order
     float4 x = *reinterpret_cast<const float4*>(P + off);
-    if (SPLITS)
+    if (KS > 0) {
+#pragma unroll
+      for (int s = 1; s < KS; ++s)
+        x = add4(x, *reinterpret_cast<const float4*>(P + s * sstride + off));
+    } else {
       for (int s = 1; s < k_split; ++s)
         x = add4(x, *reinterpret_cast<const float4*>(P + s * sstride + off));
+    }
     return x;
   };
   // absent gains read the conv taps (always there) and are replaced by 1 as
@@ -464,11 +471,13 @@ hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
 template <typename T, int NB, int ITEMS>
 hipError_t launch_finalize_reg_items(int32_t k_split, const float* split, const ConvArgs& a,
                                      hipStream_t s) {
-  if (k_split == 1)
-    return launch(decode_finalize_reg_kernel<T, NB, ITEMS, false>, (unsigned)a.B, 256, 0, s, a,
-                  split, k_split, a.dil);
-  return launch(decode_finalize_reg_kernel<T, NB, ITEMS, true>, (unsigned)a.B, 256, 0, s, a, split,
-                k_split, a.dil);
+  const unsigned g = (unsigned)a.B;
+  switch (k_split) {
+    case 1: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 1>, g, 256, 0, s, a, split, k_split, a.dil);
+    case 2: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 2>, g, 256, 0, s, a, split, k_split, a.dil);
+    case 4: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 4>, g, 256, 0, s, a, split, k_split, a.dil);
+    default: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 0>, g, 256, 0, s, a, split, k_split, a.dil);
+  }
 }
 
 template <typename T, int NB>

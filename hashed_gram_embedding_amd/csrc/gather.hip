@@ -56,10 +56,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   }
 }
 
-// Hash + gather in one pass, one wavefront per token: every lane reads the
-// token's context ids (the same few words, served by the cache), lane j
-// hashes table j, and each 16-byte chunk's lane fetches its table's row id
-// from lane j with a cross-lane read before the loads above.
+// Hash + gather in one pass for the decode step, one wavefront per token:
+// every lane reads the token's context ids (the same few words, served by the
+// cache), lane j hashes table j, and each 16-byte chunk's lane fetches its
+// table's row id from lane j with a cross-lane read before the loads above.
+// E is written in the decode projection's operand order (internal.h,
+// "decode E tiles"), so that kernel reads each 16-row x 32-k operand of
+// v_mfma_f32_16x16x32_bf16 as one contiguous kilobyte.
 __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restrict__ ids,
                                                           int32_t B, int32_t T,
                                                           const int32_t* __restrict__ hist,
@@ -78,6 +81,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
   const int32_t chunks = h.n_tables * row_chunks;
   const int jl = lane < h.n_tables ? lane : 0;
   const int order_l = h.orders[jl / h.heads];
+  const int32_t n_kk = chunks >> 2;  // 32-wide K steps per token
   for (int64_t tok = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6); tok < n_tok;
        tok += wstride) {
     const int32_t b = (int32_t)(tok / T);
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
     uint64_t c[NGRAM_MAX_ORDER];
     context_ids<true>(ids, tok, b, t, hist, lut, h, err, c);
     const int32_t my_row = (int32_t)table_row(h, jl, order_l, c);
-    uint4* dst = mem + tok * chunks;
+    uint4* dst = mem + (tok >> 4) * n_kk * 64 + (tok & 15);
     for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
       uint4 v[kGatherUnroll];
 #pragma unroll
@@ -97,8 +101,8 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
       }
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
-        const int q = base + u * 64 + lane;
-        if (q < chunks) dst[q] = v[u];
+        const int q = base + u * 64 + lane;  // chunk q: K step q/4, quarter q%4
+        if (q < chunks) dst[(q >> 2) * 64 + (q & 3) * 16] = v[u];
       }
     }
   }
@@ -110,9 +114,9 @@ hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t 
                               const int32_t* hist, const int32_t* lut, const HashArgs& h,
                               int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,
                               int32_t* err, hipStream_t s) {
-  const int esize = dtype == NGRAM_BF16 ? 2 : 4;
-  const int32_t row_chunks = row_dim * esize / 16;
-  (void)n_tables;
+  // the tiled E layout is defined for bf16 rows of whole 32-wide K steps
+  if (dtype != NGRAM_BF16 || (n_tables * row_dim) % 32 != 0) return hipErrorInvalidValue;
+  const int32_t row_chunks = row_dim * 2 / 16;
   const int64_t n_tok = (int64_t)B * T;
   int64_t blocks = (n_tok + 3) / 4;
   if (blocks > 262144) blocks = 262144;

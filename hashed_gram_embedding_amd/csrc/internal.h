@@ -122,11 +122,6 @@ struct AsyncProjArgs {
   const bf16_bits* wv;       // [d, K]
   EpiArgs epi;
   int32_t K, tiles_m, tiles_n, group_m;
-  // split-K (k_split > 1): workgroup ks covers K steps [ks*K/k_split, ...)
-  // and stores its raw fp32 tile into split_out[ks][M][(nb+1)*d]; no
-  // epilogue math (the decode finalize sums the splits)
-  int32_t k_split;
-  float* split_out;
 };
 
 // Gate + gated value + conv block over a [B, T] token grid.
@@ -210,7 +205,34 @@ int async_plan(int64_t M);
 int async_wave_cols(int plan);
 hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s);
 // split-K raw-tile variant for small M (decode); E given densely
-hipError_t launch_projection_split(int plan, const AsyncProjArgs& a, hipStream_t s);
+// Decode E tiles: the decode step's E [M, K] bf16 is stored as 1 KB tiles of
+// 16 tokens x 32 K values, tile (mb, kk) at element ((mb * K/32) + kk) * 512,
+// and inside a tile the 8 values k = 32*kk + 8*q .. +8 of token 16*mb + r at
+// element (16*q + r) * 8: lane 16*q + r's A operand of
+// v_mfma_f32_16x16x32_bf16.  The buffer holds whole 16-token blocks.
+//
+// Weight-stationary decode projection (project_decode.hip): workgroup
+// (n-tile of 16*ni columns, K slice) holds its weight block in LDS and writes
+// the fp32 partial of its slice to split_out[slice][M][(nb+1)*d].  The grid is
+// sized for kWstatCus compute units (MI355X).
+constexpr int kWstatLdsBytes = 128 * 1024;
+constexpr int kWstatCus = 256;
+struct WstatPlan {
+  int ni;     // 16-column MFMA blocks per workgroup (0: no plan fits)
+  int split;  // K slices
+  int ring;   // K steps of E loads in flight per wave
+};
+struct WstatArgs {
+  const bf16_bits* e;   // [M, K]
+  const bf16_bits* wk;  // [nb*d, K]
+  const bf16_bits* wv;  // [d, K]
+  int64_t M;
+  int32_t K, nb, d;
+  int32_t kt, tiles_n;  // set by the launcher
+  float* split_out;
+};
+WstatPlan wstat_plan(int64_t M, int32_t N, int32_t K);
+hipError_t launch_projection_wstat(const WstatPlan& plan, const WstatArgs& a, hipStream_t s);
 hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t T,
                               const int32_t* hist, const int32_t* lut, const HashArgs& h,
                               int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,

@@ -85,7 +85,7 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int ti
   n = sn - seg * tiles_n;
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool GATHER, bool SPLIT = false>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool GATHER>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProjArgs a) {
   constexpr int NW = WGM * WGN;          // waves per workgroup
   constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
@@ -115,15 +115,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   const int wm = wave / WGN, wn = wave % WGN;
   const EpiArgs& ep = a.epi;
   const int n_seg = ep.nb + 1;
-  int m_tile, seg, n_tile, ks = 0;
-  if (SPLIT) {
-    // K split outermost: the splits of one tile share neither A nor B
-    const int tiles = a.tiles_m * n_seg * a.tiles_n;
-    ks = blockIdx.x / tiles;
-    map_tile(blockIdx.x - ks * tiles, a.tiles_m, n_seg, a.tiles_n, a.group_m, m_tile, seg, n_tile);
-  } else {
-    map_tile(blockIdx.x, a.tiles_m, n_seg, a.tiles_n, a.group_m, m_tile, seg, n_tile);
-  }
+  int m_tile, seg, n_tile;
+  map_tile(blockIdx.x, a.tiles_m, n_seg, a.tiles_n, a.group_m, m_tile, seg, n_tile);
   const int64_t M = ep.M;
   const int64_t m0 = (int64_t)m_tile * BM;
   const int n0 = n_tile * BN;
@@ -147,7 +140,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     __syncthreads();
   }
 
-  int kt0 = 0;  // first K step of this workgroup (split-K)
 
   // Copy lanes: lane -> (row lrow of the copy's RPI-row block, 16-byte chunk
   // pch of the LDS row).  A block starts at a multiple of RPI rows, so the
@@ -168,7 +160,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   auto issue = [&](int kt, int sl) {
     bf16_bits* As = slot(sl);
     bf16_bits* Bs = As + A_ELEMS;
-    const int k0 = (kt0 + kt) * BK;
+    const int k0 = kt * BK;
     int j = 0, cofs = 0;
     const bf16_bits* tab = nullptr;
     if (GATHER) {
@@ -228,12 +220,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     }
   };
 
-  int nk = K / BK;
-  if (SPLIT) {
-    const int per = nk / a.k_split;  // the host checks that k_split divides nk
-    kt0 = ks * per;
-    nk = per;
-  }
+  const int nk = K / BK;
   // The last slot first receives a throw-away copy of step 0 (overwritten
   // before it is read), so that on entry to the loop every slot has one copy
   // outstanding in the same order as at the loop's back edge; the compiler's
@@ -263,26 +250,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
 
   const int wcol0 = n0 + wn * WTN;
   if (wcol0 >= d) return;
-  if (SPLIT) {
-    // raw fp32 tile: split_out[ks][row][seg*d + col]; a half-wave stores 32
-    // consecutive columns (128 bytes) of one row per register
-    const int64_t ntot = (int64_t)n_seg * d;
-    float* __restrict__ P = a.split_out + (int64_t)ks * M * ntot + (int64_t)seg * d;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int col = wcol0 + ni * 32 + (lane & 31);
-        if (col < d) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * WTM + mi * 32 + acc_row(r, lane);
-            if (row < M) P[row * ntot + col] = acc[mi][ni][r];
-          }
-        }
-      }
-    return;
-  }
   gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
 }
 
@@ -300,18 +267,6 @@ hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
     return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>, (unsigned)blocks,
                   64 * WGM * WGN, 0, s, a);
   return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false>, (unsigned)blocks,
-                64 * WGM * WGN, 0, s, a);
-}
-
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
-hipError_t launch_split_t(const AsyncProjArgs& a0, hipStream_t s) {
-  AsyncProjArgs a = a0;
-  if (a.k_split < 1 || (a.K / BK) % a.k_split != 0 || a.split_out == nullptr)
-    return hipErrorInvalidValue;
-  a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
-  a.tiles_n = (a.epi.d + BN - 1) / BN;
-  const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n * a.k_split;
-  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>, (unsigned)blocks,
                 64 * WGM * WGN, 0, s, a);
 }
 
@@ -354,15 +309,6 @@ int async_wave_cols(int plan) {
   NGRAM_ASYNC_PLANS(NGRAM_WAVE_COLS)
 #undef NGRAM_WAVE_COLS
   return -1;
-}
-
-hipError_t launch_projection_split(int plan, const AsyncProjArgs& a, hipStream_t s) {
-  if (a.epi.M == 0) return hipSuccess;
-#define NGRAM_LAUNCH_SPLIT(id, bm, bn, bk, st, wgm, wgn) \
-  if (plan == id) return launch_split_t<bm, bn, bk, st, wgm, wgn>(a, s);
-  NGRAM_ASYNC_PLANS(NGRAM_LAUNCH_SPLIT)
-#undef NGRAM_LAUNCH_SPLIT
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s) {

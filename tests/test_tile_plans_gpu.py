@@ -78,28 +78,36 @@ def test_forward_each_plan(orc, plan_env):
 
 @pytest.fixture
 def decode_env(request):
-    tile, split = request.param
-    old = {k: os.environ.get(k) for k in ("NGRAM_DECODE_TILE", "NGRAM_DECODE_SPLIT")}
-    os.environ["NGRAM_DECODE_TILE"] = tile
-    os.environ["NGRAM_DECODE_SPLIT"] = split
+    old = os.environ.get("NGRAM_DECODE_PLAN")
+    if request.param == "default":
+        os.environ.pop("NGRAM_DECODE_PLAN", None)
+    else:
+        os.environ["NGRAM_DECODE_PLAN"] = request.param
     yield request.param
-    for k, v in old.items():
-        if v is None:
-            os.environ.pop(k, None)
-        else:
-            os.environ[k] = v
+    if old is None:
+        os.environ.pop("NGRAM_DECODE_PLAN", None)
+    else:
+        os.environ["NGRAM_DECODE_PLAN"] = old
 
 
-@pytest.mark.parametrize("decode_env", [("2", "1"), ("2", "4"), ("2", "8"), ("5", "2"),
-                                        ("0", "16"), ("1", "5")], indirect=True)
-@pytest.mark.parametrize("name", ["qwen_decode", "qwen_multibranch_zipf13"])
-def test_decode_path_splits(orc, decode_env, name):
-    """One new token per sequence (T = 1): hash+gather, split-K projection and
-    the decode finalize, with a populated conv state, the residual flag and
-    random RMSNorm gains."""
+# "ni,split,ring": 16*ni weight columns per workgroup, K slices (each a
+# multiple of 128 wide), K steps of E loads in flight (4, or 10 up to 80
+# columns).  With K = 2560: 5,4,10, 4,4,10 and 3,5,4 take the fully unrolled K
+# loop (20 and 16 steps per slice), the others the looped one; 3 (48 columns)
+# leaves a ragged last column tile.
+DECODE_PLANS = ["default", "5,4,10", "5,4,4", "4,4,10", "2,2,4", "8,10,4", "3,5,4", "10,10,4"]
+
+
+@pytest.mark.parametrize("decode_env", DECODE_PLANS, indirect=True)
+@pytest.mark.parametrize("name,batch", [("qwen_decode", 64), ("qwen_decode", 300),
+                                        ("qwen_multibranch_zipf13", 64)])
+def test_decode_path_plans(orc, decode_env, name, batch):
+    """One new token per sequence (T = 1): hash+gather, the weight-stationary
+    projection and the decode finalize, with a populated conv state, the
+    residual flag and random RMSNorm gains (300 rows: two ragged passes)."""
     H = G.H()
-    w = W.get(name).replace(batch=64, seq_len=1, history_len=2)
-    print(f"[decode tile/split {decode_env}] {name}", flush=True)
+    w = W.get(name).replace(batch=batch, seq_len=1, history_len=2)
+    print(f"[decode plan {decode_env}] {name} batch {batch}", flush=True)
     cfg = G.config(w, "d_mem")
     ids, hist = W.make_ids(w)
     wk, wv = G.weights(w, "d_mem")
@@ -126,4 +134,30 @@ def test_decode_path_splits(orc, decode_env, name):
         w.batch, -1, d)[:, :1 if nb == 1 else nb]
     got = G.to_f64(out).reshape(want.shape)
     assert G.rel_err(got, want) < G.TOL
+    assert G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"]) < G.TOL
+
+
+def test_single_token_large_batch_takes_fused_route(orc):
+    """T = 1 with more sequences than the decode route serves: the fused
+    route (per-token tiles with history) gives the same result."""
+    w = W.get("engram_small").replace(batch=2100, seq_len=1, history_len=2, heads=2,
+                                      hidden=128)
+    print("[single token, 2100 sequences]", flush=True)
+    H = G.H()
+    cfg = G.config(w, "d_mem")
+    ids, hist = W.make_ids(w)
+    wk, wv = G.weights(w, "d_mem")
+    hidden = SD.make_hidden(w, ids.size)
+    out = torch.empty((w.batch, 1, 1, w.hidden), dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty((w.batch, 1, 1), dtype=torch.float32, device="cuda")
+    H.ngram_forward(cfg, torch.from_numpy(ids).cuda(), torch.from_numpy(W.make_lut(w)).cuda(),
+                    G.tables(w), hidden, 0, wk, wv, G.conv_w(w), out,
+                    history=torch.from_numpy(hist).cuda(), gates=gates)
+    torch.cuda.synchronize()
+    wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
+    ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
+                      w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
+                      W.hidden_values(w, np.arange(ids.size)), wk_h, wv_h,
+                      W.conv_weight_values(w), "bf16", eps=w.rms_eps)
+    assert G.rel_err(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"]) < G.TOL
     assert G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"]) < G.TOL
