@@ -142,7 +142,7 @@ _CS = "hashed_gram_embedding_amd/csrc/"
 # sequence) and the fused route of every other workload
 STAGE_SOURCES = {
     ("gather", "decode"): [_CS + "gather.hip", _CS + "hashing.h"],
-    ("projection", "decode"): [_CS + "project_async.hip"],
+    ("projection", "decode"): [_CS + "project_decode.hip"],
     ("gate_conv", "decode"): [_CS + "finalize.hip"],
     ("projection", "fused"): [_CS + "project_async.hip", _CS + "epilogue.h",
                               _CS + "hashing.h"],

@@ -108,7 +108,14 @@ bool async_path(const ngram_config* c) {
 }
 // ... and the forward hashes and gathers inside the projection when every
 // 64-wide K step lies within one table row.
-bool fused_gather(const ngram_config* c) { return async_path(c) && c->row_dim % 64 == 0; }
+// The projection gathers its own A operand when every 64-wide K step lies
+// inside one table row.  NGRAM_FUSED_GATHER=0 materialises E first instead (a
+// tuning knob: both routes compute the same result).
+bool fused_gather(const ngram_config* c) {
+  const char* e = getenv("NGRAM_FUSED_GATHER");
+  if (e && e[0] == '0' && e[1] == 0) return false;
+  return async_path(c) && c->row_dim % 64 == 0;
+}
 
 // Decode (one new token per sequence, up to kDecodeMaxRows sequences): E is
 // materialised once by the hash + gather kernel, the weight-stationary

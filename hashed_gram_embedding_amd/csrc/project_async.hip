@@ -27,8 +27,9 @@
 // LDS layout per stage: A [BM][BK], B [BN][BK] bf16, rows of BK*2 bytes whose
 // 16-byte chunks are XOR-swizzled by row (chunk ^ f(row)); a copy writes the
 // lanes' chunks contiguously, so the swizzle is applied to the source address,
-// and the MFMA operand reads (8 lanes x 16 bytes per LDS cycle) hit distinct
-// banks.  Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD
+// and the MFMA operand reads hit distinct banks: a 16-byte-per-lane LDS read
+// is served 16 lanes (256 bytes, all 64 banks) at a time, and those 16 lanes
+// read rows r..r+15 of one logical chunk.  Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD
 // gets a contiguous range of tiles, walked in groups of group_m M-tiles with
 // the M index fastest -- concurrently running workgroups of one XCD share A
 // and B slabs in its L2.
@@ -60,13 +61,24 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, bf16_bits* wave_d
 
 template <int BK>
 __device__ __forceinline__ int swz(int row);
+// 64-wide K: 128-byte rows, two per 256-byte bank window, so the 16 rows of
+// one read pass must spread over 8 chunk slots per row parity: the low three
+// row bits, flipped by row bit 3, do that.
 template <>
 __device__ __forceinline__ int swz<64>(int row) {
-  return row & 7;
+  return (row & 7) ^ ((row >> 3) & 1);
 }
+// 32-wide K: four 64-byte rows per bank window.
 template <>
 __device__ __forceinline__ int swz<32>(int row) {
   return (row >> 2) & 3;
+}
+
+// Part of swz(rblk + lrow) that depends on the copy's first row rblk (a
+// multiple of the 64 / (BK / 8) rows one wave-wide copy covers).
+template <int BK>
+__device__ __forceinline__ int swz_block(int rblk) {
+  return BK == 64 ? (rblk >> 3) & 1 : 0;
 }
 
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int tiles_n, int gm,
@@ -143,13 +155,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
 
   // Copy lanes: lane -> (row lrow of the copy's RPI-row block, 16-byte chunk
   // pch of the LDS row).  A block starts at a multiple of RPI rows, so the
-  // row's swizzle is that of lrow and the chunk each lane fetches is fixed.
+  // row's swizzle is that of lrow, XOR the block's part (swz_block).
   const int lrow = lane / CH, pch = lane - (lane / CH) * CH;
   const int lch8 = (pch ^ swz<BK>(lrow)) * 8;  // element offset of the fetched chunk
   // Operand-read lanes: LDS byte offset of this lane's A and B rows for
   // mi = ni = 0; the other blocks are +32 rows (immediate offsets), and the
   // swizzle of all of them equals that of the lane's row (rows differ by
-  // multiples of 16).
+  // multiples of 16, which leaves row bits 0..3 alone).
   const int frow = lane & 31;
   const uint32_t a_row_b = (uint32_t)((wm * WTM + frow) * BK * 2);
   const uint32_t b_row_b = (uint32_t)((wn * WTN + frow) * BK * 2);
@@ -165,28 +177,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     const bf16_bits* tab = nullptr;
     if (GATHER) {
       j = k0 / a.row_dim;
-      cofs = k0 - j * a.row_dim + lch8;
+      cofs = k0 - j * a.row_dim;
       tab = static_cast<const bf16_bits*>(a.tabs.p[j]);
     }
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int rblk = (wave * A_INS + i) * RPI;
+      const int ch8 = lch8 ^ (swz_block<BK>(rblk) << 3);
       const bf16_bits* src;
       if (GATHER) {
-        src = tab + (int64_t)s_rid[(rblk + lrow) * NGRAM_MAX_TABLES + j] * a.row_dim + cofs;
+        src = tab + (int64_t)s_rid[(rblk + lrow) * NGRAM_MAX_TABLES + j] * a.row_dim + cofs + ch8;
       } else {
         int64_t grow = m0 + rblk + lrow;
         if (grow > M - 1) grow = M - 1;
-        src = a.e + grow * K + k0 + lch8;
+        src = a.e + grow * K + k0 + ch8;
       }
       copy16_to_lds(src, As + rblk * BK);
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const int rblk = (wave * B_INS + i) * RPI;
+      const int ch8 = lch8 ^ (swz_block<BK>(rblk) << 3);
       int n = n0 + rblk + lrow;
       if (n > d - 1) n = d - 1;  // columns past d are computed, never stored
-      copy16_to_lds(W + (uint32_t)(n * K + k0 + lch8), Bs + rblk * BK);
+      copy16_to_lds(W + (uint32_t)(n * K + k0 + ch8), Bs + rblk * BK);
     }
   };
 

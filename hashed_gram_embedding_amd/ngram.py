@@ -20,7 +20,9 @@ F32, BF16 = 0, 1
 W_MEM_D, W_D_MEM = 0, 1  # projection storage: [mem, d] or [d, mem] (fast path)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libngram.so")
+# NGRAM_LIBRARY names another build of the library (a variant under test);
+# by default the in-tree build next to this file is loaded.
+LIB_PATH = os.environ.get("NGRAM_LIBRARY") or os.path.join(_HERE, "libngram.so")
 
 
 class NgramError(RuntimeError):
