@@ -107,11 +107,12 @@ class Setup:
 # ---------------------------------------------------------------------------
 
 def algorithmic(w):
-    es = 4 if w.dtype == "f32" else 2
+    es = 4 if w.dtype == "f32" else 2              # activations, weights, E
+    tes = {"f32": 4, "bf16": 2, "fp8": 1}[w.tdtype]  # table storage
     n = w.n_tokens
     nbh = w.n_branches if w.n_branches > 1 else 1
     ids_b = 4 * (n + w.batch * w.history_len)
-    rows_b = n * w.n_tables * w.row_dim * es
+    rows_b = n * w.n_tables * w.row_dim * tes
     hid_b = n * nbh * w.hidden * es
     out_b = n * w.n_branches * w.hidden * es
     w_b = (w.n_branches + 1) * w.mem_dim * w.hidden * es
@@ -138,10 +139,9 @@ def source_sha(paths):
 
 
 _CS = "hashed_gram_embedding_amd/csrc/"
-# kernel sources of each stage, per route: decode (one new token per
-# sequence) and the fused route of every other workload
+# kernel sources of each stage, per route (see route())
 STAGE_SOURCES = {
-    ("gather", "decode"): [_CS + "gather.hip", _CS + "hashing.h"],
+    ("gather", "decode"): [_CS + "gather.hip", _CS + "hashing.h", _CS + "internal.h"],
     ("projection", "decode"): [_CS + "project_decode.hip"],
     ("gate_conv", "decode"): [_CS + "finalize.hip"],
     ("projection", "fused"): [_CS + "project_async.hip", _CS + "epilogue.h",
@@ -151,13 +151,22 @@ STAGE_SOURCES = {
     ("gather", "f32"): [_CS + "gather.hip"],
     ("projection", "f32"): [_CS + "project.hip"],
     ("gate_conv", "f32"): [_CS + "finalize.hip"],
+    ("hash", "materialised"): [_CS + "ids.hip", _CS + "hashing.h"],
+    ("gather", "materialised"): [_CS + "gather.hip", _CS + "internal.h"],
+    ("projection", "materialised"): [_CS + "project_async.hip", _CS + "epilogue.h"],
+    ("gate_conv", "materialised"): [_CS + "finalize.hip"],
 }
 
 
 def route(w) -> str:
+    """Kernel route of a workload's forward: fp32; decode (one new token per
+    sequence); fused (the projection gathers bf16 rows itself); materialised
+    (hash, gather to E, then the projection: fp8 tables, rows not 64-wide)."""
     if w.dtype == "f32":
         return "f32"
-    return "decode" if w.seq_len == 1 else "fused"
+    if w.seq_len == 1:
+        return "decode"
+    return "materialised" if w.tdtype == "fp8" or w.row_dim % 64 else "fused"
 
 
 def stage_source_sha(stage: str, w):
@@ -365,8 +374,8 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
             "history": w.history_len, "tokens_per_step": w.n_tokens,
-            "tables": f"{w.n_tables} x {w.rows()[0]}.. rows x {w.row_dim} {w.dtype}",
-            "table_gib": sum(w.rows()) * w.row_dim * (2 if w.dtype == "bf16" else 4) / 2 ** 30,
+            "tables": f"{w.n_tables} x {w.rows()[0]}.. rows x {w.row_dim} {w.tdtype}",
+            "table_gib": sum(w.rows()) * w.row_dim * {"f32": 4, "bf16": 2, "fp8": 1}[w.tdtype] / 2 ** 30,
             "mem_dim": w.mem_dim, "hidden": w.hidden, "branches": w.n_branches,
             "orders": list(w.orders), "heads_per_order": w.heads,
             "distinct_batches": setup.pool, "parallelism": "single GPU",

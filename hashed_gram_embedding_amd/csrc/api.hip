@@ -15,10 +15,16 @@ ngram::StageClock* ngram::g_open_stage = nullptr;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 
-int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : 4; }
+int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : dtype == NGRAM_FP8_E4M3 ? 1 : 4; }
+
+// dtype of the memory vector E: the tables', except that fp8 tables are
+// widened to bf16 while they are gathered
+int mem_dtype(const ngram_config* c) {
+  return c->table_dtype == NGRAM_FP8_E4M3 ? NGRAM_BF16 : c->table_dtype;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -70,9 +76,11 @@ bool is_prime_u32(uint64_t n) {
 
 int validate(const ngram_config* c) {
   if (c == nullptr) return NGRAM_EINVAL;
-  if (c->table_dtype != NGRAM_F32 && c->table_dtype != NGRAM_BF16) return NGRAM_EDTYPE;
+  if (c->table_dtype != NGRAM_F32 && c->table_dtype != NGRAM_BF16 &&
+      c->table_dtype != NGRAM_FP8_E4M3)
+    return NGRAM_EDTYPE;
   if (c->act_dtype != NGRAM_F32 && c->act_dtype != NGRAM_BF16) return NGRAM_EDTYPE;
-  if (c->table_dtype != c->act_dtype) return NGRAM_EDTYPE;
+  if (mem_dtype(c) != c->act_dtype) return NGRAM_EDTYPE;
   if (c->n_orders < 1 || c->n_orders > NGRAM_MAX_ORDER) return NGRAM_EINVAL;
   for (int o = 0; o < c->n_orders; ++o) {
     if (c->orders[o] < 1 || c->orders[o] > NGRAM_MAX_ORDER) return NGRAM_EINVAL;
@@ -89,8 +97,11 @@ int validate(const ngram_config* c) {
   if (c->row_dim < 1 || ((int64_t)c->row_dim * es) % 16 != 0) return NGRAM_ESHAPE;
   if ((int64_t)c->mem_dim != (int64_t)c->n_tables * c->row_dim) return NGRAM_EINVAL;
   if (c->hidden_dim < 4 || c->hidden_dim % 4 != 0) return NGRAM_ESHAPE;
-  if (c->table_dtype == NGRAM_BF16 && (c->mem_dim % 64 != 0 || c->hidden_dim % 32 != 0))
+  if (c->act_dtype == NGRAM_BF16 && (c->mem_dim % 64 != 0 || c->hidden_dim % 32 != 0))
     return NGRAM_ESHAPE;
+  if (c->table_dtype == NGRAM_FP8_E4M3)
+    for (int j = 0; j < c->n_tables; ++j)
+      if (!(c->table_scale[j] > 0.0f) || !isfinite(c->table_scale[j])) return NGRAM_EINVAL;
   if (c->n_branches < 1 || c->n_branches > NGRAM_MAX_BRANCHES) return NGRAM_EINVAL;
   if (c->conv_kernel != 4) return NGRAM_EINVAL;
   if (c->conv_dilation != c->orders[c->n_orders - 1]) return NGRAM_EINVAL;
@@ -104,7 +115,7 @@ int validate(const ngram_config* c) {
 
 // bf16 with W stored [d, mem]: operands copied global -> LDS (project_async).
 bool async_path(const ngram_config* c) {
-  return c->table_dtype == NGRAM_BF16 && c->w_layout == NGRAM_W_D_MEM;
+  return mem_dtype(c) == NGRAM_BF16 && c->w_layout == NGRAM_W_D_MEM;
 }
 // ... and the forward hashes and gathers inside the projection when every
 // 64-wide K step lies within one table row.
@@ -114,7 +125,7 @@ bool async_path(const ngram_config* c) {
 bool fused_gather(const ngram_config* c) {
   const char* e = getenv("NGRAM_FUSED_GATHER");
   if (e && e[0] == '0' && e[1] == 0) return false;
-  return async_path(c) && c->row_dim % 64 == 0;
+  return async_path(c) && c->table_dtype == NGRAM_BF16 && c->row_dim % 64 == 0;
 }
 
 // Decode (one new token per sequence, up to kDecodeMaxRows sequences): E is
@@ -181,14 +192,14 @@ Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward, int32_t T 
     L.plan.np = 1;
     size_t off = 0;
     L.e = off;  // decode E tiles: whole 16-token blocks
-    off = align_up(off + (size_t)((n_tok + 15) / 16 * 16) * c->mem_dim * esize_of(c->table_dtype));
+    off = align_up(off + (size_t)((n_tok + 15) / 16 * 16) * c->mem_dim * esize_of(mem_dtype(c)));
     L.split = off;
     off = align_up(off + (size_t)L.k_split * n_tok * (c->n_branches + 1) * c->hidden_dim *
                              sizeof(float));
     L.total = off;
     return L;
   }
-  const int dt = c->table_dtype;
+  const int dt = mem_dtype(c);
   const int nb = c->n_branches, d = c->hidden_dim;
   L.plan = plan_projection(dt, n_tok, d);
   if (async_path(c)) {
@@ -258,6 +269,7 @@ int check_tables(const ngram_config* c, const void* const* tables, TablePtrs* ou
     if (tables[j] == nullptr) return NGRAM_EINVAL;
     if (!aligned16(tables[j])) return NGRAM_EALIGN;
     out->p[j] = tables[j];
+    out->scale[j] = c->table_dtype == NGRAM_FP8_E4M3 ? c->table_scale[j] : 1.0f;
   }
   return NGRAM_OK;
 }
@@ -317,7 +329,7 @@ AsyncProjArgs async_args(const ngram_config* c, const ProjArgs& p) {
 // Launch the projection for E (or, with gather, for raw ids hashed in-kernel).
 hipError_t run_projection(const ngram_config* c, const Layout& L, const ProjArgs& p,
                           hipStream_t s) {
-  if (L.async < 0) return launch_projection(c->table_dtype, L.plan, p, s);
+  if (L.async < 0) return launch_projection(mem_dtype(c), L.plan, p, s);
   return launch_projection_async(false, L.async, async_args(c, p), s);
 }
 

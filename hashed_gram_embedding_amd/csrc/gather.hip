@@ -1,6 +1,8 @@
 // Gather + concatenation of the hashed rows into the memory vector E_t
 // ("Qwen3.8-Flash-Next 深度研究" §2.3: the row ids' rows are concatenated into
-// E_t; Engram's second component in "Qwen 4用上DeepSeek的Engram").
+// E_t; Engram's second component in "Qwen 4用上DeepSeek的Engram").  FP8 E4M3
+// tables (the same page, §9.3: FP8 storage with a per-tensor scale) are
+// widened to bf16 E on the way, each value times its table's scale.
 //
 // HBM-bound random reads.  One wavefront owns one token: its n_tables rows
 // are split into 16-byte chunks, lane l takes chunks l, l+64, ..., so a
@@ -17,24 +19,32 @@ namespace {
 
 constexpr int kGatherUnroll = 8;
 
+// FP8 tables: a source chunk holds 16 values and becomes two bf16 chunks of E
+// (fp8x16_to_bf16 applies the table's scale); otherwise chunks are copied.
+// row_chunks counts the 16-byte chunks of one table row in the table.
+template <bool FP8>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ row_idx,
                                                      int64_t n_tok, int32_t n_tables,
                                                      int32_t row_chunks, TablePtrs tabs,
                                                      uint4* __restrict__ mem) {
   __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
-  if (threadIdx.x < NGRAM_MAX_TABLES)
-    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[threadIdx.x < n_tables ? threadIdx.x : 0]);
+  __shared__ float s_scale[NGRAM_MAX_TABLES];
+  if (threadIdx.x < NGRAM_MAX_TABLES) {
+    const int j = threadIdx.x < n_tables ? threadIdx.x : 0;
+    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[j]);
+    s_scale[threadIdx.x] = tabs.scale[j];
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int waves_per_block = blockDim.x >> 6;
   const int64_t wave0 = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6);
   const int64_t wstride = (int64_t)gridDim.x * waves_per_block;
-  const int32_t chunks = n_tables * row_chunks;  // 16-byte chunks per token
+  const int32_t chunks = n_tables * row_chunks;  // table chunks per token
 
   for (int64_t tok = wave0; tok < n_tok; tok += wstride) {
     const int32_t* rix = row_idx + tok * n_tables;
-    uint4* dst = mem + tok * chunks;
+    uint4* dst = mem + tok * chunks * (FP8 ? 2 : 1);
     for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
       uint4 v[kGatherUnroll];
 #pragma unroll
@@ -50,7 +60,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
         const int q = base + u * 64 + lane;
-        if (q < chunks) dst[q] = v[u];
+        if (q < chunks) {
+          if (FP8) {
+            uint4 lo, hi;
+            fp8x16_to_bf16(v[u], s_scale[q / row_chunks], lo, hi);
+            dst[2 * q] = lo;
+            dst[2 * q + 1] = hi;
+          } else {
+            dst[q] = v[u];
+          }
+        }
       }
     }
   }
@@ -63,6 +82,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 // E is written in the decode projection's operand order (internal.h,
 // "decode E tiles"), so that kernel reads each 16-row x 32-k operand of
 // v_mfma_f32_16x16x32_bf16 as one contiguous kilobyte.
+template <bool FP8>
 __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restrict__ ids,
                                                           int32_t B, int32_t T,
                                                           const int32_t* __restrict__ hist,
@@ -71,17 +91,21 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
                                                           uint4* __restrict__ mem,
                                                           int32_t* __restrict__ err) {
   __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
-  if (threadIdx.x < NGRAM_MAX_TABLES)
-    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[threadIdx.x < h.n_tables ? threadIdx.x : 0]);
+  __shared__ float s_scale[NGRAM_MAX_TABLES];
+  if (threadIdx.x < NGRAM_MAX_TABLES) {
+    const int j = threadIdx.x < h.n_tables ? threadIdx.x : 0;
+    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[j]);
+    s_scale[threadIdx.x] = tabs.scale[j];
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int waves_per_block = blockDim.x >> 6;
   const int64_t n_tok = (int64_t)B * T;
   const int64_t wstride = (int64_t)gridDim.x * waves_per_block;
-  const int32_t chunks = h.n_tables * row_chunks;
+  const int32_t chunks = h.n_tables * row_chunks;  // table chunks per token
   const int jl = lane < h.n_tables ? lane : 0;
   const int order_l = h.orders[jl / h.heads];
-  const int32_t n_kk = chunks >> 2;  // 32-wide K steps per token
+  const int32_t n_kk = chunks * (FP8 ? 2 : 1) >> 2;  // 32-wide K steps per token
   for (int64_t tok = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6); tok < n_tok;
        tok += wstride) {
     const int32_t b = (int32_t)(tok / T);
@@ -90,6 +114,8 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
     context_ids<true>(ids, tok, b, t, hist, lut, h, err, c);
     const int32_t my_row = (int32_t)table_row(h, jl, order_l, c);
     uint4* dst = mem + (tok >> 4) * n_kk * 64 + (tok & 15);
+    // E chunk e (16 bytes, 8 bf16): K step e/4, quarter e%4
+    auto put = [&](int e, const uint4& x) { dst[(e >> 2) * 64 + (e & 3) * 16] = x; };
     for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
       uint4 v[kGatherUnroll];
 #pragma unroll
@@ -101,8 +127,17 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
       }
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
-        const int q = base + u * 64 + lane;  // chunk q: K step q/4, quarter q%4
-        if (q < chunks) dst[(q >> 2) * 64 + (q & 3) * 16] = v[u];
+        const int q = base + u * 64 + lane;
+        if (q < chunks) {
+          if (FP8) {
+            uint4 lo, hi;
+            fp8x16_to_bf16(v[u], s_scale[q / row_chunks], lo, hi);
+            put(2 * q, lo);
+            put(2 * q + 1, hi);
+          } else {
+            put(q, v[u]);
+          }
+        }
       }
     }
   }
@@ -114,26 +149,34 @@ hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t 
                               const int32_t* hist, const int32_t* lut, const HashArgs& h,
                               int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,
                               int32_t* err, hipStream_t s) {
-  // the tiled E layout is defined for bf16 rows of whole 32-wide K steps
-  if (dtype != NGRAM_BF16 || (n_tables * row_dim) % 32 != 0) return hipErrorInvalidValue;
-  const int32_t row_chunks = row_dim * 2 / 16;
+  // the tiled E layout is defined for bf16 E of whole 32-wide K steps
+  if ((dtype != NGRAM_BF16 && dtype != NGRAM_FP8_E4M3) || (n_tables * row_dim) % 32 != 0)
+    return hipErrorInvalidValue;
+  const bool fp8 = dtype == NGRAM_FP8_E4M3;
+  const int32_t row_chunks = row_dim * (fp8 ? 1 : 2) / 16;
   const int64_t n_tok = (int64_t)B * T;
   int64_t blocks = (n_tok + 3) / 4;
   if (blocks > 262144) blocks = 262144;
   if (blocks < 1) blocks = 1;
-  return launch(hash_gather_kernel, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h,
+  if (fp8)
+    return launch(hash_gather_kernel<true>, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h,
+                  row_chunks, t, static_cast<uint4*>(mem), err);
+  return launch(hash_gather_kernel<false>, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h,
                 row_chunks, t, static_cast<uint4*>(mem), err);
 }
 
 hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
                          int32_t row_dim, const TablePtrs& t, void* mem, hipStream_t s) {
-  const int esize = dtype == NGRAM_BF16 ? 2 : 4;
+  const int esize = dtype == NGRAM_BF16 ? 2 : dtype == NGRAM_FP8_E4M3 ? 1 : 4;
   const int32_t row_chunks = row_dim * esize / 16;
   const int threads = 256;
   int64_t blocks = (n_tok + 3) / 4;
   if (blocks > 262144) blocks = 262144;
   if (blocks < 1) blocks = 1;
-  return launch(gather_kernel, (unsigned)blocks, threads, 0, s, row_idx, n_tok, n_tables,
+  if (dtype == NGRAM_FP8_E4M3)
+    return launch(gather_kernel<true>, (unsigned)blocks, threads, 0, s, row_idx, n_tok, n_tables,
+                  row_chunks, t, static_cast<uint4*>(mem));
+  return launch(gather_kernel<false>, (unsigned)blocks, threads, 0, s, row_idx, n_tok, n_tables,
                 row_chunks, t, static_cast<uint4*>(mem));
 }
 

@@ -73,7 +73,37 @@ struct HashArgs {
 
 struct TablePtrs {
   const void* p[NGRAM_MAX_TABLES];
+  float scale[NGRAM_MAX_TABLES];  // fp8 tables: value = scale * decode(byte)
 };
+
+// OCP FP8 E4M3 -> fp32 (exact): sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent field 0 holds the subnormals m * 2^-9, S.1111.111 is NaN.
+__device__ __forceinline__ float fp8_e4m3_to_f32(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 24;
+  const uint32_t ex = (b >> 3) & 0xFu, m = b & 7u;
+  const float sub = __uint_as_float(sign | __float_as_uint((float)m * 0x1p-9f));
+  const float nor = __uint_as_float(sign | ((ex + 120u) << 23) | (m << 20));
+  const float v = ex == 0 ? sub : nor;
+  return (ex == 15u && m == 7u) ? __uint_as_float(sign | 0x7FC00000u) : v;
+}
+
+// 16 fp8 table values (one 16-byte chunk) -> 16 bf16 of E: each value times
+// the table's scale in fp32, then rounded to bf16 (both to nearest even).
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, float scale, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float a = fp8_e4m3_to_f32((w[i] >> (16 * h)) & 0xFFu) * scale;
+      const float b = fp8_e4m3_to_f32((w[i] >> (16 * h + 8)) & 0xFFu) * scale;
+      o[2 * i + h] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    }
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
 
 // Projection + gate-partials problem (one launch covers all segments: the
 // n_branches key projections, then the value projection).

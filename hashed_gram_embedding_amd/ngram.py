@@ -16,7 +16,7 @@ MAX_TABLES = 16
 MAX_ORDER = 4
 MAX_BRANCHES = 4
 ADD_RESIDUAL = 1
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2  # FP8_E4M3: table storage only
 W_MEM_D, W_D_MEM = 0, 1  # projection storage: [mem, d] or [d, mem] (fast path)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,7 @@ class NgramConfig(ctypes.Structure):
         ("table_dtype", ctypes.c_int32),
         ("act_dtype", ctypes.c_int32),
         ("w_layout", ctypes.c_int32),
+        ("table_scale", ctypes.c_float * MAX_TABLES),
     ]
 
 
@@ -60,8 +61,11 @@ def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_
                 row_dim: int, hidden_dim: int, n_branches: int, vocab: int,
                 vocab_compressed: int, dtype: int, pad_id: int = 0, rms_eps: float = 1e-6,
                 conv_kernel: int = 4, conv_dilation: Optional[int] = None,
-                w_layout: int = W_MEM_D) -> NgramConfig:
-    """Fill an NgramConfig; ``hash_mult`` is indexable as [table][slot]."""
+                w_layout: int = W_MEM_D, table_dtype: Optional[int] = None,
+                table_scales: Optional[Sequence[float]] = None) -> NgramConfig:
+    """Fill an NgramConfig; ``hash_mult`` is indexable as [table][slot].
+    ``dtype`` is the activation dtype and, unless ``table_dtype`` says
+    otherwise (FP8_E4M3 with one scale per table), the tables' too."""
     c = NgramConfig()
     c.n_orders = len(orders)
     for i, o in enumerate(orders):
@@ -83,9 +87,11 @@ def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_
     c.vocab_compressed = vocab_compressed
     c.pad_id = pad_id
     c.rms_eps = rms_eps
-    c.table_dtype = dtype
+    c.table_dtype = dtype if table_dtype is None else table_dtype
     c.act_dtype = dtype
     c.w_layout = w_layout
+    for j, sc in enumerate(table_scales or ()):
+        c.table_scale[j] = float(sc)
     return c
 
 

@@ -64,7 +64,18 @@ typedef enum ngram_status {
   NGRAM_EWORKSPACE = -7  /* workspace missing or smaller than required */
 } ngram_status;
 
-typedef enum ngram_dtype { NGRAM_F32 = 0, NGRAM_BF16 = 1 } ngram_dtype;
+/*
+ * NGRAM_FP8_E4M3 is a table storage type only: OCP FP8 E4M3 (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals
+ * m * 2^-9; S.1111.111 is NaN; no infinities).  Table j's row values are
+ * table_scale[j] * decode(byte), and the memory vector holds each as bf16:
+ * E = bf16(fp32(decode(byte) * table_scale[j])), each conversion rounding to
+ * nearest even.  The FP8 release of the model stores this table in FP8 with
+ * one scale per tensor, and a loader that discarded the scale degraded the
+ * model without any error ("Qwen3.8-Flash-Next 深度研究" §9.3): here the
+ * scale is an explicit part of every lookup.
+ */
+typedef enum ngram_dtype { NGRAM_F32 = 0, NGRAM_BF16 = 1, NGRAM_FP8_E4M3 = 2 } ngram_dtype;
 
 /*
  * Storage of the projection matrices (ngram_config.w_layout).
@@ -110,8 +121,9 @@ typedef struct ngram_config {
   int32_t pad_id;                                        /* in [0, vocab_compressed) */
   float rms_eps;                                         /* >= 0, RMSNorm epsilon */
   int32_t table_dtype;                                   /* ngram_dtype */
-  int32_t act_dtype;                                     /* ngram_dtype, == table_dtype */
+  int32_t act_dtype;                                     /* == table_dtype; bf16 for fp8 tables */
   int32_t w_layout;                                      /* ngram_w_layout */
+  float table_scale[NGRAM_MAX_TABLES];                   /* fp8 tables: finite, > 0 */
 } ngram_config;
 
 /* Human-readable name of a status code (static string). */
@@ -123,8 +135,9 @@ int ngram_abi_version(void);
 /*
  * Check a configuration without touching the GPU.  Returns NGRAM_OK or the
  * first failing status.  Shape rules: row_dim * sizeof(table dtype) must be a
- * multiple of 16 bytes; for bf16, mem_dim % 64 == 0 and hidden_dim % 32 == 0;
- * for fp32, hidden_dim % 4 == 0.  conv_kernel must be 4 (the pages' kernel)
+ * multiple of 16 bytes; for bf16 activations, mem_dim % 64 == 0 and
+ * hidden_dim % 32 == 0; for fp32, hidden_dim % 4 == 0.  fp8 tables take bf16
+ * activations, and the memory vector E is bf16.  conv_kernel must be 4 (the pages' kernel)
  * and conv_dilation the largest order.
  */
 int ngram_config_validate(const ngram_config* cfg);
@@ -161,7 +174,7 @@ int ngram_hash(const ngram_config* cfg, const int32_t* comp_ids, int32_t B, int3
  *   row_idx  device int32[n_tok, n_tables]; each entry must be < rows[j]
  *   tables   HOST array of n_tables device pointers, table j is
  *            [rows[j], row_dim] of table_dtype
- *   mem      device [n_tok, mem_dim] of table_dtype (output)
+ *   mem      device [n_tok, mem_dim] (output): table_dtype, bf16 for fp8 tables
  */
 int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
                  const void* const* tables, void* mem, void* stream);
@@ -175,7 +188,7 @@ int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
  *   hidden   device [n_tok, nbh, d] act_dtype with hidden_branch_stride == 0
  *            (nbh = 1: one query row shared by all branches) or == d
  *            (nbh = n_branches: one query row per branch)
- *   mem      device [n_tok, mem_dim] table_dtype (E)
+ *   mem      device [n_tok, mem_dim] (E): table_dtype, bf16 for fp8 tables
  *   w_k      device [n_branches, mem_dim, d] act_dtype and w_v [mem_dim, d]
  *            (NGRAM_W_MEM_D), or [n_branches, d, mem_dim] and [d, mem_dim]
  *            (NGRAM_W_D_MEM)

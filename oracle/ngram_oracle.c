@@ -22,6 +22,8 @@
  *      Norm(K_t)); U_t = g_t * V_t; Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))).
  *  [C] same page, §3-D lineage table: the related Over-Encoding method hashes
  *      by a modulus.
+ *  [D] same page, §9.3: the FP8 release stores the N-gram table in FP8 with a
+ *      per-tensor scale (a loader that dropped the scale broke the model).
  *
  * Readings where the pages leave a step open (each is the plainest one the
  * rest of the text supports):
@@ -32,7 +34,9 @@
  *  - RMSNorm(x) = gamma * x / sqrt(mean(x^2) + eps); the gate's scaled dot
  *    product divides by sqrt(d); the gate is the logistic sigmoid;
  *  - conv tap i multiplies position t - i*dilation, depthwise, no bias, zero
- *    before the sequence start (or the caller's normalised state rows).
+ *    before the sequence start (or the caller's normalised state rows);
+ *  - FP8 table values are OCP E4M3 times the table's scale, held in E as
+ *    bf16 (product rounded to fp32, then to bf16).
  */
 #include <math.h>
 #include <stdint.h>
@@ -42,7 +46,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
 
 static double load_value(const void* base, int dtype, int64_t i) {
   if (dtype == ORC_F32) return (double)((const float*)base)[i];
@@ -135,19 +139,67 @@ void orc_hash(const int32_t* comp, int32_t B, int32_t T, const int32_t* hist,
 }
 
 /*
+ * FP8 E4M3 (the OCP 8-bit floating-point format): sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits.  Exponent field 0 encodes the subnormals
+ * m * 2^-9; exponent field 15 with mantissa 7 is NaN; there are no
+ * infinities, so the largest value is 1.75 * 2^8 = 448.
+ */
+double orc_fp8_e4m3_value(uint32_t byte) {
+  const int sign = (byte >> 7) & 1;
+  const int ex = (byte >> 3) & 15;
+  const int m = byte & 7;
+  double v;
+  if (ex == 15 && m == 7)
+    v = NAN;
+  else if (ex == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* fp32 -> bf16 (the upper 16 bits of the fp32 pattern), round to nearest,
+ * ties to even; the result is returned as the value it encodes. */
+static double round_bf16(float f) {
+  uint32_t bits;
+  memcpy(&bits, &f, sizeof bits);
+  const uint32_t low = bits & 0xFFFFu;
+  uint32_t high = bits >> 16;
+  if (low > 0x8000u || (low == 0x8000u && (high & 1u))) high += 1;
+  bits = high << 16;
+  float r;
+  memcpy(&r, &bits, sizeof r);
+  return (double)r;
+}
+
+/*
  * Step 3 -- gather and concatenate [A, second component; B, the row ids' rows
  * joined end to end into E_t]: E_t = table_0[r_0] ++ table_1[r_1]
  * ++ ... in table order (orders ascending, then heads).  e is [n_tok, mem]
- * with mem = n_tables * row_dim.
+ * with mem = n_tables * row_dim.  FP8 tables (dtype ORC_FP8): a row value is
+ * scales[j] * decode(byte), and E holds it as bf16 -- the product rounded to
+ * fp32, then to bf16, each to nearest even (the storage format's
+ * definition of E; the scale is per table, [D]).
  */
 void orc_gather(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
-                const void* const* tables, int32_t dtype, int32_t row_dim, double* e) {
+                const void* const* tables, int32_t dtype, int32_t row_dim, const float* scales,
+                double* e) {
   const int64_t mem = (int64_t)n_tables * row_dim;
   for (int64_t t = 0; t < n_tok; ++t)
     for (int32_t j = 0; j < n_tables; ++j) {
       int64_t r = row_idx[t * n_tables + j];
-      for (int32_t c = 0; c < row_dim; ++c)
-        e[t * mem + (int64_t)j * row_dim + c] = load_value(tables[j], dtype, r * row_dim + c);
+      for (int32_t c = 0; c < row_dim; ++c) {
+        double v;
+        if (dtype == ORC_FP8) {
+          const uint8_t byte = ((const uint8_t*)tables[j])[r * row_dim + c];
+          /* exact in double (4 + 24 significant bits), then rounded to fp32 */
+          const float prod = (float)(orc_fp8_e4m3_value(byte) * (double)scales[j]);
+          v = round_bf16(prod);
+        } else {
+          v = load_value(tables[j], dtype, r * row_dim + c);
+        }
+        e[t * mem + (int64_t)j * row_dim + c] = v;
+      }
     }
 }
 

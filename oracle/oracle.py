@@ -20,7 +20,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libngram_oracle.so")
-_DT = {"f32": 0, "bf16": 1}
+_DT = {"f32": 0, "bf16": 1, "fp8": 2}
 _lib = None
 
 _p = ctypes.c_void_p
@@ -57,7 +57,9 @@ def _load(path: str):
     L.orc_compress.restype = _i64
     L.orc_compress.argtypes = [_p, _i64, _p, _i32, _i32, _i32, _p]
     L.orc_hash.argtypes = [_p, _i32, _i32, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p]
-    L.orc_gather.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p]
+    L.orc_gather.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p, _p]
+    L.orc_fp8_e4m3_value.restype = _f64
+    L.orc_fp8_e4m3_value.argtypes = [ctypes.c_uint32]
     L.orc_project.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p]
     L.orc_gate.argtypes = [_p, _i32, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _f64, _p]
     L.orc_gated_value.argtypes = [_p, _p, _i64, _i32, _i32, _p]
@@ -83,7 +85,12 @@ def set_num_threads(n: int) -> None:
 
 
 def _storage(a, dtype: str) -> np.ndarray:
-    return _c(a, np.float32 if dtype == "f32" else np.uint16)
+    return _c(a, {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype])
+
+
+def fp8_e4m3_value(byte: int) -> float:
+    """The value an OCP FP8 E4M3 byte encodes."""
+    return float(lib().orc_fp8_e4m3_value(int(byte)))
 
 
 # ---------------------------------------------------------------------------
@@ -114,20 +121,24 @@ def hash_rows(comp, hist, orders: Sequence[int], heads: int, rows: Sequence[int]
     return out
 
 
-def gather(row_idx, tables: Sequence[np.ndarray], dtype: str) -> np.ndarray:
-    """row_idx int32[n, nt]; tables[j] [rows_j, row_dim] storage -> float64[n, mem]."""
+def gather(row_idx, tables: Sequence[np.ndarray], dtype: str, scales=None) -> np.ndarray:
+    """row_idx int32[n, nt]; tables[j] [rows_j, row_dim] storage -> float64[n, mem].
+    ``dtype`` "fp8" takes uint8 E4M3 tables and one float32 scale per table."""
     row_idx = _c(row_idx, np.int32)
     n, nt = row_idx.shape
     tabs = [_storage(t, dtype) for t in tables]
     row_dim = tabs[0].shape[1]
     ptrs = (ctypes.c_void_p * nt)(*[t.ctypes.data for t in tabs])
+    sc = None if scales is None else _c(list(scales), np.float32)
+    if dtype == "fp8" and (sc is None or sc.size < nt):
+        raise ValueError("fp8 tables need one scale per table")
     e = np.empty((n, nt * row_dim), dtype=np.float64)
-    lib().orc_gather(_ptr(row_idx), n, nt, ptrs, _DT[dtype], row_dim, _ptr(e))
+    lib().orc_gather(_ptr(row_idx), n, nt, ptrs, _DT[dtype], row_dim, _ptr(sc), _ptr(e))
     return e
 
 
 def gather_from_rows(row_idx, provider: Callable[[int, np.ndarray], np.ndarray],
-                     dtype: str) -> np.ndarray:
+                     dtype: str, scales=None) -> np.ndarray:
     """Gather when the tables are too large to hold: ``provider(j, rows)`` returns
     the storage of rows ``rows`` of table j; the oracle indexes a compact copy."""
     row_idx = _c(row_idx, np.int32)
@@ -136,7 +147,7 @@ def gather_from_rows(row_idx, provider: Callable[[int, np.ndarray], np.ndarray],
         uniq, inv = np.unique(row_idx[:, j], return_inverse=True)
         compact.append(provider(j, uniq))
         remap[:, j] = inv.reshape(-1)
-    return gather(remap, compact, dtype)
+    return gather(remap, compact, dtype, scales)
 
 
 def project(e, w, dtype: str) -> np.ndarray:
@@ -194,10 +205,12 @@ def conv_block(u, conv_w, dtype: str, dilation: int, gamma_u=None, eps: float = 
 
 def forward(raw, hist_raw, lut, vocab: int, vocab_c: int, orders, heads: int, rows, mult,
             tables_or_provider, hidden, wk, wv, conv_w, dtype: str, *, gamma_q=None,
-            gamma_k=None, gamma_u=None, eps: float = 1e-6, conv_state=None, pad_id: int = 0):
+            gamma_k=None, gamma_u=None, eps: float = 1e-6, conv_state=None, pad_id: int = 0,
+            table_dtype: Optional[str] = None, table_scales=None):
     """Full forward on raw ids int32[B, T] (history raw int32[B, H] or None).
 
-    ``tables_or_provider``: list of full tables, or ``provider(j, rows)``.
+    ``tables_or_provider``: list of full tables, or ``provider(j, rows)``, in
+    ``table_dtype`` (default ``dtype``; "fp8" with ``table_scales``).
     hidden: [B*T, nbh, d] storage; wk: [nb, mem, d]; wv: [mem, d]; conv_w: [4, d].
     Returns a dict with every intermediate (float64 where floating point).
     """
@@ -209,10 +222,11 @@ def forward(raw, hist_raw, lut, vocab: int, vocab_c: int, orders, heads: int, ro
         hist_c, bad_h = compress(hist_raw, lut, vocab, vocab_c, pad_id)
         bad += bad_h
     r = hash_rows(comp, hist_c, orders, heads, rows, mult, pad_id)
+    tdt = table_dtype or dtype
     if callable(tables_or_provider):
-        e = gather_from_rows(r, tables_or_provider, dtype)
+        e = gather_from_rows(r, tables_or_provider, tdt, table_scales)
     else:
-        e = gather(r, tables_or_provider, dtype)
+        e = gather(r, tables_or_provider, tdt, table_scales)
     wk = np.asarray(wk)
     nb = wk.shape[0]
     k = np.stack([project(e, wk[b], dtype) for b in range(nb)], axis=1)

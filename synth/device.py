@@ -26,6 +26,10 @@ def lib():
         L.synth_fill_normal.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                         ctypes.c_uint64, ctypes.c_int64, ctypes.c_float,
                                         ctypes.c_void_p]
+        L.synth_fill_normal_fp8.restype = ctypes.c_int
+        L.synth_fill_normal_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                            ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                            ctypes.c_void_p]
         _LIB = L
     return _LIB
 
@@ -50,6 +54,19 @@ def fill_normal(t, seed: int, sigma: float, offset: int = 0, stream=None):
     return t
 
 
+def fill_normal_fp8(t, seed: int, sigma: float, inv_scale: float, offset: int = 0, stream=None):
+    """Fill a contiguous uint8 CUDA tensor with E4M3 codes of normal draws * inv_scale."""
+    import torch
+    assert t.is_cuda and t.is_contiguous() and t.dtype == torch.uint8
+    rc = lib().synth_fill_normal_fp8(ctypes.c_void_p(t.data_ptr()), t.numel(),
+                                     ctypes.c_uint64(seed & ((1 << 64) - 1)), offset,
+                                     ctypes.c_float(float(rng.normal_scale(sigma))),
+                                     ctypes.c_float(float(inv_scale)), _stream_ptr(stream))
+    if rc != 0:
+        raise RuntimeError(f"synth_fill_normal_fp8 failed ({rc})")
+    return t
+
+
 def torch_dtype(w: Workload):
     import torch
     return torch.float32 if w.dtype == "f32" else torch.bfloat16
@@ -59,8 +76,12 @@ def make_tables(w: Workload, device="cuda"):
     import torch
     out = []
     for j, r in enumerate(w.rows()):
-        t = torch.empty((r, w.row_dim), dtype=torch_dtype(w), device=device)
-        out.append(fill_normal(t, w.table_seed(j), w.table_sigma))
+        if w.tdtype == "fp8":
+            t = torch.empty((r, w.row_dim), dtype=torch.uint8, device=device)
+            out.append(fill_normal_fp8(t, w.table_seed(j), w.table_sigma, 1.0 / w.table_scale))
+        else:
+            t = torch.empty((r, w.row_dim), dtype=torch_dtype(w), device=device)
+            out.append(fill_normal(t, w.table_seed(j), w.table_sigma))
     return out
 
 

@@ -95,11 +95,22 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal_values(seed: int, idx, sigma: float, dtype: str) -> np.ndarray:
-    """Normal draws stored as ``dtype``: 'f32' -> float32, 'bf16' -> uint16 bits."""
+def f32_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to OCP FP8 E4M3 (nearest, ties to even); uint8 codes.  Uses
+    torch's float8_e4m3fn conversion; inputs stay within +-448."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def normal_values(seed: int, idx, sigma: float, dtype: str, inv_scale: float = 1.0) -> np.ndarray:
+    """Normal draws stored as ``dtype``: 'f32' -> float32, 'bf16' -> uint16 bits,
+    'fp8' -> uint8 E4M3 codes of draw * inv_scale (one fp32 multiply)."""
     x = normal_f32(seed, idx, sigma)
     if dtype == "f32":
         return x
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
+    if dtype == "fp8":
+        return f32_to_fp8_e4m3_bits(x * np.float32(inv_scale))
     raise ValueError(f"unknown dtype {dtype!r}")

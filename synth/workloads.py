@@ -16,7 +16,8 @@ Input recipe (what the generator draws; none of it is the method itself):
   start, otherwise it is fresh Zipf).
 * LUT: seeded surjective map, raw 0 -> 0 (pad); raw [1, V) onto [1, C).
 * hash multipliers: SplitMix64 draws forced odd, one per (table, n-gram slot).
-* tables N(0, 0.02); hidden N(0, 1); W_K, W_V N(0, 1/sqrt(mem));
+* tables N(0, 0.02) (FP8 tables: the same draws divided by the table scale,
+  rounded to E4M3); hidden N(0, 1); W_K, W_V N(0, 1/sqrt(mem));
   conv taps N(0, 0.5); RMSNorm gains 1 unless a test asks for random gains.
 """
 from __future__ import annotations
@@ -89,6 +90,8 @@ class Workload:
     rms_eps: float = 1e-6
     explicit_rows: tuple = ()  # table sizes given outright
     param_index: int = 0       # workloads that share tables/weights share this (0: own)
+    table_dtype: Optional[str] = None  # tables' storage if not ``dtype``: 'fp8' (E4M3)
+    table_scale: float = 2.0 ** -12    # fp8 tables: value = table_scale * code
 
     @property
     def seed(self) -> int:
@@ -102,6 +105,16 @@ class Workload:
     @property
     def vocab_compressed(self) -> int:
         return compressed_vocab(self.vocab)
+
+    @property
+    def tdtype(self) -> str:
+        """Storage dtype of the tables."""
+        return self.table_dtype or self.dtype
+
+    def table_scales(self) -> list:
+        """Per-table scales (fp8 tables; 1 otherwise)."""
+        s = self.table_scale if self.tdtype == "fp8" else 1.0
+        return [s] * self.n_tables
 
     @property
     def n_tables(self) -> int:
@@ -176,6 +189,16 @@ WORKLOADS = {
                                         orders=(2, 3), heads=4, row_start=20000003,
                                         row_dim=320, hidden=2560, n_branches=4,
                                         dtype="bf16", zipf_s=1.3, param_index=3),
+    # the same decode and prefill steps over the tables stored as FP8 E4M3
+    # (scale 2^-12: the draws of N(0, 0.02) span at most +-0.07 -> codes +-283)
+    "qwen_decode_fp8": Workload("qwen_decode_fp8", 3, vocab=248320, batch=256, seq_len=1,
+                                history_len=2, orders=(2, 3), heads=4, row_start=20000003,
+                                row_dim=320, hidden=2560, n_branches=1, dtype="bf16",
+                                zipf_s=1.1, param_index=3, table_dtype="fp8"),
+    "qwen_prefill_fp8": Workload("qwen_prefill_fp8", 4, vocab=248320, batch=1, seq_len=262144,
+                                 history_len=0, orders=(2, 3), heads=4, row_start=20000003,
+                                 row_dim=320, hidden=2560, n_branches=1, dtype="bf16",
+                                 zipf_s=1.1, copy_prob=0.2, param_index=3, table_dtype="fp8"),
 }
 
 
@@ -282,13 +305,14 @@ def table_row_values(w: Workload, j: int, rows: np.ndarray) -> np.ndarray:
     """Rows ``rows`` of table ``j``: [len(rows), row_dim] (f32 or bf16 bits)."""
     rows = np.asarray(rows, dtype=np.int64)
     idx = rows[:, None] * w.row_dim + np.arange(w.row_dim, dtype=np.int64)[None, :]
-    return rng.normal_values(w.table_seed(j), idx, w.table_sigma, w.dtype)
+    return rng.normal_values(w.table_seed(j), idx, w.table_sigma, w.tdtype, 1.0 / w.table_scale)
 
 
 def table_values(w: Workload, j: int) -> np.ndarray:
     """Whole table ``j`` (only sensible for the small workloads)."""
     n = w.rows()[j] * w.row_dim
-    return rng.normal_values(w.table_seed(j), np.arange(n), w.table_sigma, w.dtype).reshape(
+    return rng.normal_values(w.table_seed(j), np.arange(n), w.table_sigma, w.tdtype,
+                             1.0 / w.table_scale).reshape(
         -1, w.row_dim)
 
 
@@ -343,4 +367,6 @@ def layer_config(w: Workload, w_layout: str = "mem_d") -> dict:
                 hash_mult=hash_multipliers(w), row_dim=w.row_dim, hidden_dim=w.hidden,
                 n_branches=w.n_branches, vocab=w.vocab, vocab_compressed=w.vocab_compressed,
                 dtype=0 if w.dtype == "f32" else 1, pad_id=0, rms_eps=w.rms_eps,
-                w_layout={"mem_d": 0, "d_mem": 1}[w_layout])
+                w_layout={"mem_d": 0, "d_mem": 1}[w_layout],
+                table_dtype={"f32": 0, "bf16": 1, "fp8": 2}[w.tdtype],
+                table_scales=w.table_scales())

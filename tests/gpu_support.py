@@ -48,7 +48,7 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def tables(w: W.Workload):
-    key = (w.param_seed, tuple(w.rows()), w.row_dim, w.dtype)
+    key = (w.param_seed, tuple(w.rows()), w.row_dim, w.tdtype)
     if key not in _TABLES:
         # the Qwen-scale set is 95 GiB: keep at most one large set resident
         if sum(w.rows()) * w.row_dim > 1e9:
@@ -92,6 +92,11 @@ def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
 TOL = 2e-3  # normwise relative error bound for floating-point outputs
 
 
+def oracle_table_kw(w: W.Workload) -> dict:
+    """The oracle's table arguments for a workload (storage dtype, scales)."""
+    return dict(table_dtype=w.tdtype, table_scales=w.table_scales())
+
+
 def oracle_rows(w: W.Workload):
     """Row provider for the oracle: rows regenerated on the host."""
     return lambda j, rows: W.table_row_values(w, j, rows)
@@ -120,7 +125,8 @@ def oracle_forward_window(orc, w, ids, hist, b, start, length, hidden_fn, wk_hos
         kw = dict(gamma_q=gam["q"], gamma_k=gam["k"], gamma_u=gam["u"])
     out = orc.forward(sub, hist_sub, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders,
                       w.heads, w.rows(), W.hash_multipliers(w), oracle_rows(w), hid, wk_host,
-                      wv_host, conv_host, w.dtype, eps=w.rms_eps, conv_state=conv_state, **kw)
+                      wv_host, conv_host, w.dtype, eps=w.rms_eps, conv_state=conv_state,
+                      **oracle_table_kw(w), **kw)
     keep = slice(start - s0, start - s0 + length)
     return {k: (v[keep] if isinstance(v, np.ndarray) and v.ndim >= 2 and v.shape[0] == len(toks)
                 else v) for k, v in out.items()}

@@ -59,7 +59,7 @@ def test_config_layout_matches_c(H):
 
 
 def test_status_strings_and_version(H):
-    assert H.ngram.abi_version() == 2
+    assert H.ngram.abi_version() == 3
     for code in range(-7, 1):
         assert H.ngram.status_str(code).startswith("NGRAM_")
 
@@ -109,6 +109,23 @@ def test_validation_codes(H):
     c = _cfg(H)
     c.rms_eps = float("nan")
     assert H.ngram_config_validate(c) == E["INVAL"]
+    # FP8 tables: bf16 activations, rows of whole 16-byte chunks, positive finite scales
+    f = _cfg(H, "qwen_decode_fp8")
+    assert H.ngram_config_validate(f) == 0
+    f.table_scale[3] = 0.0
+    assert H.ngram_config_validate(f) == E["INVAL"]
+    f = _cfg(H, "qwen_decode_fp8")
+    f.table_scale[0] = float("inf")
+    assert H.ngram_config_validate(f) == E["INVAL"]
+    f = _cfg(H, "qwen_decode_fp8")
+    f.act_dtype = 0
+    assert H.ngram_config_validate(f) == E["DTYPE"]                # fp8 tables, fp32 activations
+    f = _cfg(H, "qwen_decode_fp8")
+    f.row_dim, f.mem_dim = 312, 8 * 312
+    assert H.ngram_config_validate(f) == E["SHAPE"]                # 312-byte fp8 rows
+    c = _cfg(H)
+    c.table_dtype = 2                                              # fp8 tables, fp32 activations
+    assert H.ngram_config_validate(c) == E["DTYPE"]
     assert H.ngram.lib().ngram_config_validate(None) == E["INVAL"]
 
 

@@ -42,6 +42,11 @@ MUTANTS = [
     ("conv drops the residual U", "delta[off + n] = u[off + n] + c / (1.0 + exp(-c));",
      "delta[off + n] = c / (1.0 + exp(-c));"),
     ("conv state row off by one", "int64_t s = (int64_t)span + p;", "int64_t s = (int64_t)span + p - 1;"),
+    ("fp8 exponent bias 8", "v = ldexp(1.0 + m / 8.0, ex - 7);", "v = ldexp(1.0 + m / 8.0, ex - 8);"),
+    ("fp8 subnormal step 2^-10", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("fp8 table scale dropped", "* (double)scales[j]);", "* 1.0);"),
+    ("fp8 E rounded to bf16 by truncation", "if (low > 0x8000u || (low == 0x8000u && (high & 1u))) high += 1;",
+     "(void)low;"),
 ]
 
 # the pins run against each mutant (test function, keyword arguments)
@@ -66,6 +71,8 @@ PINS = [
     (P.test_conv_single_tap_alignment, {"tap": 1}),
     (P.test_conv_single_tap_alignment, {"tap": 2}),
     (P.test_conv_causal_and_state_streaming, {}),
+    (P.test_fp8_decode_definition_and_library, {}),
+    (P.test_gather_fp8_scaled_bf16, {}),
 ]
 
 

@@ -251,6 +251,57 @@ def test_gather_bf16_conversion_exact(orc):
             assert np.array_equal(e[t, j * 64:(j + 1) * 64], ref)
 
 
+# Values of OCP FP8 E4M3 codes fixed by the format's definition (bias 7, 3
+# mantissa bits, subnormals m * 2^-9, S.1111.111 NaN, no infinities).
+FP8_CODES = [(0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+             (0x0F, 1.875 * 2.0 ** -6), (0x38, 1.0), (0x39, 1.125), (0x40, 2.0),
+             (0x57, 15.0), (0x7E, 448.0), (0xB8, -1.0), (0xFE, -448.0), (0x81, -(2.0 ** -9))]
+
+
+def test_fp8_decode_definition_and_library(orc):
+    for code, value in FP8_CODES:
+        assert orc.fp8_e4m3_value(code) == value, hex(code)
+    assert np.isnan(orc.fp8_e4m3_value(0x7F)) and np.isnan(orc.fp8_e4m3_value(0xFF))
+    assert math.copysign(1.0, orc.fp8_e4m3_value(0x80)) == -1.0  # negative zero
+    # every code against torch's float8_e4m3fn
+    codes = np.arange(256, dtype=np.uint8)
+    mine = np.array([orc.fp8_e4m3_value(c) for c in codes])
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), ~fin) and np.array_equal(mine[fin], ref[fin])
+
+
+def test_gather_fp8_scaled_bf16(orc):
+    """E of an FP8 table: code value times the table's scale, rounded to fp32,
+    then to bf16 (torch's conversions as the reference); distinct scales per
+    table, each applied to its own table only."""
+    rs = np.random.default_rng(5)
+    codes = rs.integers(0, 256, (3, 50, 32)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    scales = [2.0 ** -12, 0.3, 1.7e-3]
+    r = rs.integers(0, 50, (9, 3)).astype(np.int32)
+    e = orc.gather(r, [codes[j] for j in range(3)], "fp8", scales)
+    for j in range(3):
+        v = torch.from_numpy(codes[j][r[:, j]]).view(torch.float8_e4m3fn).float()
+        ref = (v * torch.tensor(scales[j], dtype=torch.float32)).bfloat16().double().numpy()
+        assert np.array_equal(e[:, j * 32:(j + 1) * 32], ref), j
+    with pytest.raises(ValueError):
+        orc.gather(r, [codes[j] for j in range(3)], "fp8")
+
+
+def test_fp8_tables_generator(orc):
+    """The FP8 tables' codes are the bf16 tables' draws over the scale, rounded
+    to E4M3: decoding them lands within half an E4M3 step of the draw."""
+    w = W.get("qwen_decode_fp8")
+    rows = np.array([0, 1, 12345, w.rows()[0] - 1])
+    codes = W.table_row_values(w, 0, rows)
+    draws = rng.normal_f32(w.table_seed(0), (rows[:, None] * w.row_dim +
+                                            np.arange(w.row_dim)[None, :]).ravel(), w.table_sigma)
+    vals = np.array([orc.fp8_e4m3_value(c) for c in codes.ravel()]) * w.table_scale
+    rel = np.abs(vals - draws) / np.maximum(np.abs(draws), 2.0 ** -6 * w.table_scale)
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+
+
 # --------------------------------------------------------------------------
 # projections, gate, gated value
 # --------------------------------------------------------------------------

@@ -116,6 +116,50 @@ def test_forward_qwen_decode_full(orc, layout):
     assert e_out < G.TOL and e_gate < G.TOL
 
 
+def test_forward_qwen_decode_fp8_full(orc):
+    """FP8 tables on the decode route: hash + gather widens the rows to bf16
+    E (times each table's scale) for the weight-stationary projection."""
+    w = W.get("qwen_decode_fp8")
+    print("[forward] qwen_decode_fp8", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, layout="d_mem")
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    wk, wv, cw, gam = _host_params(w, inp)
+    ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
+                      w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
+                      W.hidden_values(w, np.arange(ids.size)), wk, wv, cw, w.dtype,
+                      eps=w.rms_eps, **G.oracle_table_kw(w))
+    e_out = G.rel_err(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"])
+    e_gate = G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"])
+    print(f"   decode fp8 rel_err out={e_out:.3e} gate={e_gate:.3e}")
+    assert e_out < G.TOL and e_gate < G.TOL
+
+
+@pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
+def test_forward_engram_small_fp8(orc, layout):
+    """FP8 tables on the prefill routes: gather to bf16 E, then the
+    projection kernel of the layout (E materialised)."""
+    w = W.get("engram_small").replace(table_dtype="fp8", batch=2, seq_len=1000)
+    print(f"[forward] engram_small fp8 {layout}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, layout=layout)
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 300), (1, 650, 350)])
+
+
+def test_forward_qwen_prefill_fp8(orc):
+    w = W.get("qwen_prefill_fp8")
+    print("[forward] qwen_prefill_fp8 262144 tokens", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, layout="d_mem")
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    T = w.seq_len
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 24), (0, 98765, 24), (0, T - 24, 24)])
+
+
 @pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
 def test_forward_qwen_decode_conv_state_and_residual(orc, layout):
     """A populated conv state (the last 9 normalised rows of each sequence)."""

@@ -94,6 +94,39 @@ def test_gather_bit_exact(orc, name):
     assert np.array_equal(G.to_f64(mem[torch.from_numpy(sample).cuda()]), e_ref)
 
 
+@pytest.mark.parametrize("name", ["engram_small_fp8", "qwen_decode_fp8"])
+def test_gather_fp8_bit_exact(orc, name):
+    """FP8 tables: every token's E equals the E4M3 values at the oracle's row
+    ids times the table's scale, rounded to bf16 (torch's conversions on the
+    device, all tokens), and the oracle's own gather on a sample."""
+    H = G.H()
+    w = (W.get("engram_small").replace(table_dtype="fp8") if name == "engram_small_fp8"
+         else W.get(name))
+    print(f"[gather fp8] {name}", flush=True)
+    cfg = G.config(w)
+    ids, hist = _ids(w)
+    lut = W.make_lut(w)
+    comp, _ = orc.compress(ids, lut, w.vocab, w.vocab_compressed)
+    hc = orc.compress(hist, lut, w.vocab, w.vocab_compressed)[0] if hist is not None else None
+    ref_rows = orc.hash_rows(comp, hc, w.orders, w.heads, w.rows(), W.hash_multipliers(w))
+    tabs = G.tables(w)
+    d_rows = torch.from_numpy(ref_rows).cuda()
+    n = ref_rows.shape[0]
+    mem = torch.empty((n, w.mem_dim), dtype=torch.bfloat16, device="cuda")
+    H.ngram_gather(cfg, d_rows, tabs, mem)
+    torch.cuda.synchronize()
+    scale = torch.tensor(w.table_scale, dtype=torch.float32, device="cuda")
+    for j in range(w.n_tables):
+        codes = tabs[j].index_select(0, d_rows[:, j].long())
+        want = (codes.view(torch.float8_e4m3fn).float() * scale).bfloat16()
+        got = mem[:, j * w.row_dim:(j + 1) * w.row_dim]
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), j
+    rs = np.random.default_rng(4)
+    sample = np.unique(np.concatenate([[0, n - 1], rs.integers(0, n, 200)]))
+    e_ref = orc.gather_from_rows(ref_rows[sample], G.oracle_rows(w), "fp8", w.table_scales())
+    assert np.array_equal(G.to_f64(mem[torch.from_numpy(sample).cuda()]), e_ref)
+
+
 def _synthetic_memory(w, n, seed):
     """E for op-level gate tests: N(0, 0.02) values of the table dtype."""
     return rng.normal_values(seed, np.arange(n * w.mem_dim), 0.02, w.dtype).reshape(n, w.mem_dim)
