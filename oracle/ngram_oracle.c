@@ -329,3 +329,205 @@ void orc_conv_block(const double* u, int32_t B, int32_t T, int32_t nb, int32_t d
   }
   free(nrm);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the layer (the gradients a training step needs: tables, W_K,
+ * W_V, conv taps, query, RMSNorm gains), each step the chain rule of the
+ * forward step above it, written out with the forward's own definitions.
+ * Outputs marked "accumulated" are added to, the others overwritten.
+ * ------------------------------------------------------------------------ */
+
+/* RMSNorm y = gamma (.) x / r, r = sqrt(mean(x^2) + eps), backward for one
+ * row: dx = gamma (.) dy / r - x * sum(gamma dy x) / (d r^3); dgamma += dy x / r. */
+static void rms_backward_row(const double* x, const double* dy, const void* gamma, int32_t dtype,
+                             int32_t d, double eps, double* dx, double* dgamma) {
+  double ss = 0.0;
+  for (int32_t n = 0; n < d; ++n) ss += x[n] * x[n];
+  const double r = sqrt(ss / d + eps);
+  double s = 0.0;
+  for (int32_t n = 0; n < d; ++n) {
+    const double g = gamma ? load_value(gamma, dtype, n) : 1.0;
+    s += g * dy[n] * x[n];
+  }
+  for (int32_t n = 0; n < d; ++n) {
+    const double g = gamma ? load_value(gamma, dtype, n) : 1.0;
+    dx[n] = g * dy[n] / r - x[n] * s / (d * r * r * r);
+    if (dgamma) dgamma[n] += dy[n] * x[n] / r;
+  }
+}
+
+/*
+ * Backward of the conv block: Delta = U + SiLU(C), C_t = sum_i w_i (.) N_{t-i*dil},
+ * N = RMSNorm(U).  d_delta [B,T,nb,d] in; d_u [B,T,nb,d] out; d_w [kernel, d]
+ * and d_gamma_u [d] (nullable) accumulated.  The conv state is an input with
+ * no gradient.  SiLU'(c) = s (1 + c (1 - s)), s = sigmoid(c).
+ */
+void orc_conv_block_backward(const double* u, int32_t B, int32_t T, int32_t nb, int32_t d,
+                             const void* w, int32_t w_dtype, int32_t kernel, int32_t dil,
+                             const void* gamma_u, double eps, const double* state,
+                             const double* d_delta, double* d_u, double* d_w, double* d_gamma_u) {
+  const int64_t row = (int64_t)nb * d;
+  const int64_t n_el = (int64_t)B * T * row;
+  const int32_t span = (kernel - 1) * dil;
+  double* nrm = (double*)malloc(sizeof(double) * (size_t)n_el);
+  double* dc = (double*)malloc(sizeof(double) * (size_t)n_el);
+  double* dn = (double*)malloc(sizeof(double) * (size_t)n_el);
+  if (!nrm || !dc || !dn) { free(nrm); free(dc); free(dn); return; }
+  for (int64_t tb = 0; tb < (int64_t)B * T * nb; ++tb) {
+    const double* ut = u + tb * d;
+    double ss = 0.0;
+    for (int32_t n = 0; n < d; ++n) ss += ut[n] * ut[n];
+    const double inv = 1.0 / sqrt(ss / d + eps);
+    for (int32_t n = 0; n < d; ++n) {
+      const double g = gamma_u ? load_value(gamma_u, w_dtype, n) : 1.0;
+      nrm[tb * d + n] = g * ut[n] * inv;
+    }
+  }
+  /* N at position p of sequence b (state rows before 0, zeros past them) */
+#define NVAL(b, p, br, n)                                                              \
+  ((p) >= 0 ? nrm[((int64_t)(b) * T + (p)) * row + (int64_t)(br) * d + (n)]            \
+   : (state != NULL && span + (p) >= 0)                                                  \
+       ? state[((int64_t)(b) * span + span + (p)) * row + (int64_t)(br) * d + (n)]       \
+       : 0.0)
+  /* dC, the residual term of d_u, and d_w */
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t t = 0; t < T; ++t)
+      for (int32_t br = 0; br < nb; ++br) {
+        const int64_t off = ((int64_t)b * T + t) * row + (int64_t)br * d;
+        for (int32_t n = 0; n < d; ++n) {
+          double c = 0.0;
+          for (int32_t i = 0; i < kernel; ++i)
+            c += load_value(w, w_dtype, (int64_t)i * d + n) * NVAL(b, (int64_t)t - (int64_t)i * dil, br, n);
+          const double s = 1.0 / (1.0 + exp(-c));
+          dc[off + n] = d_delta[off + n] * s * (1.0 + c * (1.0 - s));
+          d_u[off + n] = d_delta[off + n];
+          for (int32_t i = 0; i < kernel; ++i)
+            d_w[(int64_t)i * d + n] += dc[off + n] * NVAL(b, (int64_t)t - (int64_t)i * dil, br, n);
+        }
+      }
+#undef NVAL
+  /* dN_p = sum_i w_i (.) dC_{p + i*dil} inside the sequence */
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t p = 0; p < T; ++p)
+      for (int32_t br = 0; br < nb; ++br)
+        for (int32_t n = 0; n < d; ++n) {
+          double acc = 0.0;
+          for (int32_t i = 0; i < kernel; ++i) {
+            const int64_t t = (int64_t)p + (int64_t)i * dil;
+            if (t < T) acc += load_value(w, w_dtype, (int64_t)i * d + n) *
+                              dc[((int64_t)b * T + t) * row + (int64_t)br * d + n];
+          }
+          dn[((int64_t)b * T + p) * row + (int64_t)br * d + n] = acc;
+        }
+  /* through N = RMSNorm(U) */
+  double* dx = (double*)malloc(sizeof(double) * (size_t)d);
+  if (dx) {
+    for (int64_t tb = 0; tb < (int64_t)B * T * nb; ++tb) {
+      rms_backward_row(u + tb * d, dn + tb * d, gamma_u, w_dtype, d, eps, dx, d_gamma_u);
+      for (int32_t n = 0; n < d; ++n) d_u[tb * d + n] += dx[n];
+    }
+    free(dx);
+  }
+  free(nrm);
+  free(dc);
+  free(dn);
+}
+
+/* Backward of U = g V: d_gate [n, nb] = sum_n dU V; d_v [n, d] = sum_b g dU (overwritten). */
+void orc_gated_value_backward(const double* gate, const double* v, const double* d_u,
+                              int64_t n_tok, int32_t nb, int32_t d, double* d_gate, double* d_v) {
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t n = 0; n < d; ++n) d_v[t * d + n] = 0.0;
+    for (int32_t b = 0; b < nb; ++b) {
+      const double* du = d_u + (t * nb + b) * (int64_t)d;
+      double acc = 0.0;
+      for (int32_t n = 0; n < d; ++n) {
+        acc += du[n] * v[t * d + n];
+        d_v[t * d + n] += gate[t * nb + b] * du[n];
+      }
+      d_gate[t * nb + b] = acc;
+    }
+  }
+}
+
+/*
+ * Backward of the gate g = sigmoid(q . k^ / sqrt(d)), q = RMSNorm_gq(h),
+ * k^ = RMSNorm_gk(K).  d_gate [n, nb] in; d_k [n, nb, d] out; d_hidden
+ * (storage layout of hidden, as doubles; branches sharing a query row add
+ * into it), d_gamma_q, d_gamma_k (nullable) accumulated.
+ */
+void orc_gate_backward(const void* hidden, int32_t dtype, int64_t tok_stride, int64_t branch_stride,
+                       const double* k, int64_t n_tok, int32_t nb, int32_t d, const void* gamma_q,
+                       const void* gamma_k, double eps, const double* d_gate, double* d_k,
+                       double* d_hidden, double* d_gamma_q, double* d_gamma_k) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)d);
+  double* q = (double*)malloc(sizeof(double) * (size_t)d);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dq = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dkn = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dx = (double*)malloc(sizeof(double) * (size_t)d);
+  if (h && q && kn && dq && dkn && dx) {
+    const double sd = sqrt((double)d);
+    for (int64_t t = 0; t < n_tok; ++t)
+      for (int32_t b = 0; b < nb; ++b) {
+        const int64_t hbase = t * tok_stride + (int64_t)b * branch_stride;
+        const double* kr = k + (t * nb + b) * (int64_t)d;
+        double hh = 0.0, kk = 0.0;
+        for (int32_t n = 0; n < d; ++n) {
+          h[n] = load_value(hidden, dtype, hbase + n);
+          hh += h[n] * h[n];
+          kk += kr[n] * kr[n];
+        }
+        const double inv_h = 1.0 / sqrt(hh / d + eps), inv_k = 1.0 / sqrt(kk / d + eps);
+        double dot = 0.0;
+        for (int32_t n = 0; n < d; ++n) {
+          q[n] = (gamma_q ? load_value(gamma_q, dtype, n) : 1.0) * h[n] * inv_h;
+          kn[n] = (gamma_k ? load_value(gamma_k, dtype, n) : 1.0) * kr[n] * inv_k;
+          dot += q[n] * kn[n];
+        }
+        const double g = 1.0 / (1.0 + exp(-dot / sd));
+        const double dz = d_gate[t * nb + b] * g * (1.0 - g);
+        for (int32_t n = 0; n < d; ++n) {
+          dq[n] = dz * kn[n] / sd;
+          dkn[n] = dz * q[n] / sd;
+        }
+        rms_backward_row(kr, dkn, gamma_k, dtype, d, eps, d_k + (t * nb + b) * (int64_t)d,
+                         d_gamma_k);
+        rms_backward_row(h, dq, gamma_q, dtype, d, eps, dx, d_gamma_q);
+        for (int32_t n = 0; n < d; ++n) d_hidden[hbase + n] += dx[n];
+      }
+  }
+  free(h); free(q); free(kn); free(dq); free(dkn); free(dx);
+}
+
+/* Backward of out = E W (W [mem, d]): d_e [n, mem] += d_out W^T; d_w [mem, d] += E^T d_out. */
+void orc_project_backward(const double* e, int64_t n_tok, int32_t mem, const void* w, int32_t dtype,
+                          int32_t d, const double* d_out, double* d_e, double* d_w) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tok; ++t)
+    for (int32_t m = 0; m < mem; ++m) {
+      double acc = 0.0;
+      for (int32_t n = 0; n < d; ++n) acc += d_out[t * d + n] * load_value(w, dtype, (int64_t)m * d + n);
+      d_e[t * mem + m] += acc;
+    }
+#pragma omp parallel for schedule(static)
+  for (int32_t m = 0; m < mem; ++m)
+    for (int32_t n = 0; n < d; ++n) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < n_tok; ++t) acc += e[t * mem + m] * d_out[t * d + n];
+      d_w[(int64_t)m * d + n] += acc;
+    }
+}
+
+/* Backward of the gather: d_tables[j][row_idx[t][j]] += the j-th row_dim
+ * slice of d_e[t] (accumulated; a row hit by several tokens sums them). */
+void orc_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables, const double* d_e,
+                     int32_t row_dim, double* const* d_tables) {
+  const int64_t mem = (int64_t)n_tables * row_dim;
+  for (int64_t t = 0; t < n_tok; ++t)
+    for (int32_t j = 0; j < n_tables; ++j) {
+      const int64_t r = row_idx[t * n_tables + j];
+      for (int32_t c = 0; c < row_dim; ++c)
+        d_tables[j][r * row_dim + c] += d_e[t * mem + (int64_t)j * row_dim + c];
+    }
+}

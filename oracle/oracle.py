@@ -65,6 +65,13 @@ def _load(path: str):
     L.orc_gated_value.argtypes = [_p, _p, _i64, _i32, _i32, _p]
     L.orc_conv_block.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _i32, _p,
                                  _f64, _p, _p]
+    L.orc_conv_block_backward.argtypes = [_p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _i32, _p,
+                                          _f64, _p, _p, _p, _p, _p]
+    L.orc_gated_value_backward.argtypes = [_p, _p, _p, _i64, _i32, _i32, _p, _p]
+    L.orc_gate_backward.argtypes = [_p, _i32, _i64, _i64, _p, _i64, _i32, _i32, _p, _p, _f64, _p,
+                                    _p, _p, _p, _p]
+    L.orc_project_backward.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p, _p, _p]
+    L.orc_scatter_add.argtypes = [_p, _i64, _i32, _p, _i32, _p]
     return L
 
 
@@ -238,3 +245,125 @@ def forward(raw, hist_raw, lut, vocab: int, vocab_c: int, orders, heads: int, ro
                        conv_state)
     return {"comp": comp, "bad": bad, "row_idx": r, "e": e, "k": k, "v": v, "gate": g,
             "u": u, "delta": delta.reshape(B * T, nb, d)}
+
+
+# ---------------------------------------------------------------------------
+# the layer's backward pass (gradients of L = sum(d_out * out))
+# ---------------------------------------------------------------------------
+
+def conv_block_backward(u, conv_w, dtype: str, dilation: int, d_delta, gamma_u=None,
+                        eps: float = 1e-6, state=None):
+    """u, d_delta float64[B, T, nb, d] -> (d_u, d_conv_w [kernel, d], d_gamma_u [d])."""
+    u, dd = _c(u, np.float64), _c(d_delta, np.float64)
+    B, T, nb, d = u.shape
+    w = _storage(conv_w, dtype)
+    kernel = w.shape[0]
+    st = _c(state, np.float64)
+    d_u = np.empty_like(u)
+    d_w = np.zeros((kernel, d), dtype=np.float64)
+    d_g = np.zeros(d, dtype=np.float64)
+    lib().orc_conv_block_backward(_ptr(u), B, T, nb, d, _ptr(w), _DT[dtype], kernel, dilation,
+                                  _ptr(_storage(gamma_u, dtype) if gamma_u is not None else None),
+                                  eps, _ptr(st), _ptr(dd), _ptr(d_u), _ptr(d_w), _ptr(d_g))
+    return d_u, d_w, d_g
+
+
+def gated_value_backward(g, v, d_u):
+    """g [n, nb], v [n, d], d_u [n, nb, d] -> (d_gate [n, nb], d_v [n, d])."""
+    g, v, d_u = _c(g, np.float64), _c(v, np.float64), _c(d_u, np.float64)
+    n, nb = g.shape
+    d = v.shape[1]
+    d_g = np.empty((n, nb), dtype=np.float64)
+    d_v = np.empty((n, d), dtype=np.float64)
+    lib().orc_gated_value_backward(_ptr(g), _ptr(v), _ptr(d_u), n, nb, d, _ptr(d_g), _ptr(d_v))
+    return d_g, d_v
+
+
+def gate_backward(hidden, dtype: str, k, d_gate, gamma_q=None, gamma_k=None, eps: float = 1e-6):
+    """hidden [n, nbh, d] storage; k float64[n, nb, d]; d_gate [n, nb] ->
+    (d_k [n, nb, d], d_hidden [n, nbh, d], d_gamma_q [d], d_gamma_k [d])."""
+    hidden = _storage(hidden, dtype)
+    k, dg = _c(k, np.float64), _c(d_gate, np.float64)
+    n, nb, d = k.shape
+    nbh = hidden.shape[1]
+    bstride = 0 if nbh == 1 else d
+    d_k = np.empty_like(k)
+    d_h = np.zeros((n, nbh, d), dtype=np.float64)
+    d_gq = np.zeros(d, dtype=np.float64)
+    d_gk = np.zeros(d, dtype=np.float64)
+    lib().orc_gate_backward(_ptr(hidden), _DT[dtype], nbh * d, bstride, _ptr(k), n, nb, d,
+                            _ptr(_storage(gamma_q, dtype) if gamma_q is not None else None),
+                            _ptr(_storage(gamma_k, dtype) if gamma_k is not None else None),
+                            eps, _ptr(dg), _ptr(d_k), _ptr(d_h), _ptr(d_gq), _ptr(d_gk))
+    return d_k, d_h, d_gq, d_gk
+
+
+def project_backward(e, w, dtype: str, d_out, d_e):
+    """out = e @ w (w [mem, d] storage): adds d_out @ w.T into d_e [n, mem] and
+    returns d_w = e.T @ d_out [mem, d]."""
+    e, d_out = _c(e, np.float64), _c(d_out, np.float64)
+    w = _storage(w, dtype)
+    mem, d = w.shape
+    assert d_e.flags.c_contiguous and d_e.dtype == np.float64
+    d_w = np.zeros((mem, d), dtype=np.float64)
+    lib().orc_project_backward(_ptr(e), e.shape[0], mem, _ptr(w), _DT[dtype], d, _ptr(d_out),
+                               _ptr(d_e), _ptr(d_w))
+    return d_w
+
+
+def scatter_add(row_idx, d_e, row_dim: int):
+    """Table gradients of the gather: for each table j, (rows, grads): the
+    distinct rows its tokens hit and the summed d_e slices [len(rows), row_dim]."""
+    row_idx = _c(row_idx, np.int32)
+    d_e = _c(d_e, np.float64)
+    n, nt = row_idx.shape
+    rows, compact, remap = [], [], np.empty_like(row_idx)
+    for j in range(nt):
+        uniq, inv = np.unique(row_idx[:, j], return_inverse=True)
+        rows.append(uniq)
+        compact.append(np.zeros((len(uniq), row_dim), dtype=np.float64))
+        remap[:, j] = inv.reshape(-1)
+    ptrs = (ctypes.c_void_p * nt)(*[c.ctypes.data for c in compact])
+    lib().orc_scatter_add(_ptr(remap), n, nt, _ptr(d_e), row_dim, ptrs)
+    return list(zip(rows, compact))
+
+
+def backward(raw, hist_raw, lut, vocab: int, vocab_c: int, orders, heads: int, rows, mult,
+             tables_or_provider, hidden, wk, wv, conv_w, dtype: str, d_out, *, gamma_q=None,
+             gamma_k=None, gamma_u=None, eps: float = 1e-6, conv_state=None, pad_id: int = 0,
+             table_dtype: Optional[str] = None, table_scales=None, add_residual: bool = False):
+    """Gradients of L = sum(d_out * out) for the forward above (out = Delta, or
+    hidden + Delta with ``add_residual``).  d_out: [B*T, nb, d].  Returns the
+    forward's dict plus d_tables (per table: rows hit, summed gradients),
+    d_wk [nb, mem, d], d_wv [mem, d], d_conv_w [kernel, d], d_hidden [B*T, nbh, d],
+    d_gamma_q, d_gamma_k, d_gamma_u [d] (float64)."""
+    f = forward(raw, hist_raw, lut, vocab, vocab_c, orders, heads, rows, mult, tables_or_provider,
+                hidden, wk, wv, conv_w, dtype, gamma_q=gamma_q, gamma_k=gamma_k, gamma_u=gamma_u,
+                eps=eps, conv_state=conv_state, pad_id=pad_id, table_dtype=table_dtype,
+                table_scales=table_scales)
+    raw = _c(raw, np.int32)
+    B, T = raw.shape
+    wk = np.asarray(wk)
+    nb = wk.shape[0]
+    d = wk.shape[2]
+    d_out = _c(d_out, np.float64).reshape(B * T, nb, d)
+    d_u, d_conv_w, d_gamma_u = conv_block_backward(f["u"].reshape(B, T, nb, d), conv_w, dtype,
+                                                   max(orders), d_out.reshape(B, T, nb, d),
+                                                   gamma_u, eps, conv_state)
+    d_gate, d_v = gated_value_backward(f["gate"], f["v"], d_u.reshape(B * T, nb, d))
+    d_k, d_hidden, d_gamma_q, d_gamma_k = gate_backward(hidden, dtype, f["k"], d_gate, gamma_q,
+                                                        gamma_k, eps)
+    if add_residual:  # out[t, b] = hidden row of branch b (or the shared row) + Delta
+        if d_hidden.shape[1] == 1:
+            d_hidden[:, 0] += d_out.sum(axis=1)
+        else:
+            d_hidden += d_out
+    e = f["e"]
+    d_e = np.zeros_like(e)
+    d_wk = np.stack([project_backward(e, wk[b], dtype, d_k[:, b], d_e) for b in range(nb)])
+    d_wv = project_backward(e, wv, dtype, d_v, d_e)
+    d_tables = scatter_add(f["row_idx"], d_e, e.shape[1] // len(rows))
+    f.update(d_tables=d_tables, d_wk=d_wk, d_wv=d_wv, d_conv_w=d_conv_w, d_hidden=d_hidden,
+             d_gamma_q=d_gamma_q, d_gamma_k=d_gamma_k, d_gamma_u=d_gamma_u, d_e=d_e,
+             d_k=d_k, d_v=d_v, d_gate=d_gate, d_u=d_u)
+    return f

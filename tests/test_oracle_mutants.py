@@ -8,6 +8,7 @@ import tempfile
 
 import pytest
 
+import test_oracle_backward as BW
 import test_oracle_pins as P
 from oracle import oracle as O
 
@@ -47,6 +48,17 @@ MUTANTS = [
     ("fp8 table scale dropped", "* (double)scales[j]);", "* 1.0);"),
     ("fp8 E rounded to bf16 by truncation", "if (low > 0x8000u || (low == 0x8000u && (high & 1u))) high += 1;",
      "(void)low;"),
+    ("SiLU derivative drops c(1-s)", "dc[off + n] = d_delta[off + n] * s * (1.0 + c * (1.0 - s));",
+     "dc[off + n] = d_delta[off + n] * s;"),
+    ("conv backward taps run backwards", "const int64_t t = (int64_t)p + (int64_t)i * dil;",
+     "const int64_t t = (int64_t)p - (int64_t)i * dil;"),
+    ("RMSNorm backward drops the norm term", "dx[n] = g * dy[n] / r - x[n] * s / (d * r * r * r);",
+     "dx[n] = g * dy[n] / r;"),
+    ("sigmoid derivative is g", "const double dz = d_gate[t * nb + b] * g * (1.0 - g);",
+     "const double dz = d_gate[t * nb + b] * g;"),
+    ("projection backward uses W transposed",
+     "acc += d_out[t * d + n] * load_value(w, dtype, (int64_t)m * d + n);",
+     "acc += d_out[t * d + n] * load_value(w, dtype, (int64_t)n * mem + m);"),
 ]
 
 # the pins run against each mutant (test function, keyword arguments)
@@ -73,6 +85,9 @@ PINS = [
     (P.test_conv_causal_and_state_streaming, {}),
     (P.test_fp8_decode_definition_and_library, {}),
     (P.test_gather_fp8_scaled_bf16, {}),
+    (BW.test_backward_matches_finite_differences, dict(nb=2, nbh=2, with_state=True, residual=False)),
+    (BW.test_backward_matches_finite_differences, dict(nb=1, nbh=1, with_state=False, residual=True)),
+    (BW.test_scatter_is_the_gathers_adjoint, {}),
 ]
 
 
