@@ -6,7 +6,8 @@ ctypes binding.  Importing this package loads the library and fails loudly
 when it has not been built.
 """
 from . import ngram  # noqa: F401
-from .ngram import (ADD_RESIDUAL, BF16, F32, W_D_MEM, W_MEM_D, NgramConfig, NgramError, make_config,  # noqa: F401
+from .ngram import (ADD_RESIDUAL, BF16, F32, FP8_E4M3, W_D_MEM, W_MEM_D, NgramConfig,  # noqa: F401
+                    NgramError, make_config, ngram_backward, ngram_backward_workspace_size,
                     ngram_causal_conv, ngram_compress_ids, ngram_config_validate, ngram_forward,
                     ngram_forward_workspace_size, ngram_gate, ngram_gate_workspace_size,
                     ngram_gather, ngram_hash)

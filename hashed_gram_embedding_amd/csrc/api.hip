@@ -233,6 +233,58 @@ Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward, int32_t T 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 
+// Backward workspace: row ids, E, K / V (fp32), per-row stats, dC, dK / dV
+// (bf16), the weights transposed, dE (fp32), and dK / dV and E transposed
+// over tokens padded to a multiple of 64.
+struct BwdLayout {
+  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, total;
+  int64_t n_pad;
+};
+
+BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
+  BwdLayout L;
+  const int64_t nb = c->n_branches, d = c->hidden_dim, mem = c->mem_dim, N = (nb + 1) * d;
+  L.n_pad = (n + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.row_idx = take((size_t)n * c->n_tables * 4);
+  L.e = take((size_t)n * mem * 2);
+  L.kv = take((size_t)n * N * 4);
+  L.stats = take((size_t)n * nb * 16);
+  L.dc = take((size_t)n * nb * d * 4);
+  L.dkv = take((size_t)n * N * 2);
+  L.wt = take((size_t)mem * N * 2);
+  L.de = take((size_t)n * mem * 4);
+  L.dkvt = take((size_t)N * L.n_pad * 2);
+  L.et = take((size_t)mem * L.n_pad * 2);
+  L.total = off;
+  return L;
+}
+
+// C[M, (nb+1)*dd] = A[M, K] B^T in fp32 (B: nb key blocks of dd rows from wk,
+// then dd rows from wv, all [., K] bf16) on the MFMA projection kernel.
+hipError_t raw_gemm(const bf16_bits* A, int64_t M, int32_t K, const bf16_bits* wk,
+                    const bf16_bits* wv, int32_t nb, int32_t dd, float* C, int64_t ldc,
+                    hipStream_t s) {
+  AsyncProjArgs a;
+  memset(&a, 0, sizeof a);
+  a.e = A;
+  a.wk = wk;
+  a.wv = wv;
+  a.epi.M = M;
+  a.epi.d = dd;
+  a.epi.nb = nb;
+  a.K = K;
+  a.group_m = 4;
+  a.raw_out = C;
+  a.raw_ld = ldc;
+  return launch_projection_raw(M >= 8192 ? 7 : M >= 1024 ? 8 : 2, a, s);
+}
+
 // Benchmark instrumentation (ngram_set_timing_events): stage(i) closes the
 // open stage and opens stage i; the kernels launched while it is open stamp
 // the stage's event pair (launch() in internal.h).
@@ -612,6 +664,140 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   ca.tile = conv_tile_for(T);
   ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
   return hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+size_t ngram_backward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T) {
+  if (validate(cfg) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
+  return bwd_layout(cfg, (int64_t)B * T).total;
+}
+
+int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                   const int32_t* history, const int32_t* lut, const void* const* tables,
+                   const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                   const void* w_v, const void* conv_w, const void* gamma_q,
+                   const void* gamma_k, const void* gamma_u, const float* conv_state,
+                   int32_t flags, const void* d_out, float* const* d_tables, float* d_w_k,
+                   float* d_w_v, float* d_conv_w, float* d_hidden, float* d_gammas,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(cfg);
+  if (st) return st;
+  if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM) return NGRAM_EDTYPE;
+  if (cfg->hidden_dim % 64 != 0 || cfg->hidden_dim > 4096) return NGRAM_ESHAPE;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if (flags & ~NGRAM_ADD_RESIDUAL) return NGRAM_EINVAL;
+  int64_t h_tok = 0;
+  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
+  if (st) return st;
+  const int64_t n = (int64_t)B * T;
+  if (n == 0) return NGRAM_OK;
+  if (!raw_ids || !lut || !hidden || !w_k || !w_v || !conv_w || !d_out || !d_tables || !d_w_k ||
+      !d_w_v || !d_conv_w)
+    return NGRAM_EINVAL;
+  TablePtrs tp;
+  st = check_tables(cfg, tables, &tp);
+  if (st) return st;
+  GradTablePtrs gp;
+  memset(&gp, 0, sizeof gp);
+  for (int j = 0; j < cfg->n_tables; ++j) {
+    if (d_tables[j] == nullptr) return NGRAM_EINVAL;
+    if (!aligned16(d_tables[j])) return NGRAM_EALIGN;
+    gp.p[j] = d_tables[j];
+  }
+  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut)) return NGRAM_EALIGN;
+  for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, d_out,
+                        (const void*)conv_state, (const void*)d_w_k, (const void*)d_w_v,
+                        (const void*)d_conv_w, (const void*)d_hidden, (const void*)d_gammas})
+    if (!aligned16(p)) return NGRAM_EALIGN;
+  const BwdLayout L = bwd_layout(cfg, n);
+  // the dW products index their [., n_pad] operands with 32-bit offsets
+  if ((int64_t)(cfg->n_branches + 1) * cfg->hidden_dim * L.n_pad >= (int64_t(1) << 31) ||
+      (int64_t)cfg->mem_dim * L.n_pad >= (int64_t(1) << 31))
+    return NGRAM_ESHAPE;
+  if (!workspace || workspace_bytes < L.total) return NGRAM_EWORKSPACE;
+  if (!aligned16(workspace)) return NGRAM_EALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int nb = cfg->n_branches, d = cfg->hidden_dim, mem = cfg->mem_dim;
+  const int32_t N = (nb + 1) * d;
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
+  bf16_bits* e = reinterpret_cast<bf16_bits*>(ws + L.e);
+  float* kv = reinterpret_cast<float*>(ws + L.kv);
+  bf16_bits* dkv = reinterpret_cast<bf16_bits*>(ws + L.dkv);
+  bf16_bits* wt = reinterpret_cast<bf16_bits*>(ws + L.wt);
+  float* de = reinterpret_cast<float*>(ws + L.de);
+  bf16_bits* dkvt = reinterpret_cast<bf16_bits*>(ws + L.dkvt);
+  bf16_bits* et = reinterpret_cast<bf16_bits*>(ws + L.et);
+  const bf16_bits* wk = static_cast<const bf16_bits*>(w_k);
+  const bf16_bits* wv = static_cast<const bf16_bits*>(w_v);
+
+  // recompute: row ids, E, and K / V in fp32
+  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, nullptr, s));
+  if (st) return st;
+  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n, cfg->n_tables, cfg->row_dim, tp, e, s));
+  if (st) return st;
+  st = hip_status(raw_gemm(e, n, mem, wk, wv, nb, d, kv, N, s));
+  if (st) return st;
+  // the per-row backward: gates, conv, RMSNorms -> dK, dV (bf16), d_hidden, d_conv_w, d_gammas
+  st = hip_status(launch_zero_f32(d_conv_w, 4 * (int64_t)d, s));
+  if (st) return st;
+  if (d_gammas) {
+    st = hip_status(launch_zero_f32(d_gammas, 3 * (int64_t)d, s));
+    if (st) return st;
+  }
+  BwdArgs ba;
+  memset(&ba, 0, sizeof ba);
+  ba.n = n;
+  ba.T = T;
+  ba.nb = nb;
+  ba.d = d;
+  ba.dil = cfg->conv_dilation;
+  ba.eps = cfg->rms_eps;
+  ba.hidden = static_cast<const bf16_bits*>(hidden);
+  ba.h_tok = h_tok;
+  ba.h_br = hidden_branch_stride;
+  ba.kv = kv;
+  ba.kv_ld = N;
+  ba.stats = reinterpret_cast<float*>(ws + L.stats);
+  ba.dc = reinterpret_cast<float*>(ws + L.dc);
+  ba.d_out = static_cast<const bf16_bits*>(d_out);
+  ba.conv_w = static_cast<const bf16_bits*>(conv_w);
+  ba.gamma_q = static_cast<const bf16_bits*>(gamma_q);
+  ba.gamma_k = static_cast<const bf16_bits*>(gamma_k);
+  ba.gamma_u = static_cast<const bf16_bits*>(gamma_u);
+  ba.state = conv_state;
+  ba.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
+  ba.dkv = dkv;
+  ba.dkv_ld = N;
+  ba.d_hidden = d_hidden;
+  ba.d_conv_w = d_conv_w;
+  ba.d_gammas = d_gammas;
+  st = hip_status(launch_bwd_rows(ba, s));
+  if (st) return st;
+  // dE = [dK dV] [W_K; W_V]: the weights transposed to [mem, N] feed the product
+  st = hip_status(launch_transpose_bf16(wk, (int64_t)nb * d, mem, mem, wt, (int64_t)nb * d, N, s));
+  if (st) return st;
+  st = hip_status(launch_transpose_bf16(wv, d, mem, mem, wt + (int64_t)nb * d, d, N, s));
+  if (st) return st;
+  st = hip_status(raw_gemm(dkv, n, N, nullptr, wt, 0, mem, de, mem, s));
+  if (st) return st;
+  // dW = [dK dV]^T E: both operands transposed to [., n_pad], tokens padded with zeros
+  st = hip_status(launch_transpose_bf16(dkv, n, N, N, dkvt, L.n_pad, L.n_pad, s));
+  if (st) return st;
+  st = hip_status(launch_transpose_bf16(e, n, mem, mem, et, L.n_pad, L.n_pad, s));
+  if (st) return st;
+  st = hip_status(raw_gemm(dkvt, (int64_t)nb * d, (int32_t)L.n_pad, nullptr, et, 0, mem, d_w_k, mem, s));
+  if (st) return st;
+  st = hip_status(raw_gemm(dkvt + (int64_t)nb * d * L.n_pad, d, (int32_t)L.n_pad, nullptr, et, 0,
+                           mem, d_w_v, mem, s));
+  if (st) return st;
+  // the gather's adjoint
+  return hip_status(launch_scatter_add(row_idx, n, cfg->n_tables, cfg->row_dim, de, gp, s));
 }
 
 }  // extern "C"

@@ -1,0 +1,400 @@
+// Backward pass of the layer: the gradients a training step needs, for the
+// tables, W_K, W_V, the conv taps, the query rows and the RMSNorm gains.
+//
+// Each kernel is the chain rule of one forward step ("Qwen3.8-Flash-Next
+// 深度研究" §2.3: E_t -> K_t, V_t; g_t = Gate(Norm(Q_t), Norm(K_t));
+// U_t = g_t V_t; Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))); Engram's third
+// and fourth components in "Qwen 4用上DeepSeek的Engram").  The table gradient
+// is the gather's adjoint: a scatter-add of dE into the rows the tokens
+// named.  The dense products (K/V recompute, dE = dKV W, dW = dKV^T E) run on
+// the MFMA projection kernel with a raw fp32 epilogue; the kernels here do the
+// per-row work between them and the layout transposes that feed them.
+//
+// RMSNorm y = gamma (.) x / r, r = sqrt(mean(x^2) + eps) has the backward
+// dx = gamma (.) dy / r - x * sum(gamma dy x) / (d r^3), dgamma += dy x / r;
+// SiLU'(c) = s (1 + c (1 - s)) with s = sigmoid(c).
+#include "internal.h"
+
+namespace ngram {
+namespace {
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ float4 mk4(float x) { return make_float4(x, x, x, x); }
+__device__ __forceinline__ float4 add(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 mul(float4 a, float4 b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ float4 fma4(float4 a, float4 b, float4 c) {
+  return make_float4(fmaf(a.x, b.x, c.x), fmaf(a.y, b.y, c.y), fmaf(a.z, b.z, c.z),
+                     fmaf(a.w, b.w, c.w));
+}
+__device__ __forceinline__ float dot(float4 a, float4 b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+__device__ __forceinline__ float4 gain4(const bf16_bits* g, int c) {
+  return g ? Elem<bf16_bits>::load4(g, c) : mk4(1.0f);
+}
+__device__ __forceinline__ float silu_grad(float c) {
+  const float s = 1.0f / (1.0f + expf(-c));
+  return s * (1.0f + c * (1.0f - s));
+}
+
+// Sum of NV values over the 256-thread block; every thread gets the totals.
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float (*red)[NV]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v[q] += __shfl_xor(v[q], off);
+  }
+  __syncthreads();  // red may still be read from the previous call
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < NV; ++q) red[wave][q] = v[q];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NV; ++q) v[q] = red[0][q] + red[1][q] + red[2][q] + red[3][q];
+}
+
+// Columns of a thread: the 4-column groups c = 4 * (x + 256 * i), i < ITEMS.
+template <int ITEMS>
+struct Cols {
+  int c[ITEMS];
+  bool ok[ITEMS];
+  __device__ Cols(int d) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int v = 4 * ((int)threadIdx.x + 256 * i);
+      ok[i] = v < d;
+      c[i] = ok[i] ? v : d - 4;
+    }
+  }
+};
+
+// 1. Per token and branch: g = sigmoid(q^ . k^ / sqrt(d)) and the three
+// reciprocal norms 1/rho_h, 1/rho_k, 1/r (r: the norm of U = g V), from the
+// query rows and the recomputed fp32 K/V.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
+  __shared__ float red[4][4];
+  const int nb = a.nb, d = a.d;
+  const Cols<ITEMS> cl(d);
+  for (int64_t t = blockIdx.x; t < a.n; t += gridDim.x) {
+    const float* kv = a.kv + t * a.kv_ld;
+    float vv[1] = {0.0f};
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (cl.ok[i]) {
+        const float4 v = ld4(kv + nb * d + cl.c[i]);
+        vv[0] += dot(v, v);
+      }
+    block_sum<1>(vv, reinterpret_cast<float(*)[1]>(red));
+    for (int br = 0; br < nb; ++br) {
+      float s[3] = {0.0f, 0.0f, 0.0f};  // sum h^2, sum K^2, sum (gq h)(gk K)
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i)
+        if (cl.ok[i]) {
+          const float4 h = Elem<bf16_bits>::load4(a.hidden, t * a.h_tok + br * a.h_br + cl.c[i]);
+          const float4 k = ld4(kv + br * d + cl.c[i]);
+          s[0] += dot(h, h);
+          s[1] += dot(k, k);
+          s[2] += dot(mul(gain4(a.gamma_q, cl.c[i]), h), mul(gain4(a.gamma_k, cl.c[i]), k));
+        }
+      block_sum<3>(s, reinterpret_cast<float(*)[3]>(red));
+      if (threadIdx.x == 0) {
+        const float ih = 1.0f / sqrtf(s[0] / d + a.eps), ik = 1.0f / sqrtf(s[1] / d + a.eps);
+        const float g = 1.0f / (1.0f + expf(-s[2] * ih * ik / sqrtf((float)d)));
+        const float ir = 1.0f / sqrtf(g * g * vv[0] / d + a.eps);
+        st4(a.stats + (t * nb + br) * 4, make_float4(g, ih, ik, ir));
+      }
+    }
+  }
+}
+
+// N of sequence position p (relative to token t at position pos) for branch
+// br, columns c..c+3: gamma_u g V / r inside the sequence, the caller's state
+// rows before it, zeros before those.
+__device__ __forceinline__ float4 n_value(const BwdArgs& a, int64_t t, int pos, int p, int br,
+                                          int c, float4 gu) {
+  if (p >= 0) {
+    const int64_t s = t - (pos - p);
+    const float4 st = ld4(a.stats + (s * a.nb + br) * 4);
+    const float4 v = ld4(a.kv + s * a.kv_ld + a.nb * a.d + c);
+    return mul(gu, mul(v, mk4(st.x * st.w)));
+  }
+  const int span = 3 * a.dil;
+  if (a.state == nullptr || span + p < 0) return mk4(0.0f);
+  const int64_t b = t / a.T;
+  return ld4(a.state + ((b * span + span + p) * a.nb + br) * (int64_t)a.d + c);
+}
+
+// 2. dC = dOut (.) SiLU'(C) per token and branch (C = sum_i w_i (.) N_{t-i*dil}),
+// and the taps' gradient d_w[i] += dC (.) N_{t-i*dil}, summed in registers over
+// the rows of this block and added once per block.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
+  const int nb = a.nb, d = a.d, dil = a.dil;
+  const Cols<ITEMS> cl(d);
+  float4 dw[4][ITEMS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) dw[i][j] = mk4(0.0f);
+  for (int64_t row = blockIdx.x; row < a.n * nb; row += gridDim.x) {
+    const int64_t t = row / nb;
+    const int br = (int)(row - t * nb);
+    const int pos = (int)(t % a.T);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      if (!cl.ok[j]) continue;
+      const int c = cl.c[j];
+      const float4 gu = gain4(a.gamma_u, c);
+      float4 nv[4], cc = mk4(0.0f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nv[i] = n_value(a, t, pos, pos - i * dil, br, c, gu);
+        cc = fma4(Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c), nv[i], cc);
+      }
+      const float4 go = Elem<bf16_bits>::load4(a.d_out, row * d + c);
+      const float4 dc = make_float4(go.x * silu_grad(cc.x), go.y * silu_grad(cc.y),
+                                    go.z * silu_grad(cc.z), go.w * silu_grad(cc.w));
+      st4(a.dc + row * d + c, dc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dw[i][j] = fma4(dc, nv[i], dw[i][j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (cl.ok[j])
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* p = a.d_conv_w + (int64_t)i * d + cl.c[j];
+        unsafeAtomicAdd(p + 0, dw[i][j].x);
+        unsafeAtomicAdd(p + 1, dw[i][j].y);
+        unsafeAtomicAdd(p + 2, dw[i][j].z);
+        unsafeAtomicAdd(p + 3, dw[i][j].w);
+      }
+}
+
+// 3. Per token, all branches: dN -> dU (residual + RMSNorm), dg and dV (U = g V),
+// dz -> dK and the query's gradient (both RMSNorms), the gains' gradients.
+// dK and dV are written in bf16 as the operands of the dE and dW products.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
+  __shared__ float red[4][2];
+  const int nb = a.nb, d = a.d, dil = a.dil;
+  const float fd = (float)d, sd = sqrtf(fd);
+  const Cols<ITEMS> cl(d);
+  float4 dgq[ITEMS], dgk[ITEMS], dgu[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) dgq[j] = dgk[j] = dgu[j] = mk4(0.0f);
+  for (int64_t t = blockIdx.x; t < a.n; t += gridDim.x) {
+    const int pos = (int)(t % a.T);
+    const float* kv = a.kv + t * a.kv_ld;
+    float4 v[ITEMS], dv[ITEMS], dhs[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      v[j] = ld4(kv + nb * d + cl.c[j]);
+      dv[j] = dhs[j] = mk4(0.0f);
+    }
+    for (int br = 0; br < nb; ++br) {
+      const float4 st = ld4(a.stats + (t * nb + br) * 4);  // g, 1/rho_h, 1/rho_k, 1/r
+      const float g = st.x, ih = st.y, ik = st.z, ir = st.w;
+      const int64_t row = t * nb + br;
+      // dN = sum_i w_i (.) dC_{t + i*dil} inside the sequence; U = g V
+      float4 dn[ITEMS];
+      float s1[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        dn[j] = mk4(0.0f);
+        for (int i = 0; i < 4; ++i)
+          if (pos + i * dil < a.T)
+            dn[j] = fma4(Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + cl.c[j]),
+                         ld4(a.dc + (row + (int64_t)i * dil * nb) * d + cl.c[j]), dn[j]);
+        if (cl.ok[j]) s1[0] += dot(mul(gain4(a.gamma_u, cl.c[j]), dn[j]), mul(mk4(g), v[j]));
+      }
+      block_sum<2>(s1, red);
+      // dU = dOut + gamma_u dN / r - U sum(gamma_u dN U) / (d r^3); dg = sum dU V
+      float4 du[ITEMS];
+      float s2[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const float4 u = mul(mk4(g), v[j]);
+        const float4 gu = gain4(a.gamma_u, cl.c[j]);
+        du[j] = add(Elem<bf16_bits>::load4(a.d_out, row * d + cl.c[j]),
+                    add(mul(mul(gu, dn[j]), mk4(ir)), mul(u, mk4(-s1[0] * ir * ir * ir / fd))));
+        if (cl.ok[j]) {
+          s2[0] += dot(du[j], v[j]);
+          dgu[j] = fma4(mul(dn[j], u), mk4(ir), dgu[j]);
+        }
+        dv[j] = fma4(mk4(g), du[j], dv[j]);
+      }
+      block_sum<2>(s2, red);
+      const float dz = s2[0] * g * (1.0f - g);
+      // q^ = gamma_q h / rho_h, k^ = gamma_k K / rho_k; dq^ = dz k^ / sqrt d, dk^ = dz q^ / sqrt d
+      float4 h[ITEMS], k[ITEMS], dq[ITEMS], dk[ITEMS];
+      float s3[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        h[j] = Elem<bf16_bits>::load4(a.hidden, t * a.h_tok + br * a.h_br + cl.c[j]);
+        k[j] = ld4(kv + br * d + cl.c[j]);
+        const float4 gq = gain4(a.gamma_q, cl.c[j]), gk = gain4(a.gamma_k, cl.c[j]);
+        dq[j] = mul(mk4(dz / sd), mul(gk, mul(k[j], mk4(ik))));
+        dk[j] = mul(mk4(dz / sd), mul(gq, mul(h[j], mk4(ih))));
+        if (cl.ok[j]) {
+          s3[0] += dot(mul(gk, dk[j]), k[j]);
+          s3[1] += dot(mul(gq, dq[j]), h[j]);
+        }
+      }
+      block_sum<2>(s3, red);
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const float4 gq = gain4(a.gamma_q, cl.c[j]), gk = gain4(a.gamma_k, cl.c[j]);
+        const float4 dkk = add(mul(mul(gk, dk[j]), mk4(ik)), mul(k[j], mk4(-s3[0] * ik * ik * ik / fd)));
+        float4 dh = add(mul(mul(gq, dq[j]), mk4(ih)), mul(h[j], mk4(-s3[1] * ih * ih * ih / fd)));
+        if (a.add_residual) dh = add(dh, Elem<bf16_bits>::load4(a.d_out, row * d + cl.c[j]));
+        if (cl.ok[j]) {
+          Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + br * d + cl.c[j], dkk);
+          dgk[j] = fma4(mul(dk[j], k[j]), mk4(ik), dgk[j]);
+          dgq[j] = fma4(mul(dq[j], h[j]), mk4(ih), dgq[j]);
+          if (a.d_hidden) {
+            if (a.h_br == 0)
+              dhs[j] = add(dhs[j], dh);
+            else
+              st4(a.d_hidden + t * a.h_tok + br * a.h_br + cl.c[j], dh);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (cl.ok[j]) {
+        Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + nb * d + cl.c[j], dv[j]);
+        if (a.d_hidden && a.h_br == 0) st4(a.d_hidden + t * a.h_tok + cl.c[j], dhs[j]);
+      }
+  }
+  if (a.d_gammas) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (cl.ok[j]) {
+        const float4* gsrc[3] = {&dgq[j], &dgk[j], &dgu[j]};
+        for (int q = 0; q < 3; ++q) {
+          float* p = a.d_gammas + (int64_t)q * d + cl.c[j];
+          unsafeAtomicAdd(p + 0, gsrc[q]->x);
+          unsafeAtomicAdd(p + 1, gsrc[q]->y);
+          unsafeAtomicAdd(p + 2, gsrc[q]->z);
+          unsafeAtomicAdd(p + 3, gsrc[q]->w);
+        }
+      }
+  }
+}
+
+// 4. The gather's adjoint: one wavefront per token adds the token's dE slices
+// into the fp32 gradient rows of the tables it named (hardware fp32 atomics;
+// rows named by several tokens receive every contribution, in no fixed order).
+__global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t* __restrict__ row_idx,
+                                                          int64_t n_tok, int32_t n_tables,
+                                                          int32_t row_dim,
+                                                          const float* __restrict__ d_e,
+                                                          GradTablePtrs g) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int groups = row_dim / 4;
+  const int per_tok = n_tables * groups;
+  for (int64_t tok = wave0; tok < n_tok; tok += wstride) {
+    const float* src = d_e + tok * (int64_t)n_tables * row_dim;
+    for (int q = lane; q < per_tok; q += 64) {
+      const int j = q / groups, c = (q - j * groups) * 4;
+      const float4 v = ld4(src + (int64_t)j * row_dim + c);
+      float* dst = g.p[j] + (int64_t)row_idx[tok * n_tables + j] * row_dim + c;
+      unsafeAtomicAdd(dst + 0, v.x);
+      unsafeAtomicAdd(dst + 1, v.y);
+      unsafeAtomicAdd(dst + 2, v.z);
+      unsafeAtomicAdd(dst + 3, v.w);
+    }
+  }
+}
+
+// bf16 [rows, cols] (row stride ld_src) -> [cols, rows_pad] (row stride
+// ld_dst), rows rows..rows_pad-1 of the result zero; 64 x 64 tiles via LDS.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_bits* __restrict__ src,
+                                                             int64_t rows, int64_t cols,
+                                                             int64_t ld_src, bf16_bits* __restrict__ dst,
+                                                             int64_t rows_pad, int64_t ld_dst) {
+  __shared__ bf16_bits tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? src[r * ld_src + c] : (bf16_bits)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows_pad) dst[c * ld_dst + r] = tile[tx][i];
+  }
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+unsigned grid_of(int64_t work, int64_t cap) {
+  int64_t g = work < cap ? work : cap;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  const int items = (a.d + 1023) / 1024;
+  hipError_t e;
+  const unsigned g1 = grid_of(a.n, 4096), g2 = grid_of(a.n * a.nb, 2048), g3 = grid_of(a.n, 2048);
+#define NGRAM_BWD_ITEMS(I)                                                  \
+  case I:                                                                   \
+    e = launch(bwd_stats_kernel<I>, g1, 256, 0, s, a);                      \
+    if (e != hipSuccess) return e;                                          \
+    e = launch(bwd_conv_kernel<I>, g2, 256, 0, s, a);                       \
+    if (e != hipSuccess) return e;                                          \
+    return launch(bwd_main_kernel<I>, g3, 256, 0, s, a);
+  switch (items) {
+    NGRAM_BWD_ITEMS(1)
+    NGRAM_BWD_ITEMS(2)
+    NGRAM_BWD_ITEMS(3)
+    NGRAM_BWD_ITEMS(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef NGRAM_BWD_ITEMS
+}
+
+hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
+                              int32_t row_dim, const float* d_e, const GradTablePtrs& g,
+                              hipStream_t s) {
+  if (n_tok == 0) return hipSuccess;
+  if (row_dim % 4 != 0) return hipErrorInvalidValue;
+  return launch(scatter_add_kernel, grid_of((n_tok + 3) / 4, 65536), 256, 0, s, row_idx, n_tok,
+                n_tables, row_dim, d_e, g);
+}
+
+hipError_t launch_transpose_bf16(const bf16_bits* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                 bf16_bits* dst, int64_t rows_pad, int64_t ld_dst, hipStream_t s) {
+  if (rows_pad == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
+  return launch(transpose_bf16_kernel, grid, 256, 0, s, src, rows, cols, ld_src, dst, rows_pad,
+                ld_dst);
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return launch(zero_f32_kernel, grid_of((n + 255) / 256, 16384), 256, 0, s, p, n);
+}
+
+}  // namespace ngram

@@ -152,6 +152,10 @@ struct AsyncProjArgs {
   const bf16_bits* wv;       // [d, K]
   EpiArgs epi;
   int32_t K, tiles_m, tiles_n, group_m;
+  // launch_projection_raw: C[M, (nb+1)*d] = A B^T written in fp32 to
+  // raw_out[row * raw_ld + seg * d + col] instead of the gate epilogue
+  float* raw_out;
+  int64_t raw_ld;
 };
 
 // Gate + gated value + conv block over a [B, T] token grid.
@@ -212,6 +216,46 @@ inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t s
 }
 
 // ---------------------------------------------------------------------------
+// backward pass (backward.hip)
+// ---------------------------------------------------------------------------
+struct GradTablePtrs {
+  float* p[NGRAM_MAX_TABLES];  // fp32 [rows_j, row_dim] gradient accumulators
+};
+
+struct BwdArgs {
+  int64_t n;                        // tokens
+  int32_t T, nb, d, dil;
+  float eps;
+  const bf16_bits* hidden;          // query rows: token t, branch b at t*h_tok + b*h_br
+  int64_t h_tok, h_br;
+  const float* kv;                  // recomputed [n, kv_ld]: K of each branch, then V (fp32)
+  int64_t kv_ld;
+  float* stats;                     // [n, nb, 4]: g, 1/rho_h, 1/rho_k, 1/r
+  float* dc;                        // [n, nb, d]: dC
+  const bf16_bits* d_out;           // [n, nb, d]
+  const bf16_bits* conv_w;          // [4, d]
+  const bf16_bits* gamma_q;         // nullable (= 1)
+  const bf16_bits* gamma_k;
+  const bf16_bits* gamma_u;
+  const float* state;               // [B, 3*dil, nb, d] normalised rows, or nullptr
+  int32_t add_residual;
+  bf16_bits* dkv;                   // [n, dkv_ld]: dK of each branch, then dV (bf16)
+  int64_t dkv_ld;
+  float* d_hidden;                  // hidden's layout, fp32, nullable
+  float* d_conv_w;                  // [4, d], accumulated (zeroed by the caller)
+  float* d_gammas;                  // [3, d] q, k, u, accumulated, nullable
+};
+
+// stats, dC + d_conv_w, then dK / dV / d_hidden / d_gammas (d <= 4096)
+hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s);
+hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
+                              int32_t row_dim, const float* d_e, const GradTablePtrs& g,
+                              hipStream_t s);
+hipError_t launch_transpose_bf16(const bf16_bits* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                 bf16_bits* dst, int64_t rows_pad, int64_t ld_dst, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // launchers (return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 hipError_t launch_compress(const int32_t* raw, int64_t n, const int32_t* lut, int32_t vocab,
@@ -234,6 +278,7 @@ hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a,
 int async_plan(int64_t M);
 int async_wave_cols(int plan);
 hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s);
+hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s);
 // split-K raw-tile variant for small M (decode); E given densely
 // Decode E tiles: the decode step's E [M, K] bf16 is stored as 1 KB tiles of
 // 16 tokens x 32 K values, tile (mb, kk) at element ((mb * K/32) + kk) * 512,

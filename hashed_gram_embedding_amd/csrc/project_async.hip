@@ -97,7 +97,7 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int ti
   n = sn - seg * tiles_n;
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool GATHER>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool GATHER, bool RAW = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProjArgs a) {
   constexpr int NW = WGM * WGN;          // waves per workgroup
   constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
@@ -264,7 +264,37 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
 
   const int wcol0 = n0 + wn * WTN;
   if (wcol0 >= d) return;
+  if (RAW) {
+    // plain product in fp32: a half-wave stores 32 consecutive columns (128
+    // bytes) of one row per register
+    float* __restrict__ C = a.raw_out + (int64_t)seg * d;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = wcol0 + ni * 32 + (lane & 31);
+        if (col < d) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + wm * WTM + mi * 32 + acc_row(r, lane);
+            if (row < M) C[row * a.raw_ld + col] = acc[mi][ni][r];
+          }
+        }
+      }
+    return;
+  }
   gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+}
+
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
+  AsyncProjArgs a = a0;
+  if (a.raw_out == nullptr || a.K % BK != 0) return hipErrorInvalidValue;
+  a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
+  a.tiles_n = (a.epi.d + BN - 1) / BN;
+  const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>, (unsigned)blocks,
+                64 * WGM * WGN, 0, s, a);
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
@@ -323,6 +353,18 @@ int async_wave_cols(int plan) {
   NGRAM_ASYNC_PLANS(NGRAM_WAVE_COLS)
 #undef NGRAM_WAVE_COLS
   return -1;
+}
+
+// The raw product serves the backward pass; it is built for the default
+// plans only (async_plan without a NGRAM_ASYNC_TILE override).
+hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s) {
+  if (a.epi.M == 0) return hipSuccess;
+  switch (plan) {
+    case 2: return launch_raw_t<64, 64, 64, 4, 2, 2>(a, s);
+    case 7: return launch_raw_t<256, 256, 64, 2, 2, 4>(a, s);
+    case 8: return launch_raw_t<128, 128, 64, 2, 2, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s) {

@@ -112,6 +112,10 @@ _SIGS = {
     "ngram_gate": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]),
     "ngram_causal_conv": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _p]),
     "ngram_forward_workspace_size": (_sz, [_cfgp, _i32, _i32]),
+    "ngram_backward_workspace_size": (_sz, [_cfgp, _i32, _i32]),
+    "ngram_backward": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p,
+                                      _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                      _sz, _p]),
     "ngram_forward": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p,
                                      _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
 }
@@ -273,3 +277,25 @@ def ngram_forward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, 
                                _ptr(err_flag), _ptr(workspace), workspace.numel(),
                                _stream(stream)), "ngram_forward")
     return out
+
+
+def ngram_backward_workspace_size(cfg, B: int, T: int) -> int:
+    return int(lib().ngram_backward_workspace_size(ctypes.byref(cfg), B, T))
+
+
+def ngram_backward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w,
+                   d_out, d_tables, d_w_k, d_w_v, d_conv_w, history=None, gamma_q=None,
+                   gamma_k=None, gamma_u=None, conv_state=None, flags: int = 0, d_hidden=None,
+                   d_gammas=None, workspace=None, stream=None):
+    """Gradients of sum(d_out * out); ``d_tables`` (fp32, one per table) are
+    accumulated, the other gradient tensors written."""
+    B, T = raw_ids.shape
+    if workspace is None:
+        workspace = _workspace(ngram_backward_workspace_size(cfg, B, T), raw_ids.device)
+    _check(lib().ngram_backward(ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history), _ptr(lut),
+                                _table_array(tables), _ptr(hidden), hidden_branch_stride,
+                                _ptr(w_k), _ptr(w_v), _ptr(conv_w), _ptr(gamma_q), _ptr(gamma_k),
+                                _ptr(gamma_u), _ptr(conv_state), flags, _ptr(d_out),
+                                _table_array(d_tables), _ptr(d_w_k), _ptr(d_w_v), _ptr(d_conv_w),
+                                _ptr(d_hidden), _ptr(d_gammas), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "ngram_backward")

@@ -249,6 +249,45 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of ngram_forward (training): the gradients of L = sum(d_out (.) out)
+ * for the tables, W_K, W_V, the conv taps, the query rows and the RMSNorm
+ * gains, each step the chain rule of the forward step ("Qwen3.8-Flash-Next
+ * 深度研究" §2.3).  The table gradient is the lookup's adjoint, a scatter-add
+ * of dE into the rows the tokens named -- the page lists this "scatter"
+ * beside the gather among the layer's fused operators (the same page, §9.4).
+ *
+ * Supported: bf16 activations, W stored [d, mem] (NGRAM_W_D_MEM), hidden_dim
+ * a multiple of 64 and at most 4096; the tables may be bf16 or fp8.  The
+ * forward intermediates (E, K, V, gates, norms) are recomputed.
+ *
+ *   raw_ids ... conv_state, flags  as for ngram_forward (NGRAM_ADD_RESIDUAL:
+ *              out = hidden + Delta, so d_hidden also receives d_out)
+ *   d_out      device [B, T, n_branches, d] bf16: dL/d(out)
+ *   d_tables   HOST array of n_tables device pointers, table j an fp32
+ *              [rows[j], row_dim] gradient, ACCUMULATED (+=); rows named by
+ *              several tokens receive every contribution through fp32
+ *              atomics, so their last bits may differ from run to run
+ *   d_w_k      device fp32 [n_branches, d, mem_dim] (written), d_w_v fp32 [d, mem_dim]
+ *   d_conv_w   device fp32 [conv_kernel, d] (written)
+ *   d_hidden   device fp32, hidden's layout (written), nullable
+ *   d_gammas   device fp32 [3, d]: gamma_q, gamma_k, gamma_u (written), nullable
+ *   workspace  device, >= ngram_backward_workspace_size(cfg, B, T) bytes
+ *
+ * dK and dV enter the dE and dW products as bf16 (fp32 accumulation); the
+ * other gradients are fp32 throughout.  Returns NGRAM_EDTYPE / NGRAM_ESHAPE
+ * for configurations outside the supported set, otherwise as ngram_forward.
+ */
+size_t ngram_backward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T);
+int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                   const int32_t* history, const int32_t* lut, const void* const* tables,
+                   const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                   const void* w_v, const void* conv_w, const void* gamma_q,
+                   const void* gamma_k, const void* gamma_u, const float* conv_state,
+                   int32_t flags, const void* d_out, float* const* d_tables, float* d_w_k,
+                   float* d_w_v, float* d_conv_w, float* d_hidden, float* d_gammas,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Benchmark instrumentation (not part of the layer).  With n == 2 * NGRAM_N_STAGES, every
  * following ngram_forward times its stages on the device -- 0 hash, 1 gather, 2 projection,
  * 3 gate + conv: the first kernel of stage i stamps its begin time into events[2i] and every

@@ -130,3 +130,14 @@ def oracle_forward_window(orc, w, ids, hist, b, start, length, hidden_fn, wk_hos
     keep = slice(start - s0, start - s0 + length)
     return {k: (v[keep] if isinstance(v, np.ndarray) and v.ndim >= 2 and v.shape[0] == len(toks)
                 else v) for k, v in out.items()}
+
+
+def oracle_backward(orc, w, ids, hist, hidden_storage, wk_host, wv_host, conv_host, gam_storage,
+                    d_out, conv_state, residual):
+    """Oracle gradients for a whole (small) batch: hidden [n, nbh, d] storage,
+    weights in the oracle's [mem, d] orientation, d_out float64 [n, nb, d]."""
+    return orc.backward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
+                        w.rows(), W.hash_multipliers(w), oracle_rows(w), hidden_storage, wk_host,
+                        wv_host, conv_host, w.dtype, d_out, gamma_q=gam_storage["q"],
+                        gamma_k=gam_storage["k"], gamma_u=gam_storage["u"], eps=w.rms_eps,
+                        conv_state=conv_state, add_residual=residual, **oracle_table_kw(w))
