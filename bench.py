@@ -12,6 +12,10 @@ inputs are resident in HBM before timing starts.
 Prints one JSON line: tokens/s, the step's share of the HBM roofline, the
 roofline of the dominant kernel (HIP-event timing of each stage, measured in
 this run), and the CPU oracle timed on this host on a bounded sample.
+
+``--pass backward`` measures a training step of the layer instead
+(ngram_forward then ngram_backward, default workload qwen_train: 16 x 4,096
+tokens at the Qwen dimensions, 8 tables of ~2M rows) and prints its own line.
 """
 from __future__ import annotations
 
@@ -37,9 +41,11 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="qwen_decode")
+    ap.add_argument("--steps", type=int, default=None, help="2000 forward, 100 backward")
+    ap.add_argument("--warmup", type=int, default=None, help="100 forward, 10 backward")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward")
+    ap.add_argument("--workload", default=None,
+                    help="qwen_decode (forward), qwen_train (backward)")
     ap.add_argument("--pool", type=int, default=64, help="distinct batches (decode)")
     ap.add_argument("--stage-steps", type=int, default=200,
                     help="steps of the per-stage event timing region")
@@ -282,6 +288,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.pass_ == "backward":
+        main_backward(args)
+        return
+    args.workload = args.workload or "qwen_decode"
+    args.steps = 2000 if args.steps is None else args.steps
+    args.warmup = 100 if args.warmup is None else args.warmup
     print(f"[bench] setting up workload {args.workload}", file=sys.stderr, flush=True)
     setup = Setup(args.workload, args.pool)
     w = setup.w
@@ -394,6 +406,194 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# training step: forward + backward
+# ---------------------------------------------------------------------------
+
+BWD_STAGES = ("recompute", "rows", "d_e", "d_w_scatter")
+
+
+def backward_algorithmic(w):
+    """Algorithmic flops / bytes of ngram_backward's stages: the recompute of
+    K and V, the dE product and the dW products each take 2 n mem d flops per
+    projection; the per-row stage reads K, V, the query, d_out and writes dK,
+    dV, d_hidden; the scatter reads dE and read-modify-writes one fp32 table
+    row per token and table."""
+    n, nb, d, mem = w.n_tokens, w.n_branches, w.hidden, w.mem_dim
+    nbh = nb if nb > 1 else 1
+    g = 2.0 * n * mem * d * (nb + 1)
+    rows_b = n * w.n_tables * w.row_dim * 2
+    return {
+        "recompute": dict(flops=g, bytes=4 * n * (1 + w.n_tables) + rows_b + n * mem * 2
+                          + (nb + 1) * mem * d * 2 + n * (nb + 1) * d * 4),
+        "rows": dict(flops=0.0, bytes=n * (nb + 1) * d * 4 + n * nbh * d * 2 + n * nb * d * 2
+                     + n * (nb + 1) * d * 2 + n * nbh * d * 4),
+        "d_e": dict(flops=g, bytes=n * (nb + 1) * d * 2 + (nb + 1) * mem * d * 2 + n * mem * 4),
+        "d_w_scatter": dict(flops=g, bytes=n * (nb + 1) * d * 2 + n * mem * 2
+                            + (nb + 1) * mem * d * 4 + n * mem * 4 + 2 * n * w.n_tables
+                            * w.row_dim * 4),
+    }
+
+
+def cpu_baseline_backward(setup: Setup, d_out_seed: int, seconds: float):
+    """The oracle's forward + backward on 256-token slices of the workload's
+    sequences, each taken as a sequence of its own (the same shapes and
+    tables; the oracle's work per token does not depend on where a slice
+    starts)."""
+    from oracle import oracle as O
+
+    W, w = setup.W, setup.w
+    wk = np.stack([W.weight_values(w, "k", b) for b in range(w.n_branches)])
+    wv = W.weight_values(w, "v")
+    conv = W.conv_weight_values(w)
+    lut = W.make_lut(w)
+    mult = W.hash_multipliers(w)
+    rows = w.rows()
+    L = 256
+    rs = np.random.default_rng(d_out_seed)
+    O.lib()
+    done, elapsed, used = 0, 0.0, 0
+    for _ in range(64):
+        b = int(rs.integers(0, w.batch))
+        start = int(rs.integers(0, w.seq_len - L))
+        sub = setup.ids_host[0][b:b + 1, start:start + L]
+        toks = b * w.seq_len + np.arange(start, start + L)
+        hid = W.hidden_values(w, toks)
+        d_out = rs.standard_normal((L, w.n_branches, w.hidden))
+        comp, _ = O.compress(sub, lut, w.vocab, w.vocab_compressed)
+        r = O.hash_rows(comp, None, w.orders, w.heads, rows, mult)
+        cache = {j: {int(x): W.table_row_values(w, j, np.array([x]))[0]
+                     for x in np.unique(r[:, j])} for j in range(w.n_tables)}
+
+        def provider(j, rr, cache=cache):
+            return np.stack([cache[j][int(x)] for x in rr])
+
+        t0 = time.perf_counter()
+        O.backward(sub, None, lut, w.vocab, w.vocab_compressed, w.orders, w.heads, rows, mult,
+                   provider, hid, wk, wv, conv, w.dtype, d_out, eps=w.rms_eps)
+        elapsed += time.perf_counter() - t0
+        done += L
+        used += 1
+        if elapsed >= seconds:
+            break
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} tokens of workload {w.name} ({used} x 256-token slices taken as "
+                      f"sequences); oracle forward + backward, fp64 C loops, OpenMP over tokens; "
+                      f"{elapsed:.1f} s of oracle time"}
+
+
+def main_backward(args):
+    import torch
+    from synth import device as SD
+
+    name = args.workload or "qwen_train"
+    print(f"[bench] setting up training workload {name}", file=sys.stderr, flush=True)
+    setup = Setup(name, 1)
+    H, w = setup.H, setup.w
+    if w.dtype != "bf16" or w.seq_len == 1:
+        raise SystemExit("--pass backward needs a bf16 prefill-shaped workload")
+    n, nb, d = w.n_tokens, w.n_branches, w.hidden
+    d_out = torch.empty((w.batch, w.seq_len, nb, d), dtype=torch.bfloat16, device="cuda")
+    SD.fill_normal(d_out, w.hidden_seed(977), 1.0)
+    # table gradients accumulate over the steps (gradient accumulation); a
+    # sparse optimizer would clear only the rows it updates
+    d_tabs = [torch.zeros((r, w.row_dim), dtype=torch.float32, device="cuda") for r in w.rows()]
+    d_wk = torch.empty((nb, d, w.mem_dim), dtype=torch.float32, device="cuda")
+    d_wv = torch.empty((d, w.mem_dim), dtype=torch.float32, device="cuda")
+    d_cw = torch.empty((4, d), dtype=torch.float32, device="cuda")
+    d_h = torch.empty(tuple(setup.hidden[0].shape), dtype=torch.float32, device="cuda")
+    bws = torch.empty(H.ngram_backward_workspace_size(setup.cfg, w.batch, w.seq_len),
+                      dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def bwd():
+        H.ngram_backward(setup.cfg, setup.ids[0], setup.lut, setup.tables, setup.hidden[0],
+                         setup.hbs, setup.wk, setup.wv, setup.conv, d_out, d_tabs, d_wk, d_wv,
+                         d_cw, d_hidden=d_h, workspace=bws)
+
+    def train_step():
+        setup.step(0)
+        bwd()
+
+    def timed(fn, k):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    steps = 100 if args.steps is None else args.steps
+    warm = 10 if args.warmup is None else args.warmup
+    print(f"[bench] warmup {warm} training steps", file=sys.stderr, flush=True)
+    for _ in range(warm):
+        train_step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {steps} training steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ms_step = timed(train_step, steps)
+    wall = time.perf_counter() - t0
+    ms_fwd = timed(lambda: setup.step(0), max(10, steps // 4))
+    ms_bwd = timed(bwd, max(10, steps // 4))
+
+    print("[bench] backward stage timing", file=sys.stderr, flush=True)
+    k = min(args.stage_steps, 50)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * H.ngram.N_STAGES)]
+           for _ in range(k)]
+    for i in range(k):
+        H.ngram.ngram_set_timing_events(evs[i])
+        bwd()
+    mask = H.ngram.ngram_timing_stage_mask()
+    H.ngram.ngram_set_timing_events(None)
+    torch.cuda.synchronize()
+    stage_avg = {BWD_STAGES[s]: (float(np.mean([e[2 * s].elapsed_time(e[2 * s + 1])
+                                                for e in evs])) if mask >> s & 1 else 0.0)
+                 for s in range(len(BWD_STAGES))}
+    alg = backward_algorithmic(w)
+    dom = max(stage_avg, key=stage_avg.get)
+    a = alg[dom]
+    sec = stage_avg[dom] * 1e-3
+    if a["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > a["bytes"] / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": a["flops"] / sec / 1e12,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": a["bytes"] / sec / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel=dom,
+                algorithmic_bytes=a["bytes"], algorithmic_flops=a["flops"],
+                avg_ms=stage_avg[dom])
+    fwd_flops = 2.0 * n * w.mem_dim * d * (nb + 1)
+    bwd_flops = sum(v["flops"] for v in alg.values())
+    result = {
+        "metric": "N-gram-embedding training-step tokens/sec (forward + backward), 1 MI355X",
+        "value": n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+                   "tokens_per_step": n,
+                   "tables": f"{w.n_tables} x {w.rows()[0]}.. rows x {w.row_dim} {w.tdtype}",
+                   "table_grads": "fp32, accumulated", "mem_dim": w.mem_dim, "hidden": d,
+                   "branches": nb, "parallelism": "single GPU", "weight_layout": "[d, mem]"},
+        "ms_forward": ms_fwd, "ms_backward": ms_bwd,
+        "tflops_step": (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12,
+        "tflops_backward": bwd_flops / (ms_bwd * 1e-3) / 1e12,
+        "stage_ms": stage_avg, "wall_s_timed": wall, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_backward(setup, 977, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

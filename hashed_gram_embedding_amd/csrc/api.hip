@@ -683,6 +683,7 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
                    int32_t flags, const void* d_out, float* const* d_tables, float* d_w_k,
                    float* d_w_v, float* d_conv_w, float* d_hidden, float* d_gammas,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  const TimedCall timed;
   int st = validate(cfg);
   if (st) return st;
   if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM) return NGRAM_EDTYPE;
@@ -736,6 +737,7 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   const bf16_bits* wv = static_cast<const bf16_bits*>(w_v);
 
   // recompute: row ids, E, and K / V in fp32
+  stage(0);
   const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
   st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, nullptr, s));
   if (st) return st;
@@ -744,6 +746,7 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   st = hip_status(raw_gemm(e, n, mem, wk, wv, nb, d, kv, N, s));
   if (st) return st;
   // the per-row backward: gates, conv, RMSNorms -> dK, dV (bf16), d_hidden, d_conv_w, d_gammas
+  stage(1);
   st = hip_status(launch_zero_f32(d_conv_w, 4 * (int64_t)d, s));
   if (st) return st;
   if (d_gammas) {
@@ -780,6 +783,7 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   st = hip_status(launch_bwd_rows(ba, s));
   if (st) return st;
   // dE = [dK dV] [W_K; W_V]: the weights transposed to [mem, N] feed the product
+  stage(2);
   st = hip_status(launch_transpose_bf16(wk, (int64_t)nb * d, mem, mem, wt, (int64_t)nb * d, N, s));
   if (st) return st;
   st = hip_status(launch_transpose_bf16(wv, d, mem, mem, wt + (int64_t)nb * d, d, N, s));
@@ -787,6 +791,7 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   st = hip_status(raw_gemm(dkv, n, N, nullptr, wt, 0, mem, de, mem, s));
   if (st) return st;
   // dW = [dK dV]^T E: both operands transposed to [., n_pad], tokens padded with zeros
+  stage(3);
   st = hip_status(launch_transpose_bf16(dkv, n, N, N, dkvt, L.n_pad, L.n_pad, s));
   if (st) return st;
   st = hip_status(launch_transpose_bf16(e, n, mem, mem, et, L.n_pad, L.n_pad, s));

@@ -296,8 +296,11 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
  * packet between the kernels.  A kernel that covers several stages counts in the last of them
  * (the decode path hashes and gathers in one kernel; the fused path hashes, gathers and
  * projects in one); the stages it absorbs launch nothing and leave their events untouched.
+ * ngram_backward times four stages the same way: 0 the recompute (hash, gather, K / V
+ * product), 1 the per-row backward, 2 the dE product (with its transposes), 3 the dW products
+ * and the table scatter-add.
  * ngram_timing_stage_mask() returns the bit mask (bit i = stage i) of the stages that launched
- * a kernel in the last ngram_forward call.  n == 0 turns timing off.  The setting is
+ * a kernel in the last ngram_forward or ngram_backward call.  n == 0 turns timing off.  The setting is
  * process-wide and not synchronised: set it only while no other thread calls ngram_forward.
  * Returns NGRAM_EINVAL for other n or NULL events.
  */

@@ -195,6 +195,12 @@ WORKLOADS = {
                                 history_len=2, orders=(2, 3), heads=4, row_start=20000003,
                                 row_dim=320, hidden=2560, n_branches=1, dtype="bf16",
                                 zipf_s=1.1, param_index=3, table_dtype="fp8"),
+    # a training step of the layer at the Qwen dimensions: 16 x 4,096 tokens;
+    # tables of ~2M rows so that their fp32 gradients (8 x 2M x 320 x 4 B) fit
+    "qwen_train": Workload("qwen_train", 7, vocab=248320, batch=16, seq_len=4096,
+                           history_len=0, orders=(2, 3), heads=4, row_start=2000003,
+                           row_dim=320, hidden=2560, n_branches=1, dtype="bf16",
+                           zipf_s=1.1),
     "qwen_prefill_fp8": Workload("qwen_prefill_fp8", 4, vocab=248320, batch=1, seq_len=262144,
                                  history_len=0, orders=(2, 3), heads=4, row_start=20000003,
                                  row_dim=320, hidden=2560, n_branches=1, dtype="bf16",
