@@ -237,7 +237,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 // (bf16), the weights transposed, dE (fp32), and dK / dV and E transposed
 // over tokens padded to a multiple of 64.
 struct BwdLayout {
-  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, total;
+  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, total;
   int64_t n_pad;
 };
 
@@ -254,13 +254,15 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
   L.row_idx = take((size_t)n * c->n_tables * 4);
   L.e = take((size_t)n * mem * 2);
   L.kv = take((size_t)n * N * 4);
-  L.stats = take((size_t)n * nb * 16);
+  L.stats = take((size_t)n * nb * kStatsStride * 4);
   L.dc = take((size_t)n * nb * d * 4);
   L.dkv = take((size_t)n * N * 2);
   L.wt = take((size_t)mem * N * 2);
   L.de = take((size_t)n * mem * 4);
   L.dkvt = take((size_t)N * L.n_pad * 2);
   L.et = take((size_t)mem * L.n_pad * 2);
+  L.part = take((size_t)kBwdBlocks * 7 * d * 4);
+  L.rtmp = take((size_t)32 * 4 * d * 4);
   L.total = off;
   return L;
 }
@@ -747,12 +749,6 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   if (st) return st;
   // the per-row backward: gates, conv, RMSNorms -> dK, dV (bf16), d_hidden, d_conv_w, d_gammas
   stage(1);
-  st = hip_status(launch_zero_f32(d_conv_w, 4 * (int64_t)d, s));
-  if (st) return st;
-  if (d_gammas) {
-    st = hip_status(launch_zero_f32(d_gammas, 3 * (int64_t)d, s));
-    if (st) return st;
-  }
   BwdArgs ba;
   memset(&ba, 0, sizeof ba);
   ba.n = n;
@@ -778,9 +774,10 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   ba.dkv = dkv;
   ba.dkv_ld = N;
   ba.d_hidden = d_hidden;
-  ba.d_conv_w = d_conv_w;
-  ba.d_gammas = d_gammas;
-  st = hip_status(launch_bwd_rows(ba, s));
+  ba.part_conv = reinterpret_cast<float*>(ws + L.part);
+  ba.part_gain = d_gammas ? ba.part_conv + (size_t)kBwdBlocks * 4 * d : nullptr;
+  st = hip_status(launch_bwd_rows(ba, d_conv_w, d_gammas, reinterpret_cast<float*>(ws + L.rtmp),
+                                  s));
   if (st) return st;
   // dE = [dK dV] [W_K; W_V]: the weights transposed to [mem, N] feed the product
   stage(2);

@@ -75,9 +75,10 @@ struct Cols {
   }
 };
 
-// 1. Per token and branch: g = sigmoid(q^ . k^ / sqrt(d)) and the three
-// reciprocal norms 1/rho_h, 1/rho_k, 1/r (r: the norm of U = g V), from the
-// query rows and the recomputed fp32 K/V.
+// 1. Per token and branch: g = sigmoid(q^ . k^ / sqrt(d)), the three
+// reciprocal norms 1/rho_h, 1/rho_k, 1/r (r: the norm of U = g V) and the
+// gate's raw product P = sum (gamma_q h)(gamma_k K), from the query rows and
+// the recomputed fp32 K/V.  stats row: g, 1/rho_h, 1/rho_k, 1/r, P, 0, 0, 0.
 template <int ITEMS>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
   __shared__ float red[4][4];
@@ -109,7 +110,9 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
         const float ih = 1.0f / sqrtf(s[0] / d + a.eps), ik = 1.0f / sqrtf(s[1] / d + a.eps);
         const float g = 1.0f / (1.0f + expf(-s[2] * ih * ik / sqrtf((float)d)));
         const float ir = 1.0f / sqrtf(g * g * vv[0] / d + a.eps);
-        st4(a.stats + (t * nb + br) * 4, make_float4(g, ih, ik, ir));
+        float* o = a.stats + (t * nb + br) * kStatsStride;
+        st4(o, make_float4(g, ih, ik, ir));
+        st4(o + 4, make_float4(s[2], 0.0f, 0.0f, 0.0f));
       }
     }
   }
@@ -122,7 +125,7 @@ __device__ __forceinline__ float4 n_value(const BwdArgs& a, int64_t t, int pos, 
                                           int c, float4 gu) {
   if (p >= 0) {
     const int64_t s = t - (pos - p);
-    const float4 st = ld4(a.stats + (s * a.nb + br) * 4);
+    const float4 st = ld4(a.stats + (s * a.nb + br) * kStatsStride);
     const float4 v = ld4(a.kv + s * a.kv_ld + a.nb * a.d + c);
     return mul(gu, mul(v, mk4(st.x * st.w)));
   }
@@ -133,8 +136,9 @@ __device__ __forceinline__ float4 n_value(const BwdArgs& a, int64_t t, int pos, 
 }
 
 // 2. dC = dOut (.) SiLU'(C) per token and branch (C = sum_i w_i (.) N_{t-i*dil}),
-// and the taps' gradient d_w[i] += dC (.) N_{t-i*dil}, summed in registers over
-// the rows of this block and added once per block.
+// and the taps' gradient d_w[i] = sum dC (.) N_{t-i*dil}: summed in registers
+// over the rows of this block, written as the block's partial row [4 d] of
+// a.part_conv (the column sum over blocks runs afterwards, no atomics).
 template <int ITEMS>
 __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
   const int nb = a.nb, d = a.d, dil = a.dil;
@@ -167,31 +171,39 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) dw[i][j] = fma4(dc, nv[i], dw[i][j]);
     }
   }
+  float* part = a.part_conv + (int64_t)blockIdx.x * 4 * d;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j)
     if (cl.ok[j])
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* p = a.d_conv_w + (int64_t)i * d + cl.c[j];
-        unsafeAtomicAdd(p + 0, dw[i][j].x);
-        unsafeAtomicAdd(p + 1, dw[i][j].y);
-        unsafeAtomicAdd(p + 2, dw[i][j].z);
-        unsafeAtomicAdd(p + 3, dw[i][j].w);
-      }
+      for (int i = 0; i < 4; ++i) st4(part + (int64_t)i * d + cl.c[j], dw[i][j]);
 }
 
 // 3. Per token, all branches: dN -> dU (residual + RMSNorm), dg and dV (U = g V),
 // dz -> dK and the query's gradient (both RMSNorms), the gains' gradients.
 // dK and dV are written in bf16 as the operands of the dE and dW products.
-template <int ITEMS>
+//
+// One block reduction per row suffices.  With A = sum gamma_u dN V and
+// B = sum dOut V (both from rows already loaded):
+//   dg = sum dU V = B + A r^-1 (1 - g^2 sum(V^2) / (d r^2)) = B + A eps r^-3,
+// since r^2 = g^2 sum(V^2) / d + eps (the norm's scale invariance leaves only
+// the eps term; this form also avoids the cancellation).  The two RMSNorm
+// backward sums of the gate are multiples of the gate's raw product P:
+//   sum gamma_k dk^ K = (dz / sqrt d) rho_h^-1 P,  sum gamma_q dq^ h = (dz / sqrt d) rho_k^-1 P.
+// The gains' gradients accumulate per thread in LDS (each thread owns its
+// columns) and leave as the block's partial row [3 d] of a.part_gain.
+template <int ITEMS, bool ONE_BRANCH>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   __shared__ float red[4][2];
-  const int nb = a.nb, d = a.d, dil = a.dil;
-  const float fd = (float)d, sd = sqrtf(fd);
+  __shared__ float4 gacc[3][ITEMS][256];
+  const int nb = ONE_BRANCH ? 1 : a.nb, d = a.d, dil = a.dil;
+  const float fd = (float)d, rsd = 1.0f / sqrtf(fd);
   const Cols<ITEMS> cl(d);
-  float4 dgq[ITEMS], dgk[ITEMS], dgu[ITEMS];
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) dgq[j] = dgk[j] = dgu[j] = mk4(0.0f);
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) gacc[q][j][tid] = mk4(0.0f);
   for (int64_t t = blockIdx.x; t < a.n; t += gridDim.x) {
     const int pos = (int)(t % a.T);
     const float* kv = a.kv + t * a.kv_ld;
@@ -202,100 +214,109 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       dv[j] = dhs[j] = mk4(0.0f);
     }
     for (int br = 0; br < nb; ++br) {
-      const float4 st = ld4(a.stats + (t * nb + br) * 4);  // g, 1/rho_h, 1/rho_k, 1/r
-      const float g = st.x, ih = st.y, ik = st.z, ir = st.w;
       const int64_t row = t * nb + br;
-      // dN = sum_i w_i (.) dC_{t + i*dil} inside the sequence; U = g V
-      float4 dn[ITEMS];
-      float s1[2] = {0.0f, 0.0f};
+      const float4 st = ld4(a.stats + row * kStatsStride);  // g, 1/rho_h, 1/rho_k, 1/r
+      const float P = a.stats[row * kStatsStride + 4];
+      const float g = st.x, ih = st.y, ik = st.z, ir = st.w;
+      // dN = sum_i w_i (.) dC_{t + i*dil} inside the sequence
+      float4 dn[ITEMS], go[ITEMS], h[ITEMS], k[ITEMS];
+      float s[2] = {0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
+        const int c = cl.c[j];
+        go[j] = Elem<bf16_bits>::load4(a.d_out, row * d + c);
+        h[j] = Elem<bf16_bits>::load4(a.hidden, t * a.h_tok + br * a.h_br + c);
+        k[j] = ld4(kv + br * d + c);
         dn[j] = mk4(0.0f);
+#pragma unroll
         for (int i = 0; i < 4; ++i)
           if (pos + i * dil < a.T)
-            dn[j] = fma4(Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + cl.c[j]),
-                         ld4(a.dc + (row + (int64_t)i * dil * nb) * d + cl.c[j]), dn[j]);
-        if (cl.ok[j]) s1[0] += dot(mul(gain4(a.gamma_u, cl.c[j]), dn[j]), mul(mk4(g), v[j]));
-      }
-      block_sum<2>(s1, red);
-      // dU = dOut + gamma_u dN / r - U sum(gamma_u dN U) / (d r^3); dg = sum dU V
-      float4 du[ITEMS];
-      float s2[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < ITEMS; ++j) {
-        const float4 u = mul(mk4(g), v[j]);
-        const float4 gu = gain4(a.gamma_u, cl.c[j]);
-        du[j] = add(Elem<bf16_bits>::load4(a.d_out, row * d + cl.c[j]),
-                    add(mul(mul(gu, dn[j]), mk4(ir)), mul(u, mk4(-s1[0] * ir * ir * ir / fd))));
+            dn[j] = fma4(Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c),
+                         ld4(a.dc + (row + (int64_t)i * dil * nb) * d + c), dn[j]);
         if (cl.ok[j]) {
-          s2[0] += dot(du[j], v[j]);
-          dgu[j] = fma4(mul(dn[j], u), mk4(ir), dgu[j]);
-        }
-        dv[j] = fma4(mk4(g), du[j], dv[j]);
-      }
-      block_sum<2>(s2, red);
-      const float dz = s2[0] * g * (1.0f - g);
-      // q^ = gamma_q h / rho_h, k^ = gamma_k K / rho_k; dq^ = dz k^ / sqrt d, dk^ = dz q^ / sqrt d
-      float4 h[ITEMS], k[ITEMS], dq[ITEMS], dk[ITEMS];
-      float s3[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < ITEMS; ++j) {
-        h[j] = Elem<bf16_bits>::load4(a.hidden, t * a.h_tok + br * a.h_br + cl.c[j]);
-        k[j] = ld4(kv + br * d + cl.c[j]);
-        const float4 gq = gain4(a.gamma_q, cl.c[j]), gk = gain4(a.gamma_k, cl.c[j]);
-        dq[j] = mul(mk4(dz / sd), mul(gk, mul(k[j], mk4(ik))));
-        dk[j] = mul(mk4(dz / sd), mul(gq, mul(h[j], mk4(ih))));
-        if (cl.ok[j]) {
-          s3[0] += dot(mul(gk, dk[j]), k[j]);
-          s3[1] += dot(mul(gq, dq[j]), h[j]);
+          s[0] += dot(mul(gain4(a.gamma_u, c), dn[j]), v[j]);
+          s[1] += dot(go[j], v[j]);
         }
       }
-      block_sum<2>(s3, red);
+      block_sum<2>(s, red);
+      const float A = s[0];
+      const float dz = (s[1] + A * a.eps * ir * ir * ir) * g * (1.0f - g);
+      const float cu = -g * g * A * ir * ir * ir / fd;  // dU's term along V
+      const float cz = dz * rsd;
+      const float sk = cz * ih * P * ik * ik * ik / fd, sq = cz * ik * P * ih * ih * ih / fd;
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
-        const float4 gq = gain4(a.gamma_q, cl.c[j]), gk = gain4(a.gamma_k, cl.c[j]);
-        const float4 dkk = add(mul(mul(gk, dk[j]), mk4(ik)), mul(k[j], mk4(-s3[0] * ik * ik * ik / fd)));
-        float4 dh = add(mul(mul(gq, dq[j]), mk4(ih)), mul(h[j], mk4(-s3[1] * ih * ih * ih / fd)));
-        if (a.add_residual) dh = add(dh, Elem<bf16_bits>::load4(a.d_out, row * d + cl.c[j]));
-        if (cl.ok[j]) {
-          Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + br * d + cl.c[j], dkk);
-          dgk[j] = fma4(mul(dk[j], k[j]), mk4(ik), dgk[j]);
-          dgq[j] = fma4(mul(dq[j], h[j]), mk4(ih), dgq[j]);
+        if (!cl.ok[j]) continue;
+        const int c = cl.c[j];
+        const float4 gu = gain4(a.gamma_u, c), gq = gain4(a.gamma_q, c), gk = gain4(a.gamma_k, c);
+        // dU = dOut + gamma_u dN / r - U sum(gamma_u dN U) / (d r^3), U = g V
+        const float4 du = fma4(v[j], mk4(cu), fma4(mul(gu, dn[j]), mk4(ir), go[j]));
+        // q^ = gamma_q h / rho_h, k^ = gamma_k K / rho_k; dq^ = dz k^ / sqrt d, dk^ = dz q^ / sqrt d
+        const float4 dqh = mul(mk4(cz * ik), mul(gk, k[j]));
+        const float4 dkh = mul(mk4(cz * ih), mul(gq, h[j]));
+        const float4 dkk = fma4(k[j], mk4(-sk), mul(mul(gk, dkh), mk4(ik)));
+        float4 dh = fma4(h[j], mk4(-sq), mul(mul(gq, dqh), mk4(ih)));
+        if (a.add_residual) dh = add(dh, go[j]);
+        Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + br * d + c, dkk);
+        gacc[0][j][tid] = fma4(mul(dqh, h[j]), mk4(ih), gacc[0][j][tid]);
+        gacc[1][j][tid] = fma4(mul(dkh, k[j]), mk4(ik), gacc[1][j][tid]);
+        gacc[2][j][tid] = fma4(mul(dn[j], v[j]), mk4(g * ir), gacc[2][j][tid]);
+        if (ONE_BRANCH) {
+          Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + d + c, mul(mk4(g), du));
+          if (a.d_hidden) st4(a.d_hidden + t * a.h_tok + c, dh);
+        } else {
+          dv[j] = fma4(mk4(g), du, dv[j]);
           if (a.d_hidden) {
             if (a.h_br == 0)
               dhs[j] = add(dhs[j], dh);
             else
-              st4(a.d_hidden + t * a.h_tok + br * a.h_br + cl.c[j], dh);
+              st4(a.d_hidden + t * a.h_tok + br * a.h_br + c, dh);
           }
         }
       }
     }
+    if (!ONE_BRANCH) {
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j)
-      if (cl.ok[j]) {
-        Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + nb * d + cl.c[j], dv[j]);
-        if (a.d_hidden && a.h_br == 0) st4(a.d_hidden + t * a.h_tok + cl.c[j], dhs[j]);
-      }
-  }
-  if (a.d_gammas) {
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j)
-      if (cl.ok[j]) {
-        const float4* gsrc[3] = {&dgq[j], &dgk[j], &dgu[j]};
-        for (int q = 0; q < 3; ++q) {
-          float* p = a.d_gammas + (int64_t)q * d + cl.c[j];
-          unsafeAtomicAdd(p + 0, gsrc[q]->x);
-          unsafeAtomicAdd(p + 1, gsrc[q]->y);
-          unsafeAtomicAdd(p + 2, gsrc[q]->z);
-          unsafeAtomicAdd(p + 3, gsrc[q]->w);
+      for (int j = 0; j < ITEMS; ++j)
+        if (cl.ok[j]) {
+          Elem<bf16_bits>::store4(a.dkv, t * a.dkv_ld + nb * d + cl.c[j], dv[j]);
+          if (a.d_hidden && a.h_br == 0) st4(a.d_hidden + t * a.h_tok + cl.c[j], dhs[j]);
         }
-      }
+    }
+  }
+  if (a.part_gain) {
+    float* part = a.part_gain + (int64_t)blockIdx.x * 3 * d;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (cl.ok[j])
+#pragma unroll
+        for (int q = 0; q < 3; ++q) st4(part + (int64_t)q * d + cl.c[j], gacc[q][j][tid]);
   }
 }
 
+// Column sums of a row-major [rows, cols] fp32 matrix: block row y of the
+// grid sums rows [y*per, min((y+1)*per, rows)) into dst[y, :].
+__global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ src,
+                                                       int64_t rows, int64_t cols, int per,
+                                                       float* __restrict__ dst) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * per;
+  const int64_t r1 = r0 + per < rows ? r0 + per : rows;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t r = r0;
+  for (; r + 8 <= r1; r += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += src[(r + u) * cols + col];
+  for (; r < r1; ++r) acc[0] += src[r * cols + col];
+  dst[(int64_t)blockIdx.y * cols + col] =
+      ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
 // 4. The gather's adjoint: one wavefront per token adds the token's dE slices
-// into the fp32 gradient rows of the tables it named (hardware fp32 atomics;
-// rows named by several tokens receive every contribution, in no fixed order).
+// into the fp32 gradient rows of the tables it named (hardware fp32 atomics,
+// 64 consecutive floats per instruction; rows named by several tokens
+// receive every contribution, in no fixed order).
 __global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t* __restrict__ row_idx,
                                                           int64_t n_tok, int32_t n_tables,
                                                           int32_t row_dim,
@@ -304,18 +325,13 @@ __global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t* __restr
   const int lane = threadIdx.x & 63;
   const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int groups = row_dim / 4;
-  const int per_tok = n_tables * groups;
   for (int64_t tok = wave0; tok < n_tok; tok += wstride) {
     const float* src = d_e + tok * (int64_t)n_tables * row_dim;
-    for (int q = lane; q < per_tok; q += 64) {
-      const int j = q / groups, c = (q - j * groups) * 4;
-      const float4 v = ld4(src + (int64_t)j * row_dim + c);
-      float* dst = g.p[j] + (int64_t)row_idx[tok * n_tables + j] * row_dim + c;
-      unsafeAtomicAdd(dst + 0, v.x);
-      unsafeAtomicAdd(dst + 1, v.y);
-      unsafeAtomicAdd(dst + 2, v.z);
-      unsafeAtomicAdd(dst + 3, v.w);
+    const int32_t* ri = row_idx + tok * n_tables;
+    for (int j = 0; j < n_tables; ++j) {
+      float* dst = g.p[j] + (int64_t)ri[j] * row_dim;
+      const float* sj = src + (int64_t)j * row_dim;
+      for (int c = lane; c < row_dim; c += 64) unsafeAtomicAdd(dst + c, sj[c]);
     }
   }
 }
@@ -353,18 +369,22 @@ unsigned grid_of(int64_t work, int64_t cap) {
 
 }  // namespace
 
-hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_rows(const BwdArgs& a, float* d_conv_w, float* d_gammas,
+                           float* reduce_tmp, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   const int items = (a.d + 1023) / 1024;
   hipError_t e;
-  const unsigned g1 = grid_of(a.n, 4096), g2 = grid_of(a.n * a.nb, 2048), g3 = grid_of(a.n, 2048);
-#define NGRAM_BWD_ITEMS(I)                                                  \
-  case I:                                                                   \
-    e = launch(bwd_stats_kernel<I>, g1, 256, 0, s, a);                      \
-    if (e != hipSuccess) return e;                                          \
-    e = launch(bwd_conv_kernel<I>, g2, 256, 0, s, a);                       \
-    if (e != hipSuccess) return e;                                          \
-    return launch(bwd_main_kernel<I>, g3, 256, 0, s, a);
+  const unsigned g1 = grid_of(a.n, 4096), g2 = grid_of(a.n * a.nb, kBwdBlocks),
+                 g3 = grid_of(a.n, kBwdBlocks);
+#define NGRAM_BWD_ITEMS(I)                                                        \
+  case I:                                                                         \
+    e = launch(bwd_stats_kernel<I>, g1, 256, 0, s, a);                            \
+    if (e != hipSuccess) return e;                                                \
+    e = launch(bwd_conv_kernel<I>, g2, 256, 0, s, a);                             \
+    if (e != hipSuccess) return e;                                                \
+    e = a.nb == 1 ? launch(bwd_main_kernel<I, true>, g3, 256, 0, s, a)            \
+                  : launch(bwd_main_kernel<I, false>, g3, 256, 0, s, a);          \
+    break;
   switch (items) {
     NGRAM_BWD_ITEMS(1)
     NGRAM_BWD_ITEMS(2)
@@ -373,13 +393,26 @@ hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef NGRAM_BWD_ITEMS
+  if (e != hipSuccess) return e;
+  // column sums of the per-block partial rows, in two passes of <= 32 rows
+  auto col_sum = [&](const float* part, int64_t rows, int64_t cols, float* out) {
+    const unsigned gx = (unsigned)((cols + 255) / 256);
+    const int64_t mid = (rows + 31) / 32;
+    hipError_t r = launch(sum_rows_kernel, dim3(gx, (unsigned)mid), 256, 0, s, part, rows, cols,
+                          32, reduce_tmp);
+    if (r != hipSuccess) return r;
+    return launch(sum_rows_kernel, dim3(gx, 1), 256, 0, s, (const float*)reduce_tmp, mid, cols,
+                  (int)mid, out);
+  };
+  e = col_sum(a.part_conv, g2, 4 * (int64_t)a.d, d_conv_w);
+  if (e != hipSuccess || d_gammas == nullptr) return e;
+  return col_sum(a.part_gain, g3, 3 * (int64_t)a.d, d_gammas);
 }
 
 hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
                               int32_t row_dim, const float* d_e, const GradTablePtrs& g,
                               hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
-  if (row_dim % 4 != 0) return hipErrorInvalidValue;
   return launch(scatter_add_kernel, grid_of((n_tok + 3) / 4, 65536), 256, 0, s, row_idx, n_tok,
                 n_tables, row_dim, d_e, g);
 }

@@ -230,7 +230,7 @@ struct BwdArgs {
   int64_t h_tok, h_br;
   const float* kv;                  // recomputed [n, kv_ld]: K of each branch, then V (fp32)
   int64_t kv_ld;
-  float* stats;                     // [n, nb, 4]: g, 1/rho_h, 1/rho_k, 1/r
+  float* stats;                     // [n, nb, kStatsStride]: g, 1/rho_h, 1/rho_k, 1/r, P
   float* dc;                        // [n, nb, d]: dC
   const bf16_bits* d_out;           // [n, nb, d]
   const bf16_bits* conv_w;          // [4, d]
@@ -242,12 +242,18 @@ struct BwdArgs {
   bf16_bits* dkv;                   // [n, dkv_ld]: dK of each branch, then dV (bf16)
   int64_t dkv_ld;
   float* d_hidden;                  // hidden's layout, fp32, nullable
-  float* d_conv_w;                  // [4, d], accumulated (zeroed by the caller)
-  float* d_gammas;                  // [3, d] q, k, u, accumulated, nullable
+  float* part_conv;                 // [kBwdBlocks, 4, d]: per-block partial d_conv_w
+  float* part_gain;                 // [kBwdBlocks, 3, d]: per-block partial d_gammas, nullable
 };
 
-// stats, dC + d_conv_w, then dK / dV / d_hidden / d_gammas (d <= 4096)
-hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s);
+constexpr int kStatsStride = 8;     // floats per (token, branch) stats row
+constexpr int kBwdBlocks = 1024;    // grid cap of the per-row backward kernels
+
+// stats, dC, then dK / dV / d_hidden; d_conv_w [4, d] and d_gammas [3, d]
+// (nullable) written from the per-block partials by a two-pass column sum
+// through reduce_tmp [32, 4 d] (d <= 4096)
+hipError_t launch_bwd_rows(const BwdArgs& a, float* d_conv_w, float* d_gammas,
+                           float* reduce_tmp, hipStream_t s);
 hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
                               int32_t row_dim, const float* d_e, const GradTablePtrs& g,
                               hipStream_t s);
