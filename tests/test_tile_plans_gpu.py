@@ -105,11 +105,26 @@ def test_decode_path_plans(orc, decode_env, name, batch):
     """One new token per sequence (T = 1): hash+gather, the weight-stationary
     projection and the decode finalize, with a populated conv state, the
     residual flag and random RMSNorm gains (300 rows: two ragged passes)."""
+    print(f"[decode plan {decode_env}] {name} batch {batch}", flush=True)
+    _decode_case(orc, name, batch)
+
+
+def test_decode_invalid_ids_are_pad(orc):
+    """Ids outside the vocabulary, in the new tokens and in the history, hash
+    as the pad id and set the error flag."""
+    print("[decode invalid ids]", flush=True)
+    _decode_case(orc, "qwen_decode", 300, bad_ids=True)
+
+
+def _decode_case(orc, name, batch, bad_ids=False):
     H = G.H()
     w = W.get(name).replace(batch=batch, seq_len=1, history_len=2)
-    print(f"[decode plan {decode_env}] {name} batch {batch}", flush=True)
     cfg = G.config(w, "d_mem")
     ids, hist = W.make_ids(w)
+    if bad_ids:
+        ids[3, 0], ids[290, 0] = -5, w.vocab + 11
+        hist[7, 1], hist[260, 0] = w.vocab, -1
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
     wk, wv = G.weights(w, "d_mem")
     nb, d, halo = w.n_branches, w.hidden, 3 * w.max_order
     hidden = SD.make_hidden(w, ids.size)
@@ -121,8 +136,9 @@ def test_decode_path_plans(orc, decode_env, name, batch):
                     G.tables(w), hidden, 0 if nb == 1 else d, wk, wv, G.conv_w(w), out,
                     history=torch.from_numpy(hist).cuda(), gamma_q=gam["q"], gamma_k=gam["k"],
                     gamma_u=gam["u"], conv_state=torch.from_numpy(state).cuda(), flags=1,
-                    gates=gates)
+                    gates=gates, err_flag=err)
     torch.cuda.synchronize()
+    assert err.item() == (1 if bad_ids else 0)
     wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
     gh = {k: G.to_storage(v) for k, v in gam.items()}
     ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
