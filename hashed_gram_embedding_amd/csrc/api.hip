@@ -237,9 +237,29 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 // (bf16), the weights transposed, dE (fp32), and dK / dV and E transposed
 // over tokens padded to a multiple of 64.
 struct BwdLayout {
-  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, total;
+  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, dw, total;
   int64_t n_pad;
+  int32_t dw_split;  // K splits of the dW product
 };
+
+// K splits of the dW product [(nb+1) d, mem] over n_pad tokens on the
+// 256 x 256 tile plan (one workgroup per CU): the count in 1..8 that
+// minimises the launch's rounds of 256 workgroups per unit of work, the
+// smaller count on ties, keeping at least 16 K steps per split.
+int32_t dw_split_for(int64_t rows, int64_t cols, int64_t n_pad) {
+  const int64_t tiles = ((rows + 255) / 256) * ((cols + 255) / 256);
+  int32_t best = 1;
+  double best_cost = 0.0;
+  for (int32_t sp = 1; sp <= 8; ++sp) {
+    if (n_pad / 64 / sp < 16) break;
+    const double cost = (double)((tiles * sp + kWstatCus - 1) / kWstatCus) / sp;
+    if (sp == 1 || cost < best_cost - 1e-9) {
+      best = sp;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
   BwdLayout L;
@@ -263,6 +283,8 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
   L.et = take((size_t)mem * L.n_pad * 2);
   L.part = take((size_t)kBwdBlocks * 7 * d * 4);
   L.rtmp = take((size_t)32 * 4 * d * 4);
+  L.dw_split = dw_split_for(N, mem, L.n_pad);
+  L.dw = take((size_t)L.dw_split * N * mem * 4);
   L.total = off;
   return L;
 }
@@ -271,7 +293,7 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
 // then dd rows from wv, all [., K] bf16) on the MFMA projection kernel.
 hipError_t raw_gemm(const bf16_bits* A, int64_t M, int32_t K, const bf16_bits* wk,
                     const bf16_bits* wv, int32_t nb, int32_t dd, float* C, int64_t ldc,
-                    hipStream_t s) {
+                    hipStream_t s, int32_t split = 1) {
   AsyncProjArgs a;
   memset(&a, 0, sizeof a);
   a.e = A;
@@ -284,7 +306,10 @@ hipError_t raw_gemm(const bf16_bits* A, int64_t M, int32_t K, const bf16_bits* w
   a.group_m = 4;
   a.raw_out = C;
   a.raw_ld = ldc;
-  return launch_projection_raw(M >= 8192 ? 7 : M >= 1024 ? 8 : 2, a, s);
+  a.raw_split = split;
+  a.raw_split_stride = M * ldc;
+  // split-K products run on the 256 x 256 plan, whose tile count the split was chosen for
+  return launch_projection_raw(split > 1 || M >= 8192 ? 7 : M >= 1024 ? 8 : 2, a, s);
 }
 
 // Benchmark instrumentation (ngram_set_timing_events): stage(i) closes the
@@ -793,10 +818,14 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
   if (st) return st;
   st = hip_status(launch_transpose_bf16(e, n, mem, mem, et, L.n_pad, L.n_pad, s));
   if (st) return st;
-  st = hip_status(raw_gemm(dkvt, (int64_t)nb * d, (int32_t)L.n_pad, nullptr, et, 0, mem, d_w_k, mem, s));
+  // one split-K product for every row of [dK dV]^T, the splits summed into d_w_k and d_w_v
+  float* dw = reinterpret_cast<float*>(ws + L.dw);
+  st = hip_status(raw_gemm(dkvt, N, (int32_t)L.n_pad, nullptr, et, 0, mem, dw, mem, s, L.dw_split));
   if (st) return st;
-  st = hip_status(raw_gemm(dkvt + (int64_t)nb * d * L.n_pad, d, (int32_t)L.n_pad, nullptr, et, 0,
-                           mem, d_w_v, mem, s));
+  const int64_t kw = (int64_t)nb * d * mem;
+  st = hip_status(launch_sum_splits(dw, L.dw_split, N * mem, kw, d_w_k, s));
+  if (st) return st;
+  st = hip_status(launch_sum_splits(dw + kw, L.dw_split, N * mem, (int64_t)d * mem, d_w_v, s));
   if (st) return st;
   // the gather's adjoint
   return hip_status(launch_scatter_add(row_idx, n, cfg->n_tables, cfg->row_dim, de, gp, s));

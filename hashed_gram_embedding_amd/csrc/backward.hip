@@ -336,6 +336,19 @@ __global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t* __restr
   }
 }
 
+// out[i] = sum_s part[s * stride + i] over the split-K partial products,
+// four floats per thread, the splits added in order.
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part,
+                                                         int32_t split, int64_t stride, int64_t n4,
+                                                         float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    float4 x = ld4(part + 4 * i);
+    for (int sp = 1; sp < split; ++sp) x = add(x, ld4(part + sp * stride + 4 * i));
+    st4(out + 4 * i, x);
+  }
+}
+
 // bf16 [rows, cols] (row stride ld_src) -> [cols, rows_pad] (row stride
 // ld_dst), rows rows..rows_pad-1 of the result zero; 64 x 64 tiles via LDS.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_bits* __restrict__ src,
@@ -415,6 +428,14 @@ hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_t
   if (n_tok == 0) return hipSuccess;
   return launch(scatter_add_kernel, grid_of((n_tok + 3) / 4, 65536), 256, 0, s, row_idx, n_tok,
                 n_tables, row_dim, d_e, g);
+}
+
+hipError_t launch_sum_splits(const float* part, int32_t split, int64_t stride, int64_t n,
+                             float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 4 != 0 || stride % 4 != 0 || split < 1) return hipErrorInvalidValue;
+  return launch(sum_splits_kernel, grid_of((n / 4 + 255) / 256, 8192), 256, 0, s, part, split,
+                stride, n / 4, out);
 }
 
 hipError_t launch_transpose_bf16(const bf16_bits* src, int64_t rows, int64_t cols, int64_t ld_src,

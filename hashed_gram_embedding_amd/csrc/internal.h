@@ -153,9 +153,14 @@ struct AsyncProjArgs {
   EpiArgs epi;
   int32_t K, tiles_m, tiles_n, group_m;
   // launch_projection_raw: C[M, (nb+1)*d] = A B^T written in fp32 to
-  // raw_out[row * raw_ld + seg * d + col] instead of the gate epilogue
+  // raw_out[row * raw_ld + seg * d + col] instead of the gate epilogue.
+  // raw_split > 1 splits the K steps over that many workgroups per tile
+  // (split-major block order, ragged), split s writing its partial product
+  // at raw_out + s * raw_split_stride.
   float* raw_out;
   int64_t raw_ld;
+  int32_t raw_split;
+  int64_t raw_split_stride;
 };
 
 // Gate + gated value + conv block over a [B, T] token grid.
@@ -257,6 +262,9 @@ hipError_t launch_bwd_rows(const BwdArgs& a, float* d_conv_w, float* d_gammas,
 hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
                               int32_t row_dim, const float* d_e, const GradTablePtrs& g,
                               hipStream_t s);
+// out[i] = sum_{s < split} part[s * stride + i], i < n (fp32, in split order)
+hipError_t launch_sum_splits(const float* part, int32_t split, int64_t stride, int64_t n,
+                             float* out, hipStream_t s);
 hipError_t launch_transpose_bf16(const bf16_bits* src, int64_t rows, int64_t cols, int64_t ld_src,
                                  bf16_bits* dst, int64_t rows_pad, int64_t ld_dst, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);

@@ -127,8 +127,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   const int wm = wave / WGN, wn = wave % WGN;
   const EpiArgs& ep = a.epi;
   const int n_seg = ep.nb + 1;
+  // RAW split-K: blocks [s * tiles, (s + 1) * tiles) take K split s
+  const int split = RAW && a.raw_split > 1 ? a.raw_split : 1;
+  const int tiles = a.tiles_m * n_seg * a.tiles_n;
+  const int ksl = split > 1 ? (int)blockIdx.x / tiles : 0;
+  const int bid = split > 1 ? (int)blockIdx.x - ksl * tiles : (int)blockIdx.x;
   int m_tile, seg, n_tile;
-  map_tile(blockIdx.x, a.tiles_m, n_seg, a.tiles_n, a.group_m, m_tile, seg, n_tile);
+  map_tile(bid, a.tiles_m, n_seg, a.tiles_n, a.group_m, m_tile, seg, n_tile);
   const int64_t M = ep.M;
   const int64_t m0 = (int64_t)m_tile * BM;
   const int n0 = n_tile * BN;
@@ -153,6 +158,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   }
 
 
+  const int kt_first = split > 1 ? ksl * (K / BK) / split : 0;
+
   // Copy lanes: lane -> (row lrow of the copy's RPI-row block, 16-byte chunk
   // pch of the LDS row).  A block starts at a multiple of RPI rows, so the
   // row's swizzle is that of lrow, XOR the block's part (swz_block).
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   auto issue = [&](int kt, int sl) {
     bf16_bits* As = slot(sl);
     bf16_bits* Bs = As + A_ELEMS;
-    const int k0 = kt * BK;
+    const int k0 = (kt_first + kt) * BK;
     int j = 0, cofs = 0;
     const bf16_bits* tab = nullptr;
     if (GATHER) {
@@ -234,7 +241,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     }
   };
 
-  const int nk = K / BK;
+  // this block's K steps: [kt_first, kt_first + nk) of K / BK
+  const int nk = split > 1 ? (ksl + 1) * (K / BK) / split - kt_first : K / BK;
   // The last slot first receives a throw-away copy of step 0 (overwritten
   // before it is read), so that on entry to the loop every slot has one copy
   // outstanding in the same order as at the loop's back edge; the compiler's
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   if (RAW) {
     // plain product in fp32: a half-wave stores 32 consecutive columns (128
     // bytes) of one row per register
-    float* __restrict__ C = a.raw_out + (int64_t)seg * d;
+    float* __restrict__ C = a.raw_out + ksl * a.raw_split_stride + (int64_t)seg * d;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -292,7 +300,10 @@ hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
   if (a.raw_out == nullptr || a.K % BK != 0) return hipErrorInvalidValue;
   a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
   a.tiles_n = (a.epi.d + BN - 1) / BN;
-  const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
+  const int split = a.raw_split > 1 ? a.raw_split : 1;
+  if (split > a.K / BK) return hipErrorInvalidValue;  // every split needs a K step
+  const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n * split;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>, (unsigned)blocks,
                 64 * WGM * WGN, 0, s, a);
 }

@@ -113,6 +113,16 @@ def test_backward_qwen_dims(orc):
     _case(orc, w, 1, False, True, True, seed=5)
 
 
+@pytest.mark.parametrize("nb", [1, 2])
+def test_backward_split_k_weight_gradients(orc, nb):
+    """4,500 tokens (71 K steps of 64 after padding): the dW product splits
+    its K steps over 4 workgroups per tile, raggedly (17/18/18/18), and the
+    summed splits land in d_w_k and d_w_v on either side of the boundary."""
+    w = SMALL.replace(batch=3, seq_len=1500, n_branches=nb)
+    print(f"[backward] split-K dW, 3 x 1500 tokens, nb={nb}", flush=True)
+    _case(orc, w, 1, False, True, True, seed=20 + nb)
+
+
 def test_backward_single_token_sequences_and_ragged(orc):
     """T = 1 (every conv tap outside the sequence) and a ragged token count."""
     w = SMALL.replace(batch=37, seq_len=1, history_len=2)
