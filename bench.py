@@ -333,15 +333,20 @@ def main():
     torch.cuda._sleep(int(min(0.2, 3e-4 * args.stage_steps) * 2.5e9))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)]
            for _ in range(args.stage_steps)]
-    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.stage_steps)]
     for i in range(args.stage_steps):
         setup.H.ngram.ngram_set_timing_events(evs[i])
+        setup.step(i % setup.pool)
+    mask = setup.H.ngram.ngram_timing_stage_mask()
+    setup.H.ngram.ngram_set_timing_events(None)
+    torch.cuda.synchronize()
+    # per-step distribution: one plain event pair around each step, no stage hook
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.stage_steps)]
+    torch.cuda._sleep(int(min(0.2, 3e-4 * args.stage_steps) * 2.5e9))
+    for i in range(args.stage_steps):
         step_evs[i][0].record(stream)
         setup.step(i % setup.pool)
         step_evs[i][1].record(stream)
-    mask = setup.H.ngram.ngram_timing_stage_mask()
-    setup.H.ngram.ngram_set_timing_events(None)
     torch.cuda.synchronize()
     names = setup.H.ngram.STAGE_NAMES
     stage_avg = {}
