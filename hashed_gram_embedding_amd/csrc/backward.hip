@@ -351,21 +351,43 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
 
 // bf16 [rows, cols] (row stride ld_src) -> [cols, rows_pad] (row stride
 // ld_dst), rows rows..rows_pad-1 of the result zero; 64 x 64 tiles via LDS.
+// A thread reads 8 consecutive columns of a source row and writes 8
+// consecutive entries of a result row (8 source rows of one column, gathered
+// from the tile), both as 16-byte accesses: rows 16-byte aligned on both
+// sides, rows_pad a multiple of 64; columns may be ragged.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_bits* __restrict__ src,
-                                                             int64_t rows, int64_t cols,
-                                                             int64_t ld_src, bf16_bits* __restrict__ dst,
-                                                             int64_t rows_pad, int64_t ld_dst) {
-  __shared__ bf16_bits tile[64][66];
+                                                                 int64_t rows, int64_t cols,
+                                                                 int64_t ld_src,
+                                                                 bf16_bits* __restrict__ dst,
+                                                                 int64_t ld_dst) {
+  __shared__ __attribute__((aligned(16))) bf16_bits tile[64][72];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? src[r * ld_src + c] : (bf16_bits)0;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, cc = (i & 7) * 8;
+    const int64_t gr = r0 + r, gc = c0 + cc;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (gr < rows) {
+      const bf16_bits* sp = src + gr * ld_src + gc;
+      if (gc + 8 <= cols) {
+        v = *reinterpret_cast<const uint4*>(sp);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8 && gc + e < cols; ++e) w[e >> 1] |= (uint32_t)sp[e] << (16 * (e & 1));
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[r][cc]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows_pad) dst[c * ld_dst + r] = tile[tx][i];
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = i >> 3, rr = (i & 7) * 8;
+    const int64_t gc = c0 + c;
+    if (gc >= cols) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)tile[rr + 2 * k][c] | ((uint32_t)tile[rr + 2 * k + 1][c] << 16);
+    *reinterpret_cast<uint4*>(dst + gc * ld_dst + r0 + rr) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -442,8 +464,10 @@ hipError_t launch_transpose_bf16(const bf16_bits* src, int64_t rows, int64_t col
                                  bf16_bits* dst, int64_t rows_pad, int64_t ld_dst, hipStream_t s) {
   if (rows_pad == 0 || cols == 0) return hipSuccess;
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
-  return launch(transpose_bf16_kernel, grid, 256, 0, s, src, rows, cols, ld_src, dst, rows_pad,
-                ld_dst);
+  if (ld_src % 8 != 0 || ld_dst % 8 != 0 || rows_pad % 64 != 0 ||
+      reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return hipErrorInvalidValue;
+  return launch(transpose_bf16_kernel, grid, 256, 0, s, src, rows, cols, ld_src, dst, ld_dst);
 }
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
