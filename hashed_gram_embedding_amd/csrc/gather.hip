@@ -82,7 +82,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 // E is written in the decode projection's operand order (internal.h,
 // "decode E tiles"), so that kernel reads each 16-row x 32-k operand of
 // v_mfma_f32_16x16x32_bf16 as one contiguous kilobyte.
-template <bool FP8>
+//
+// WPT waves share one token (a few hundred tokens cannot otherwise occupy
+// every CU): each hashes all of the token's tables and fetches 1 / WPT of its
+// chunks.
+template <bool FP8, int WPT>
 __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restrict__ ids,
                                                           int32_t B, int32_t T,
                                                           const int32_t* __restrict__ hist,
@@ -99,15 +103,18 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int waves_per_block = blockDim.x >> 6;
+  constexpr int tok_per_block = 4 / WPT;
+  const int part = (threadIdx.x >> 6) % WPT;
   const int64_t n_tok = (int64_t)B * T;
-  const int64_t wstride = (int64_t)gridDim.x * waves_per_block;
+  const int64_t tstride = (int64_t)gridDim.x * tok_per_block;
   const int32_t chunks = h.n_tables * row_chunks;  // table chunks per token
+  const int32_t per = (chunks + WPT - 1) / WPT;
+  const int32_t q0 = part * per, q1 = q0 + per < chunks ? q0 + per : chunks;
   const int jl = lane < h.n_tables ? lane : 0;
   const int order_l = h.orders[jl / h.heads];
   const int32_t n_kk = chunks * (FP8 ? 2 : 1) >> 2;  // 32-wide K steps per token
-  for (int64_t tok = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6); tok < n_tok;
-       tok += wstride) {
+  for (int64_t tok = (int64_t)blockIdx.x * tok_per_block + (threadIdx.x >> 6) / WPT; tok < n_tok;
+       tok += tstride) {
     const int32_t b = (int32_t)(tok / T);
     const int32_t t = (int32_t)(tok - (int64_t)b * T);
     uint64_t c[NGRAM_MAX_ORDER];
@@ -116,19 +123,19 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
     uint4* dst = mem + (tok >> 4) * n_kk * 64 + (tok & 15);
     // E chunk e (16 bytes, 8 bf16): K step e/4, quarter e%4
     auto put = [&](int e, const uint4& x) { dst[(e >> 2) * 64 + (e & 3) * 16] = x; };
-    for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
+    for (int base = q0; base < q1; base += 64 * kGatherUnroll) {
       uint4 v[kGatherUnroll];
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
         const int q = base + u * 64 + lane;
         const int j = q / row_chunks;
         const int64_t r = __shfl(my_row, j < h.n_tables ? j : 0);
-        if (q < chunks) v[u] = s_tab[j][r * row_chunks + (q - j * row_chunks)];
+        if (q < q1) v[u] = s_tab[j][r * row_chunks + (q - j * row_chunks)];
       }
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
         const int q = base + u * 64 + lane;
-        if (q < chunks) {
+        if (q < q1) {
           if (FP8) {
             uint4 lo, hi;
             fp8x16_to_bf16(v[u], s_scale[q / row_chunks], lo, hi);
@@ -155,14 +162,27 @@ hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t 
   const bool fp8 = dtype == NGRAM_FP8_E4M3;
   const int32_t row_chunks = row_dim * (fp8 ? 1 : 2) / 16;
   const int64_t n_tok = (int64_t)B * T;
-  int64_t blocks = (n_tok + 3) / 4;
+  // waves per token: enough to put work on every CU for the decode batch
+  // (one wave per token left three quarters of the CUs idle at 256 tokens;
+  // 5 or 8 waves per token measured no better than 4)
+  const int wpt = n_tok <= 1024 ? 4 : n_tok <= 2048 ? 2 : 1;
+  int64_t blocks = (n_tok * wpt + 3) / 4;
   if (blocks > 262144) blocks = 262144;
   if (blocks < 1) blocks = 1;
-  if (fp8)
-    return launch(hash_gather_kernel<true>, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h,
-                  row_chunks, t, static_cast<uint4*>(mem), err);
-  return launch(hash_gather_kernel<false>, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h,
-                row_chunks, t, static_cast<uint4*>(mem), err);
+  uint4* m = static_cast<uint4*>(mem);
+#define NGRAM_HG(F, W)                                                                     \
+  return launch(hash_gather_kernel<F, W>, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h, \
+                row_chunks, t, m, err)
+#define NGRAM_HG_W(F)       \
+  switch (wpt) {            \
+    case 4: NGRAM_HG(F, 4); \
+    case 2: NGRAM_HG(F, 2); \
+    default: NGRAM_HG(F, 1); \
+  }
+  if (fp8) NGRAM_HG_W(true);
+  NGRAM_HG_W(false);
+#undef NGRAM_HG_W
+#undef NGRAM_HG
 }
 
 hipError_t launch_gather(int dtype, const int32_t* row_idx, int64_t n_tok, int32_t n_tables,

@@ -109,6 +109,13 @@ def test_decode_path_plans(orc, decode_env, name, batch):
     _decode_case(orc, name, batch)
 
 
+def test_decode_1100_sequences(orc):
+    """More than 1,024 sequences: the hash+gather kernel splits each token
+    over two waves instead of four, and the projection makes several passes."""
+    print("[decode] 1100 sequences", flush=True)
+    _decode_case(orc, "qwen_decode", 1100)
+
+
 def test_decode_invalid_ids_are_pad(orc):
     """Ids outside the vocabulary, in the new tokens and in the history, hash
     as the pad id and set the error flag."""
