@@ -27,6 +27,8 @@ namespace {
 constexpr int kMaxTile = 64;
 constexpr int kMaxHalo = 3 * NGRAM_MAX_ORDER;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float4 f4(float x) { return make_float4(x, x, x, x); }
 __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
   return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
@@ -352,15 +354,19 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
     ok[i] = c < d;
     col[i] = ok[i] ? c : d - 4;
   }
+  // the partials are read once: streamed, so that they do not evict the
+  // weights the next decode step's projection reads from L2
+  auto ld_stream = [](const float* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  };
   auto splits = [&](int64_t off) {  // sum of the K slices, 4 columns, in slice order
-    float4 x = *reinterpret_cast<const float4*>(P + off);
+    float4 x = ld_stream(P + off);
     if (KS > 0) {
 #pragma unroll
-      for (int s = 1; s < KS; ++s)
-        x = add4(x, *reinterpret_cast<const float4*>(P + s * sstride + off));
+      for (int s = 1; s < KS; ++s) x = add4(x, ld_stream(P + s * sstride + off));
     } else {
-      for (int s = 1; s < k_split; ++s)
-        x = add4(x, *reinterpret_cast<const float4*>(P + s * sstride + off));
+      for (int s = 1; s < k_split; ++s) x = add4(x, ld_stream(P + s * sstride + off));
     }
     return x;
   };

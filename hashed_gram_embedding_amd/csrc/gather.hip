@@ -17,6 +17,8 @@
 namespace ngram {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kGatherUnroll = 8;
 
 // FP8 tables: a source chunk holds 16 values and becomes two bf16 chunks of E
@@ -130,7 +132,11 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
         const int q = base + u * 64 + lane;
         const int j = q / row_chunks;
         const int64_t r = __shfl(my_row, j < h.n_tables ? j : 0);
-        if (q < q1) v[u] = s_tab[j][r * row_chunks + (q - j * row_chunks)];
+        if (q < q1) {  // random rows, read once: streamed past the caches
+          const u32x4 x = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(s_tab[j] + r * row_chunks + (q - j * row_chunks)));
+          v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {

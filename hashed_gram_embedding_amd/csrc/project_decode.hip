@@ -154,7 +154,9 @@ __global__ __launch_bounds__(64 * kWstatWaves, 1) void proj_wstat_kernel(WstatAr
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) {
             const int col = n0 + ni * 16 + r16;
-            if (col < N) P[row * N + col] = acc[mi][ni][r];
+            // streamed: the partials are read once, by the finalize, and
+            // should not evict the weights, which the next step reads again
+            if (col < N) __builtin_nontemporal_store(acc[mi][ni][r], &P[row * N + col]);
           }
         }
       }
