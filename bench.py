@@ -166,13 +166,16 @@ STAGE_SOURCES = {
 
 def route(w) -> str:
     """Kernel route of a workload's forward: fp32; decode (one new token per
-    sequence); fused (the projection gathers bf16 rows itself); materialised
-    (hash, gather to E, then the projection: fp8 tables, rows not 64-wide)."""
+    sequence); materialised (hash, gather to E, then the projection: the
+    default); fused (the projection gathers bf16 rows itself, with
+    NGRAM_FUSED_GATHER=1 and 64-wide rows)."""
     if w.dtype == "f32":
         return "f32"
     if w.seq_len == 1:
         return "decode"
-    return "materialised" if w.tdtype == "fp8" or w.row_dim % 64 else "fused"
+    fused = (os.environ.get("NGRAM_FUSED_GATHER") == "1" and w.tdtype == "bf16"
+             and w.row_dim % 64 == 0)
+    return "fused" if fused else "materialised"
 
 
 def stage_source_sha(stage: str, w):

@@ -120,7 +120,7 @@ __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], con
             const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
             if (row < M) {
               const float v = acc[mi][ni][r];
-              V[row * d + col] = v;
+              __builtin_nontemporal_store(v, &V[row * d + col]);  // read once, by the conv
               xv[r] += v * v;
             }
           }

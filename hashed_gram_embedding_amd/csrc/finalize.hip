@@ -190,7 +190,9 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
           float4 src = f4(0.0f), nq = f4(0.0f);
           if (q >= 0) {
             if (FUSED) {
-              src = *reinterpret_cast<const float4*>(a.v + (seq0 + q) * a.v_stride + c0);
+              const f32x4 x = __builtin_nontemporal_load(
+                  reinterpret_cast<const f32x4*>(a.v + (seq0 + q) * a.v_stride + c0));
+              src = make_float4(x[0], x[1], x[2], x[3]);
             } else {
               src = Elem<T>::load4(static_cast<const T*>(a.u), ((seq0 + q) * nb + br) * d + c0);
             }
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
               const float4 h = Elem<T>::load4(H, tok * a.h_tok_stride + br * a.h_branch_stride + c0);
               D = make_float4(D.x + h.x, D.y + h.y, D.z + h.z, D.w + h.w);
             }
-            Elem<T>::store4(OUT, (tok * nb + br) * d + c0, D);
+            Elem<T>::store4_stream(OUT, (tok * nb + br) * d + c0, D);
           }
         }
       }

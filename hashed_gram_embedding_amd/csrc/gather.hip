@@ -19,6 +19,16 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// E is written once and read by the next kernel: streamed past the caches
+__device__ __forceinline__ void nt_store16(uint4* p, const uint4& v) {
+  u32x4 x;
+  x[0] = v.x;
+  x[1] = v.y;
+  x[2] = v.z;
+  x[3] = v.w;
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
+
 constexpr int kGatherUnroll = 8;
 
 // FP8 tables: a source chunk holds 16 values and becomes two bf16 chunks of E
@@ -56,7 +66,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
           const int j = q / row_chunks;
           const int c = q - j * row_chunks;
           const int64_t r = rix[j];
-          v[u] = s_tab[j][r * row_chunks + c];
+          const u32x4 x = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(s_tab[j] + r * row_chunks + c));
+          v[u] = make_uint4(x[0], x[1], x[2], x[3]);
         }
       }
 #pragma unroll
@@ -66,10 +78,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
           if (FP8) {
             uint4 lo, hi;
             fp8x16_to_bf16(v[u], s_scale[q / row_chunks], lo, hi);
-            dst[2 * q] = lo;
-            dst[2 * q + 1] = hi;
+            nt_store16(dst + 2 * q, lo);
+            nt_store16(dst + 2 * q + 1, hi);
           } else {
-            dst[q] = v[u];
+            nt_store16(dst + q, v[u]);
           }
         }
       }

@@ -40,6 +40,15 @@ struct Elem<float> {
   __device__ __forceinline__ static void store4(float* p, int64_t i, float4 v) {
     *reinterpret_cast<float4*>(p + i) = v;
   }
+  __device__ __forceinline__ static void store4_stream(float* p, int64_t i, float4 v) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    f4v x;
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
+    __builtin_nontemporal_store(x, reinterpret_cast<f4v*>(p + i));
+  }
 };
 template <>
 struct Elem<bf16_bits> {
@@ -56,6 +65,13 @@ struct Elem<bf16_bits> {
     r.x = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
     r.y = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
     *reinterpret_cast<uint2*>(p + i) = r;
+  }
+  __device__ __forceinline__ static void store4_stream(bf16_bits* p, int64_t i, float4 v) {
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    u2v r;
+    r[0] = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+    r[1] = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+    __builtin_nontemporal_store(r, reinterpret_cast<u2v*>(p + i));
   }
 };
 

@@ -52,11 +52,28 @@ def test_gate_each_plan(orc, plan_env, n):
     assert G.rel_err(G.to_f64(u), orc.gated_value(g_ref, v)) < G.TOL
 
 
+@pytest.fixture
+def fused_env(request):
+    old = os.environ.get("NGRAM_FUSED_GATHER")
+    if request.param:
+        os.environ["NGRAM_FUSED_GATHER"] = "1"
+    else:
+        os.environ.pop("NGRAM_FUSED_GATHER", None)
+    yield request.param
+    if old is None:
+        os.environ.pop("NGRAM_FUSED_GATHER", None)
+    else:
+        os.environ["NGRAM_FUSED_GATHER"] = old
+
+
+@pytest.mark.parametrize("fused_env", [False, True], indirect=True, ids=["materialised", "fused"])
 @pytest.mark.parametrize("plan_env", PLANS, indirect=True)
-def test_forward_each_plan(orc, plan_env):
+def test_forward_each_plan(orc, plan_env, fused_env):
+    """Every tile plan on both forward routes: E materialised by the gather
+    kernel, or gathered by the projection itself."""
     H = G.H()
     w = W.get("qwen_prefill").replace(batch=3, seq_len=1100)
-    print(f"[plan {plan_env}] forward", flush=True)
+    print(f"[plan {plan_env}] forward, fused gather {fused_env}", flush=True)
     cfg = G.config(w, "d_mem")
     ids, _ = W.make_ids(w)
     wk, wv = G.weights(w, "d_mem")
@@ -160,9 +177,10 @@ def _decode_case(orc, name, batch, bad_ids=False):
     assert G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"]) < G.TOL
 
 
-def test_single_token_large_batch_takes_fused_route(orc):
-    """T = 1 with more sequences than the decode route serves: the fused
-    route (per-token tiles with history) gives the same result."""
+def test_single_token_large_batch_takes_prefill_route(orc):
+    """T = 1 with more sequences than the decode route serves: the prefill
+    route (hash with history, gather, projection, conv) gives the same
+    result."""
     w = W.get("engram_small").replace(batch=2100, seq_len=1, history_len=2, heads=2,
                                       hidden=128)
     print("[single token, 2100 sequences]", flush=True)
