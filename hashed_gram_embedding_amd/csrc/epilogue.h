@@ -53,16 +53,16 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
 
 // seg < nb: key projection of branch seg; seg == nb: value projection.
 // The wave owns rows [wrow0, wrow0 + 32*MI) and columns [wcol0, wcol0 + 32*NI),
-// its partial index is pidx.
-template <int MI, int NI>
+// its partial index is pidx.  hread(row, col) returns the query element of
+// branch seg (a copy staged in LDS, or the hidden state itself).
+template <int MI, int NI, class HRead>
 __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], const EpiArgs& a,
                                               int seg, int64_t wrow0, int wcol0, int pidx,
-                                              int lane) {
+                                              int lane, HRead&& hread) {
   const int d = a.d;
   const int64_t M = a.M;
   const int nq = 3 * a.nb + 1;
   if (seg < a.nb) {
-    const bf16_bits* __restrict__ H = a.hidden + seg * a.h_branch_stride;
     float g[NI];
     bool cv[NI];
 #pragma unroll
@@ -85,7 +85,7 @@ __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], con
         for (int r = 0; r < 16; ++r) {
           const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
           if (cv[ni] && row < M) {
-            const float h = bf16_to_f32(H[row * a.h_tok_stride + col]);
+            const float h = hread(row, col);
             const float k = acc[mi][ni][r];
             xd[r] += g[ni] * h * k;
             xk[r] += k * k;
@@ -131,6 +131,16 @@ __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], con
       if (!(lane & 1) && row < M) a.parts[(row * nq + 3 * a.nb) * a.np + pidx] = sv;
     }
   }
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], const EpiArgs& a,
+                                              int seg, int64_t wrow0, int wcol0, int pidx,
+                                              int lane) {
+  const bf16_bits* __restrict__ H = a.hidden + seg * a.h_branch_stride;
+  const int64_t ht = a.h_tok_stride;
+  gate_epilogue<MI, NI>(acc, a, seg, wrow0, wcol0, pidx, lane,
+                        [&](int64_t row, int col) { return bf16_to_f32(H[row * ht + col]); });
 }
 
 // 64-bit key mod a prime p < 2^31 with magic = floor(2^64 / p): the quotient

@@ -120,7 +120,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   __shared__ int32_t s_rid[GATHER ? BM * NGRAM_MAX_TABLES : 1];
   // slot index is a compile-time constant at every use (unrolled loops)
   auto slot = [&](int sl) -> bf16_bits* {
-    return sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : ring3;
+    // (the placeholder arrays of absent slots stay unreferenced)
+    if (STAGES > 3 && sl == 3) return ring3;
+    if (STAGES > 2 && sl == 2) return ring2;
+    return sl == 1 ? ring1 : ring0;
   };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -270,6 +273,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     }
   }
 
+  // Key tiles: the tile's query rows [m0, m0 + BM) x [n0, n0 + BN) go to LDS
+  // (the ring is free now) with one 16-byte copy per lane, so the epilogue
+  // reads them there instead of with one 2-byte global load per element.
+  // Rows are split over the ring slots, RPS rows per slot.
+  constexpr int RPS = (BM + BN) * BK / BN;      // query rows per ring slot
+  constexpr int HCH = BN / 8;                   // 16-byte chunks per query row
+  constexpr int HRPI = 64 / HCH;                // rows per wave-wide copy
+  constexpr int HINS = BM / HRPI / NW;          // copies per wave
+  constexpr bool HSTAGE = !RAW && HCH <= 64 && HRPI * HCH == 64 && RPS % 32 == 0 &&
+                          RPS % HRPI == 0 && (BM + RPS - 1) / RPS <= STAGES &&
+                          HINS * HRPI * NW == BM;
+  if (HSTAGE && seg < ep.nb) {
+    __syncthreads();  // every wave is done reading the ring
+    const bf16_bits* __restrict__ Hs = ep.hidden + seg * ep.h_branch_stride;
+    const int hr = lane / HCH;
+    int hc = n0 + (lane - hr * HCH) * 8;
+    if (hc > d - 8) hc = d - 8;                 // columns past d: never read
+#pragma unroll
+    for (int i = 0; i < HINS; ++i) {
+      const int r0 = (wave * HINS + i) * HRPI;  // first row of the copy
+      int64_t grow = m0 + r0 + hr;
+      if (grow > M - 1) grow = M - 1;           // rows past M: never read
+      copy16_to_lds(Hs + grow * ep.h_tok_stride + hc, slot(r0 / RPS) + (r0 % RPS) * BN);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
   const int wcol0 = n0 + wn * WTN;
   if (wcol0 >= d) return;
   if (RAW) {
@@ -291,7 +322,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
       }
     return;
   }
-  gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+  if (HSTAGE) {
+    gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane,
+                          [&](int64_t row, int col) {
+                            const int rl = (int)(row - m0), cl = col - n0;
+                            return bf16_to_f32(slot(rl / RPS)[(rl % RPS) * BN + cl]);
+                          });
+  } else {
+    gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+  }
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
