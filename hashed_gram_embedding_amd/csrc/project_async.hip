@@ -305,7 +305,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   if (wcol0 >= d) return;
   if (RAW) {
     // plain product in fp32: a half-wave stores 32 consecutive columns (128
-    // bytes) of one row per register
+    // bytes) of one row per register, streamed (the products are larger than
+    // the caches and read by a later kernel)
     float* __restrict__ C = a.raw_out + ksl * a.raw_split_stride + (int64_t)seg * d;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t row = m0 + wm * WTM + mi * 32 + acc_row(r, lane);
-            if (row < M) C[row * a.raw_ld + col] = acc[mi][ni][r];
+            if (row < M) __builtin_nontemporal_store(acc[mi][ni][r], &C[row * a.raw_ld + col]);
           }
         }
       }
