@@ -190,12 +190,17 @@ def test_forward_qwen_prefill(orc, layout):
     assert bool(((gates > 0) & (gates < 1)).all())
 
 
-@pytest.mark.parametrize("name,layout", [("qwen_multibranch_uniform", "d_mem"),
-                                         ("qwen_multibranch_zipf13", "d_mem"),
-                                         ("qwen_multibranch_zipf13", "mem_d")])
-def test_forward_multibranch(orc, name, layout):
+@pytest.mark.parametrize("name,layout,fused", [("qwen_multibranch_uniform", "d_mem", False),
+                                               ("qwen_multibranch_zipf13", "d_mem", False),
+                                               ("qwen_multibranch_zipf13", "mem_d", False),
+                                               ("qwen_multibranch_zipf13", "d_mem", True)])
+def test_forward_multibranch(orc, name, layout, fused, monkeypatch):
+    """Four branches; the last case takes the fused-gather route (the
+    projection hashes and gathers its own operand, four key segments)."""
+    if fused:
+        monkeypatch.setenv("NGRAM_FUSED_GATHER", "1")
     w = W.get(name)
-    print(f"[forward] {name} {layout}", flush=True)
+    print(f"[forward] {name} {layout} fused={fused}", flush=True)
     ids, hist = W.make_ids(w)
     inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
