@@ -393,7 +393,9 @@ int async_plan(int64_t M) {
     const long v = strtol(e, &end, 10);
     if (*end == 0 && v >= 0 && v <= 11) return (int)v;
   }
-  if (M >= 8192) return 7;
+  // 256 x 256 tiles from 8,192 rows: waves as 4 x 2 (64 x 128 each; 1 %
+  // faster than 2 x 4 at Qwen prefill, multibranch and engram sizes)
+  if (M >= 8192) return 11;
   if (M >= 1024) return 8;
   return 2;
 }
