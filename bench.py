@@ -284,7 +284,7 @@ def copy_calibration(nbytes: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: this build measures the single-GPU path "
+        print(f"bench.py measures the single-GPU path only: the layer runs on one GPU "
               f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
         sys.exit(2)
     import torch
