@@ -123,6 +123,14 @@ def test_backward_split_k_weight_gradients(orc, nb):
     _case(orc, w, 1, False, True, True, seed=20 + nb)
 
 
+def test_backward_widest_hidden(orc):
+    """d = 4,096, the widest hidden size the backward takes (four column
+    groups per thread in the per-row kernels)."""
+    w = SMALL.replace(hidden=4096, batch=2, seq_len=70)
+    print("[backward] d=4096, 2 x 70 tokens", flush=True)
+    _case(orc, w, 1, True, True, True, seed=31)
+
+
 def test_backward_single_token_sequences_and_ragged(orc):
     """T = 1 (every conv tap outside the sequence) and a ragged token count."""
     w = SMALL.replace(batch=37, seq_len=1, history_len=2)

@@ -244,6 +244,23 @@ def test_forward_other_order_sets(orc, variant):
                    [(b, 0, w.seq_len) for b in range(w.batch)])
 
 
+@pytest.mark.parametrize("d,T", [(4096, 96), (4096, 1), (4160, 1)])
+def test_forward_wide_hidden(orc, d, T):
+    """The widest hidden sizes the kernels specialise for: d = 4,096 fills the
+    register-resident decode finalize (four column groups per thread) and the
+    prefill conv; d = 4,160 takes the decode finalize that streams columns
+    through L2.  T = 1 with a history is the decode route."""
+    w = W.get("engram_small").replace(hidden=d, heads=2, row_start=10007, batch=3, seq_len=T,
+                                      history_len=2 if T == 1 else 0)
+    print(f"[forward] d={d} T={T}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, random_gamma=True, layout="d_mem")
+    out, gates, err = _run(w, inp, flags=1)
+    assert err == 0
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, T) for b in range(w.batch)],
+                   flags=1)
+
+
 def test_forward_invalid_ids_are_pad(orc):
     w = W.get("tiny").replace(batch=2, seq_len=40)
     ids, hist = W.make_ids(w)
