@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void gate_values_kernel(ConvArgs a, int64_t M)
 }
 
 // FUSED: source is fp32 V + partials (U = g V); else the act-dtype U rows.
-template <int DIL, typename T, bool FUSED>
-__global__ __launch_bounds__(1024) void conv_kernel(ConvArgs a) {
+// RES: the hidden state is added to the output (FUSED only).
+template <int DIL, typename T, bool FUSED, bool RES>
+__global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
   constexpr int HALO = 3 * DIL;
   constexpr int R = HALO + 1;
   __shared__ float s_alpha[kMaxTile + kMaxHalo];
@@ -106,43 +107,45 @@ __global__ __launch_bounds__(1024) void conv_kernel(ConvArgs a) {
   const int nb = a.nb, d = a.d;
   const int64_t seq0 = (int64_t)b * a.T;
 
-  // ---- step 1: per-position scalars, one wave per position: the lanes split
-  // the np row partials of each sum and combine them with shuffles
+  // ---- step 1: per-position scalars, four positions per wave at a time:
+  // each 16-lane group splits the np row partials of one position and
+  // combines them with shuffles (the four positions' loads go out together)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if (FUSED) {
     const int nq = 3 * nb + 1;
     const float fd = (float)d;
-    for (int i = wave; i < L; i += nw) {
+    const int sub = lane & 15, grp = lane >> 4;
+    for (int i0 = wave * 4; i0 < L; i0 += nw * 4) {
+      const int i = i0 + grp;
       const int q = qs + i;
-      if (q < 0) {
-        if (lane == 0) {
-          s_alpha[i] = 0.0f;
-          s_scale[i] = 0.0f;
-        }
-        continue;
-      }
-      const int64_t tok = seq0 + q;
+      const bool live = i < L && q >= 0;
+      const int64_t tok = seq0 + (live ? q : 0);  // any valid row when not live
       const float* pr = a.parts + tok * nq * a.np;
       float dot = 0.0f, kk = 0.0f, hh = 0.0f, vv = 0.0f;
-      for (int p = lane; p < a.np; p += 64) {
+      for (int p = sub; p < a.np; p += 16) {
         dot += pr[(3 * br) * a.np + p];
         kk += pr[(3 * br + 1) * a.np + p];
         hh += pr[(3 * br + 2) * a.np + p];
         vv += pr[(3 * nb) * a.np + p];
       }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
+      for (int off = 8; off > 0; off >>= 1) {
         dot += __shfl_xor(dot, off);
         kk += __shfl_xor(kk, off);
         hh += __shfl_xor(hh, off);
         vv += __shfl_xor(vv, off);
       }
-      if (lane == 0) {
-        const float z = dot / (sqrtf(hh / fd + a.eps) * sqrtf(kk / fd + a.eps) * sqrtf(fd));
-        const float al = 1.0f / (1.0f + expf(-z));
-        s_alpha[i] = al;
-        s_scale[i] = al / sqrtf(al * al * (vv / fd) + a.eps);
-        if (a.gates && q >= p0) a.gates[tok * nb + br] = al;
+      if (sub == 0 && i < L) {
+        if (q < 0) {
+          s_alpha[i] = 0.0f;
+          s_scale[i] = 0.0f;
+        } else {
+          const float z = dot / (sqrtf(hh / fd + a.eps) * sqrtf(kk / fd + a.eps) * sqrtf(fd));
+          const float al = 1.0f / (1.0f + expf(-z));
+          s_alpha[i] = al;
+          s_scale[i] = al / sqrtf(al * al * (vv / fd) + a.eps);
+          if (a.gates && q >= p0) a.gates[tok * nb + br] = al;
+        }
       }
     }
   } else {
@@ -180,28 +183,56 @@ __global__ __launch_bounds__(1024) void conv_kernel(ConvArgs a) {
     const float4 w2 = Elem<T>::load4(CW, 2 * d + c0);
     const float4 w3 = Elem<T>::load4(CW, 3 * d + c0);
     const float4 gu = GU ? Elem<T>::load4(GU, c0) : f4(1.0f);
+    // Positions before the sequence occur only in its first tile (qs < 0,
+    // p0 == 0), at i < HALO of the first group: the ring starts with the
+    // caller's state rows there (zeros without a state), and the walk
+    // assigns positions q >= 0 only.  No load then sits behind a branch of
+    // the walk, which would make the compiler wait for every load in flight.
     float4 ring[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) ring[u] = f4(0.0f);
+    if (qs < 0 && a.state) {
+#pragma unroll
+      for (int u = 0; u < HALO; ++u) {
+        int q = qs + u;
+        q = q < -HALO ? -HALO : (q > -1 ? -1 : q);
+        const float4 st = *reinterpret_cast<const float4*>(
+            a.state + (((int64_t)b * HALO + HALO + q) * nb + br) * d + c0);
+        if (qs + u < 0) ring[u] = st;
+      }
+    }
     for (int base = 0; base < L; base += R) {
+      // the group's R source rows (and residual rows) are loaded first, from
+      // clamped row indices, so that all of them are in flight together; rows
+      // outside [0, p1) are never used
+      float4 raw[R], hres[RES ? R : 1];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        int q = qs + base + u;
+        q = q < 0 ? 0 : (q > p1 - 1 ? p1 - 1 : q);
+        if (FUSED) {
+          const f32x4 x = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4*>(a.v + (seq0 + q) * a.v_stride + c0));
+          raw[u] = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          raw[u] = Elem<T>::load4(static_cast<const T*>(a.u), ((seq0 + q) * nb + br) * d + c0);
+        }
+      }
+      if (RES) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          int q = qs + base + u;
+          q = q < p0 ? p0 : (q > p1 - 1 ? p1 - 1 : q);
+          hres[u] = Elem<T>::load4(H, (seq0 + q) * a.h_tok_stride + br * a.h_branch_stride + c0);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int i = base + u;
         if (i < L) {
           const int q = qs + i;
-          float4 src = f4(0.0f), nq = f4(0.0f);
-          if (q >= 0) {
-            if (FUSED) {
-              const f32x4 x = __builtin_nontemporal_load(
-                  reinterpret_cast<const f32x4*>(a.v + (seq0 + q) * a.v_stride + c0));
-              src = make_float4(x[0], x[1], x[2], x[3]);
-            } else {
-              src = Elem<T>::load4(static_cast<const T*>(a.u), ((seq0 + q) * nb + br) * d + c0);
-            }
-            nq = mul4(mul4(gu, src), f4(s_scale[i]));
-          } else if (a.state) {
-            nq = *reinterpret_cast<const float4*>(
-                a.state + (((int64_t)b * HALO + HALO + q) * nb + br) * d + c0);
-          }
-          ring[u] = nq;
+          const float4 src = raw[u];
+          if (q >= 0) ring[u] = mul4(mul4(gu, src), f4(s_scale[i]));
           if (q >= p0) {
             float4 C = mul4(w0, ring[u]);
             C = fma4(w1, ring[(u - DIL + R) % R], C);
@@ -211,10 +242,7 @@ __global__ __launch_bounds__(1024) void conv_kernel(ConvArgs a) {
             float4 D = make_float4(fmaf(g, src.x, silu(C.x)), fmaf(g, src.y, silu(C.y)),
                                    fmaf(g, src.z, silu(C.z)), fmaf(g, src.w, silu(C.w)));
             const int64_t tok = seq0 + q;
-            if (FUSED && a.add_residual) {
-              const float4 h = Elem<T>::load4(H, tok * a.h_tok_stride + br * a.h_branch_stride + c0);
-              D = make_float4(D.x + h.x, D.y + h.y, D.z + h.z, D.w + h.w);
-            }
+            if (RES) D = add4(D, hres[u]);
             Elem<T>::store4_stream(OUT, (tok * nb + br) * d + c0, D);
           }
         }
@@ -474,14 +502,23 @@ hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
   int threads = 256;
   if ((int64_t)grid.x * grid.y < 4 * 256) {
     threads = (a.d / 4 + 63) / 64 * 64;
-    if (threads > 1024) threads = 1024;
+    if (threads > 512) threads = 512;
     if (threads < 256) threads = 256;
   }
+  if (FUSED && a.add_residual) {
+    switch (dil) {
+      case 1: return launch(conv_kernel<1, T, FUSED, FUSED>, grid, threads, 0, s, a);
+      case 2: return launch(conv_kernel<2, T, FUSED, FUSED>, grid, threads, 0, s, a);
+      case 3: return launch(conv_kernel<3, T, FUSED, FUSED>, grid, threads, 0, s, a);
+      case 4: return launch(conv_kernel<4, T, FUSED, FUSED>, grid, threads, 0, s, a);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (dil) {
-    case 1: return launch(conv_kernel<1, T, FUSED>, grid, threads, 0, s, a);
-    case 2: return launch(conv_kernel<2, T, FUSED>, grid, threads, 0, s, a);
-    case 3: return launch(conv_kernel<3, T, FUSED>, grid, threads, 0, s, a);
-    case 4: return launch(conv_kernel<4, T, FUSED>, grid, threads, 0, s, a);
+    case 1: return launch(conv_kernel<1, T, FUSED, false>, grid, threads, 0, s, a);
+    case 2: return launch(conv_kernel<2, T, FUSED, false>, grid, threads, 0, s, a);
+    case 3: return launch(conv_kernel<3, T, FUSED, false>, grid, threads, 0, s, a);
+    case 4: return launch(conv_kernel<4, T, FUSED, false>, grid, threads, 0, s, a);
     default: return hipErrorInvalidValue;
   }
 }
