@@ -13,6 +13,8 @@
 // RMSNorm y = gamma (.) x / r, r = sqrt(mean(x^2) + eps) has the backward
 // dx = gamma (.) dy / r - x * sum(gamma dy x) / (d r^3), dgamma += dy x / r;
 // SiLU'(c) = s (1 + c (1 - s)) with s = sigmoid(c).
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ngram {
@@ -36,6 +38,15 @@ __device__ __forceinline__ float dot(float4 a, float4 b) {
 }
 __device__ __forceinline__ float4 gain4(const bf16_bits* g, int c) {
   return g ? Elem<bf16_bits>::load4(g, c) : mk4(1.0f);
+}
+// The same without a branch around the load: an absent gain reads the
+// always-present `any` and is replaced by 1 as 1 + (x - 1) * 0, so the load
+// goes out with the others instead of waiting behind a branch.
+__device__ __forceinline__ float4 gain4_nb(const bf16_bits* g, const bf16_bits* any, int c) {
+  const float4 x = Elem<bf16_bits>::load4(g ? g : any, c);
+  const float on = g ? 1.0f : 0.0f;
+  return make_float4(fmaf(x.x - 1.0f, on, 1.0f), fmaf(x.y - 1.0f, on, 1.0f),
+                     fmaf(x.z - 1.0f, on, 1.0f), fmaf(x.w - 1.0f, on, 1.0f));
 }
 __device__ __forceinline__ float silu_grad(float c) {
   const float s = 1.0f / (1.0f + expf(-c));
@@ -148,28 +159,50 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) dw[i][j] = mk4(0.0f);
+  // INTERIOR: every tap of the row lies inside the sequence, so the body has
+  // no branch and all of its loads go out together (columns past d read a
+  // clamped valid column and are dropped at the end)
+  auto body = [&](auto interior, int64_t row, int64_t t, int br, int pos) {
+    float4 nv[4][ITEMS], go[ITEMS], w[4][ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int c = cl.c[j];
+      const float4 gu = gain4_nb(a.gamma_u, a.conv_w, c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (decltype(interior)::value) {
+          const int64_t s = t - (int64_t)i * dil;
+          const float4 st = ld4(a.stats + (s * nb + br) * kStatsStride);
+          const float4 v = ld4(a.kv + s * a.kv_ld + nb * d + c);
+          nv[i][j] = mul(gu, mul(v, mk4(st.x * st.w)));
+        } else {
+          nv[i][j] = n_value(a, t, pos, pos - i * dil, br, c, gu);
+        }
+        w[i][j] = Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c);
+      }
+      go[j] = Elem<bf16_bits>::load4(a.d_out, row * d + c);
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      float4 cc = mk4(0.0f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cc = fma4(w[i][j], nv[i][j], cc);
+      float4 dc = make_float4(go[j].x * silu_grad(cc.x), go[j].y * silu_grad(cc.y),
+                              go[j].z * silu_grad(cc.z), go[j].w * silu_grad(cc.w));
+      if (cl.ok[j]) st4(a.dc + row * d + cl.c[j], dc);
+      dc = mul(dc, mk4(cl.ok[j] ? 1.0f : 0.0f));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dw[i][j] = fma4(dc, nv[i][j], dw[i][j]);
+    }
+  };
   for (int64_t row = blockIdx.x; row < a.n * nb; row += gridDim.x) {
     const int64_t t = row / nb;
     const int br = (int)(row - t * nb);
     const int pos = (int)(t % a.T);
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      if (!cl.ok[j]) continue;
-      const int c = cl.c[j];
-      const float4 gu = gain4(a.gamma_u, c);
-      float4 nv[4], cc = mk4(0.0f);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nv[i] = n_value(a, t, pos, pos - i * dil, br, c, gu);
-        cc = fma4(Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c), nv[i], cc);
-      }
-      const float4 go = Elem<bf16_bits>::load4(a.d_out, row * d + c);
-      const float4 dc = make_float4(go.x * silu_grad(cc.x), go.y * silu_grad(cc.y),
-                                    go.z * silu_grad(cc.z), go.w * silu_grad(cc.w));
-      st4(a.dc + row * d + c, dc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dw[i][j] = fma4(dc, nv[i], dw[i][j]);
-    }
+    if (pos >= 3 * dil)
+      body(std::true_type{}, row, t, br, pos);
+    else
+      body(std::false_type{}, row, t, br, pos);
   }
   float* part = a.part_conv + (int64_t)blockIdx.x * 4 * d;
 #pragma unroll
@@ -218,8 +251,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       const float4 st = ld4(a.stats + row * kStatsStride);  // g, 1/rho_h, 1/rho_k, 1/r
       const float P = a.stats[row * kStatsStride + 4];
       const float g = st.x, ih = st.y, ik = st.z, ir = st.w;
-      // dN = sum_i w_i (.) dC_{t + i*dil} inside the sequence
-      float4 dn[ITEMS], go[ITEMS], h[ITEMS], k[ITEMS];
+      // dN = sum_i w_i (.) dC_{t + i*dil} inside the sequence.  Every load is
+      // unconditional (taps past the sequence end read the row itself and are
+      // weighted by 0, columns past d read a clamped valid column and are
+      // dropped), so they all go out before the first wait.
+      float4 dn[ITEMS], go[ITEMS], h[ITEMS], k[ITEMS], gu[ITEMS], w[4][ITEMS], dcv[4][ITEMS];
       float s[2] = {0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
@@ -227,14 +263,22 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         go[j] = Elem<bf16_bits>::load4(a.d_out, row * d + c);
         h[j] = Elem<bf16_bits>::load4(a.hidden, t * a.h_tok + br * a.h_br + c);
         k[j] = ld4(kv + br * d + c);
+        gu[j] = gain4_nb(a.gamma_u, a.conv_w, c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool in = pos + i * dil < a.T;
+          w[i][j] = Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c);
+          dcv[i][j] = ld4(a.dc + (row + (in ? (int64_t)i * dil * nb : 0)) * d + c);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
         dn[j] = mk4(0.0f);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (pos + i * dil < a.T)
-            dn[j] = fma4(Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c),
-                         ld4(a.dc + (row + (int64_t)i * dil * nb) * d + c), dn[j]);
+          if (pos + i * dil < a.T) dn[j] = fma4(w[i][j], dcv[i][j], dn[j]);
         if (cl.ok[j]) {
-          s[0] += dot(mul(gain4(a.gamma_u, c), dn[j]), v[j]);
+          s[0] += dot(mul(gu[j], dn[j]), v[j]);
           s[1] += dot(go[j], v[j]);
         }
       }
@@ -244,13 +288,19 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       const float cu = -g * g * A * ir * ir * ir / fd;  // dU's term along V
       const float cz = dz * rsd;
       const float sk = cz * ih * P * ik * ik * ik / fd, sq = cz * ik * P * ih * ih * ih / fd;
+      float4 gqs[ITEMS], gks[ITEMS];  // both gains of every column group, loaded together
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        gqs[j] = gain4_nb(a.gamma_q, a.conv_w, cl.c[j]);
+        gks[j] = gain4_nb(a.gamma_k, a.conv_w, cl.c[j]);
+      }
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
         if (!cl.ok[j]) continue;
         const int c = cl.c[j];
-        const float4 gu = gain4(a.gamma_u, c), gq = gain4(a.gamma_q, c), gk = gain4(a.gamma_k, c);
+        const float4 gq = gqs[j], gk = gks[j];
         // dU = dOut + gamma_u dN / r - U sum(gamma_u dN U) / (d r^3), U = g V
-        const float4 du = fma4(v[j], mk4(cu), fma4(mul(gu, dn[j]), mk4(ir), go[j]));
+        const float4 du = fma4(v[j], mk4(cu), fma4(mul(gu[j], dn[j]), mk4(ir), go[j]));
         // q^ = gamma_q h / rho_h, k^ = gamma_k K / rho_k; dq^ = dz k^ / sqrt d, dk^ = dz q^ / sqrt d
         const float4 dqh = mul(mk4(cz * ik), mul(gk, k[j]));
         const float4 dkh = mul(mk4(cz * ih), mul(gq, h[j]));
