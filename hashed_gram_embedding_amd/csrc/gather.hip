@@ -110,13 +110,17 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ err) {
   __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
   __shared__ float s_scale[NGRAM_MAX_TABLES];
+  const int lane = threadIdx.x & 63;
+  // this lane's table hash constants, loaded once and first, so that their
+  // round trip overlaps the table pointers' below
+  const int jl = lane < h.n_tables ? lane : 0;
+  const RowHash rh = row_hash_of(h, jl, h.orders[jl / h.heads]);
   if (threadIdx.x < NGRAM_MAX_TABLES) {
     const int j = threadIdx.x < h.n_tables ? threadIdx.x : 0;
     s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[j]);
     s_scale[threadIdx.x] = tabs.scale[j];
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
   constexpr int tok_per_block = 4 / WPT;
   const int part = (threadIdx.x >> 6) % WPT;
   const int64_t n_tok = (int64_t)B * T;
@@ -124,16 +128,14 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
   const int32_t chunks = h.n_tables * row_chunks;  // table chunks per token
   const int32_t per = (chunks + WPT - 1) / WPT;
   const int32_t q0 = part * per, q1 = q0 + per < chunks ? q0 + per : chunks;
-  const int jl = lane < h.n_tables ? lane : 0;
-  const int order_l = h.orders[jl / h.heads];
   const int32_t n_kk = chunks * (FP8 ? 2 : 1) >> 2;  // 32-wide K steps per token
   for (int64_t tok = (int64_t)blockIdx.x * tok_per_block + (threadIdx.x >> 6) / WPT; tok < n_tok;
        tok += tstride) {
     const int32_t b = (int32_t)(tok / T);
     const int32_t t = (int32_t)(tok - (int64_t)b * T);
     uint64_t c[NGRAM_MAX_ORDER];
-    context_ids<true>(ids, tok, b, t, hist, lut, h, err, c);
-    const int32_t my_row = (int32_t)table_row(h, jl, order_l, c);
+    const bool bad = context_ids<true>(ids, tok, b, t, hist, lut, h, c);
+    const int32_t my_row = (int32_t)table_row(rh, c);
     uint4* dst = mem + (tok >> 4) * n_kk * 64 + (tok & 15);
     // E chunk e (16 bytes, 8 bf16): K step e/4, quarter e%4
     auto put = [&](int e, const uint4& x) { dst[(e >> 2) * 64 + (e & 3) * 16] = x; };
@@ -165,6 +167,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
         }
       }
     }
+    if (bad && err) *err = 1;
   }
 }
 

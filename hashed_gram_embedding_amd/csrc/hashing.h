@@ -25,39 +25,93 @@ __device__ __forceinline__ int32_t compress_one(int32_t x, const int32_t* __rest
 // Compressed ids c[i] of positions t - i (i < max_order) for token (b, t):
 // inside the sequence from ids, before it from the history (oldest first),
 // else pad.  RAW: ids/history are raw ids, compressed through the LUT.
+// Returns true when an id it used was out of the vocabulary or mapped out of
+// the compressed range (the caller raises the error flag; the store is left
+// to it so that no branch sits between these loads and the caller's next ones).
 template <bool RAW>
-__device__ __forceinline__ void context_ids(const int32_t* __restrict__ ids, int64_t tok, int32_t b,
+__device__ __forceinline__ bool context_ids(const int32_t* __restrict__ ids, int64_t tok, int32_t b,
                                             int32_t t, const int32_t* __restrict__ hist,
                                             const int32_t* __restrict__ lut, const HashArgs& a,
-                                            int32_t* __restrict__ err,
                                             uint64_t (&c)[NGRAM_MAX_ORDER]) {
+  // Every id is loaded unconditionally -- a position without one reads the
+  // token's own id as a stand-in and becomes pad -- and then every LUT entry,
+  // so each group of loads goes out at once instead of one round trip per
+  // position behind a branch.
+  int32_t x[NGRAM_MAX_ORDER];
+  bool have[NGRAM_MAX_ORDER];
 #pragma unroll
   for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
-    int32_t id = a.pad_id;
-    bool have = false;
-    if (i < a.max_order) {
-      const int32_t p = t - i;
-      if (p >= 0) {
-        id = ids[tok - i];
-        have = true;
-      } else if (hist != nullptr && a.hist_len + p >= 0) {
-        id = hist[(int64_t)b * a.hist_len + a.hist_len + p];
-        have = true;
-      }
-    }
-    if (RAW && have) id = compress_one(id, lut, a.vocab, a.vocab_c, a.pad_id, err);
-    c[i] = (uint64_t)(uint32_t)id;
+    const int32_t p = t - i;
+    const bool in_seq = p >= 0;
+    const bool in_hist = !in_seq && hist != nullptr && a.hist_len + p >= 0;
+    have[i] = i < a.max_order && (in_seq || in_hist);
+    const int32_t* src = in_seq    ? ids + (tok - i)
+                         : in_hist ? hist + ((int64_t)b * a.hist_len + a.hist_len + p)
+                                   : ids + tok;
+    x[i] = *src;
   }
+  if (RAW) {
+    int32_t cx[NGRAM_MAX_ORDER];
+    bool in_vocab[NGRAM_MAX_ORDER];
+#pragma unroll
+    for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
+      in_vocab[i] = x[i] >= 0 && x[i] < a.vocab;
+      cx[i] = lut[in_vocab[i] ? x[i] : 0];
+    }
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
+      const bool ok = in_vocab[i] && cx[i] >= 0 && cx[i] < a.vocab_c;
+      bad = bad || (have[i] && !ok);
+      c[i] = (uint64_t)(uint32_t)(have[i] && ok ? cx[i] : a.pad_id);
+    }
+    return bad;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NGRAM_MAX_ORDER; ++i)
+      c[i] = (uint64_t)(uint32_t)(have[i] ? x[i] : a.pad_id);
+    return false;
+  }
+}
+
+// Hash constants of one table: its multipliers, prime and Barrett constant.
+struct RowHash {
+  uint64_t m[NGRAM_MAX_ORDER];
+  uint64_t p, magic;
+  int order;
+};
+
+__device__ __forceinline__ RowHash row_hash_of(const HashArgs& a, int j, int order) {
+  RowHash r;
+#pragma unroll
+  for (int i = 0; i < NGRAM_MAX_ORDER; ++i) r.m[i] = a.mult[j][i];
+  r.p = a.rows[j];
+  r.magic = a.magic[j];
+  r.order = order;
+  return r;
+}
+
+// Row of the table for the context c.
+__device__ __forceinline__ uint32_t table_row(const RowHash& r, const uint64_t (&c)[NGRAM_MAX_ORDER]) {
+  // every multiplier is used, none behind a branch: the empty asm makes the
+  // values opaque, so the compiler cannot sink a multiplier's load into the
+  // i < order case (which made each load wait for the one before); a kernel
+  // that loads the constants before its token loop finds them there already
+  uint64_t m[NGRAM_MAX_ORDER];
+#pragma unroll
+  for (int i = 0; i < NGRAM_MAX_ORDER; ++i) m[i] = r.m[i];
+  static_assert(NGRAM_MAX_ORDER == 4, "one operand per order below");
+  asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]));
+  uint64_t key = 0;
+#pragma unroll
+  for (int i = 0; i < NGRAM_MAX_ORDER; ++i) key ^= i < r.order ? c[i] * m[i] : 0;
+  return mod_prime(key, r.p, r.magic);
 }
 
 // Row of table j for the context c.
 __device__ __forceinline__ uint32_t table_row(const HashArgs& a, int j, int order,
                                               const uint64_t (&c)[NGRAM_MAX_ORDER]) {
-  uint64_t key = 0;
-#pragma unroll
-  for (int i = 0; i < NGRAM_MAX_ORDER; ++i)
-    if (i < order) key ^= c[i] * a.mult[j][i];
-  return mod_prime(key, a.rows[j], a.magic[j]);
+  return table_row(row_hash_of(a, j, order), c);
 }
 
 }  // namespace ngram

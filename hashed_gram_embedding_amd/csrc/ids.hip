@@ -35,7 +35,7 @@ __global__ void hash_kernel(const int32_t* __restrict__ ids, int32_t B, int32_t 
     const int32_t b = (int32_t)(tok / T);
     const int32_t t = (int32_t)(tok - (int64_t)b * T);
     uint64_t c[NGRAM_MAX_ORDER];
-    context_ids<RAW>(ids, tok, b, t, hist, lut, a, err, c);
+    const bool bad = context_ids<RAW>(ids, tok, b, t, hist, lut, a, c);
     int32_t* out = row_idx + tok * a.n_tables;
     for (int o = 0; o < a.n_orders; ++o) {
       const int n_o = a.orders[o];
@@ -44,6 +44,7 @@ __global__ void hash_kernel(const int32_t* __restrict__ ids, int32_t B, int32_t 
         out[j] = (int32_t)table_row(a, j, n_o, c);
       }
     }
+    if (bad && err) *err = 1;
   }
 }
 

@@ -150,12 +150,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
       const int32_t b = (int32_t)(tok / a.T);
       const int32_t t = (int32_t)(tok - (int64_t)b * a.T);
       uint64_t c[NGRAM_MAX_ORDER];
-      context_ids<true>(a.ids, tok, b, t, a.hist, a.lut, a.hash, a.err, c);
+      const bool bad = context_ids<true>(a.ids, tok, b, t, a.hist, a.lut, a.hash, c);
       for (int o = 0; o < a.hash.n_orders; ++o)
         for (int k = 0; k < a.hash.heads; ++k) {
           const int j = o * a.hash.heads + k;
           s_rid[i * NGRAM_MAX_TABLES + j] = (int32_t)table_row(a.hash, j, a.hash.orders[o], c);
         }
+      if (bad && a.err) *a.err = 1;
     }
     __syncthreads();
   }
