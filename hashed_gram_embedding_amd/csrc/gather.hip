@@ -115,26 +115,33 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
   // round trip overlaps the table pointers' below
   const int jl = lane < h.n_tables ? lane : 0;
   const RowHash rh = row_hash_of(h, jl, h.orders[jl / h.heads]);
+  constexpr int tok_per_block = 4 / WPT;
+  const int64_t n_tok = (int64_t)B * T;
+  const int64_t tstride = (int64_t)gridDim.x * tok_per_block;
+  const int64_t tok0 = (int64_t)blockIdx.x * tok_per_block + (threadIdx.x >> 6) / WPT;
+  // the first token's context ids also go out before the barrier (a token
+  // past the end reads token 0's, unused)
+  auto ctx_of = [&](int64_t tok) {
+    const int64_t tk = tok < n_tok ? tok : 0;
+    const int32_t b = (int32_t)(tk / T);
+    return load_context(ids, tk, b, (int32_t)(tk - (int64_t)b * T), hist, h);
+  };
+  CtxIds ctx = ctx_of(tok0);
   if (threadIdx.x < NGRAM_MAX_TABLES) {
     const int j = threadIdx.x < h.n_tables ? threadIdx.x : 0;
     s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[j]);
     s_scale[threadIdx.x] = tabs.scale[j];
   }
   __syncthreads();
-  constexpr int tok_per_block = 4 / WPT;
   const int part = (threadIdx.x >> 6) % WPT;
-  const int64_t n_tok = (int64_t)B * T;
-  const int64_t tstride = (int64_t)gridDim.x * tok_per_block;
   const int32_t chunks = h.n_tables * row_chunks;  // table chunks per token
   const int32_t per = (chunks + WPT - 1) / WPT;
   const int32_t q0 = part * per, q1 = q0 + per < chunks ? q0 + per : chunks;
   const int32_t n_kk = chunks * (FP8 ? 2 : 1) >> 2;  // 32-wide K steps per token
-  for (int64_t tok = (int64_t)blockIdx.x * tok_per_block + (threadIdx.x >> 6) / WPT; tok < n_tok;
-       tok += tstride) {
-    const int32_t b = (int32_t)(tok / T);
-    const int32_t t = (int32_t)(tok - (int64_t)b * T);
+  for (int64_t tok = tok0; tok < n_tok; tok += tstride) {
     uint64_t c[NGRAM_MAX_ORDER];
-    const bool bad = context_ids<true>(ids, tok, b, t, hist, lut, h, c);
+    const bool bad = compress_context<true>(ctx, lut, h, c);
+    ctx = ctx_of(tok + tstride);  // the next token's ids, in flight during this one
     const int32_t my_row = (int32_t)table_row(rh, c);
     uint4* dst = mem + (tok >> 4) * n_kk * 64 + (tok & 15);
     // E chunk e (16 bytes, 8 bf16): K step e/4, quarter e%4

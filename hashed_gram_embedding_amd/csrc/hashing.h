@@ -22,56 +22,74 @@ __device__ __forceinline__ int32_t compress_one(int32_t x, const int32_t* __rest
   return pad;
 }
 
-// Compressed ids c[i] of positions t - i (i < max_order) for token (b, t):
-// inside the sequence from ids, before it from the history (oldest first),
-// else pad.  RAW: ids/history are raw ids, compressed through the LUT.
-// Returns true when an id it used was out of the vocabulary or mapped out of
-// the compressed range (the caller raises the error flag; the store is left
-// to it so that no branch sits between these loads and the caller's next ones).
-template <bool RAW>
-__device__ __forceinline__ bool context_ids(const int32_t* __restrict__ ids, int64_t tok, int32_t b,
-                                            int32_t t, const int32_t* __restrict__ hist,
-                                            const int32_t* __restrict__ lut, const HashArgs& a,
-                                            uint64_t (&c)[NGRAM_MAX_ORDER]) {
-  // Every id is loaded unconditionally -- a position without one reads the
-  // token's own id as a stand-in and becomes pad -- and then every LUT entry,
-  // so each group of loads goes out at once instead of one round trip per
-  // position behind a branch.
+// The raw ids of a token's context, positions t - i (i < max_order): inside
+// the sequence from ids, before it from the history (oldest first).  Every id
+// is loaded unconditionally -- a position without one reads the token's own id
+// as a stand-in and is marked absent -- so the loads go out at once instead of
+// one round trip per position behind a branch.
+struct CtxIds {
   int32_t x[NGRAM_MAX_ORDER];
   bool have[NGRAM_MAX_ORDER];
+};
+
+__device__ __forceinline__ CtxIds load_context(const int32_t* __restrict__ ids, int64_t tok,
+                                               int32_t b, int32_t t,
+                                               const int32_t* __restrict__ hist,
+                                               const HashArgs& a) {
+  CtxIds r;
 #pragma unroll
   for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
     const int32_t p = t - i;
     const bool in_seq = p >= 0;
     const bool in_hist = !in_seq && hist != nullptr && a.hist_len + p >= 0;
-    have[i] = i < a.max_order && (in_seq || in_hist);
+    r.have[i] = i < a.max_order && (in_seq || in_hist);
     const int32_t* src = in_seq    ? ids + (tok - i)
                          : in_hist ? hist + ((int64_t)b * a.hist_len + a.hist_len + p)
                                    : ids + tok;
-    x[i] = *src;
+    r.x[i] = *src;
   }
+  return r;
+}
+
+// Compressed ids c[i] of the context (pad where absent).  RAW: the ids are
+// raw and go through the LUT (every entry loaded at once).  Returns true when
+// an id it used was out of the vocabulary or mapped out of the compressed
+// range (the caller raises the error flag; the store is left to it so that no
+// branch sits between these loads and the caller's next ones).
+template <bool RAW>
+__device__ __forceinline__ bool compress_context(const CtxIds& r, const int32_t* __restrict__ lut,
+                                                 const HashArgs& a, uint64_t (&c)[NGRAM_MAX_ORDER]) {
   if (RAW) {
     int32_t cx[NGRAM_MAX_ORDER];
     bool in_vocab[NGRAM_MAX_ORDER];
 #pragma unroll
     for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
-      in_vocab[i] = x[i] >= 0 && x[i] < a.vocab;
-      cx[i] = lut[in_vocab[i] ? x[i] : 0];
+      in_vocab[i] = r.x[i] >= 0 && r.x[i] < a.vocab;
+      cx[i] = lut[in_vocab[i] ? r.x[i] : 0];
     }
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < NGRAM_MAX_ORDER; ++i) {
       const bool ok = in_vocab[i] && cx[i] >= 0 && cx[i] < a.vocab_c;
-      bad = bad || (have[i] && !ok);
-      c[i] = (uint64_t)(uint32_t)(have[i] && ok ? cx[i] : a.pad_id);
+      bad = bad || (r.have[i] && !ok);
+      c[i] = (uint64_t)(uint32_t)(r.have[i] && ok ? cx[i] : a.pad_id);
     }
     return bad;
   } else {
 #pragma unroll
     for (int i = 0; i < NGRAM_MAX_ORDER; ++i)
-      c[i] = (uint64_t)(uint32_t)(have[i] ? x[i] : a.pad_id);
+      c[i] = (uint64_t)(uint32_t)(r.have[i] ? r.x[i] : a.pad_id);
     return false;
   }
+}
+
+// Both steps for token (b, t).
+template <bool RAW>
+__device__ __forceinline__ bool context_ids(const int32_t* __restrict__ ids, int64_t tok, int32_t b,
+                                            int32_t t, const int32_t* __restrict__ hist,
+                                            const int32_t* __restrict__ lut, const HashArgs& a,
+                                            uint64_t (&c)[NGRAM_MAX_ORDER]) {
+  return compress_context<RAW>(load_context(ids, tok, b, t, hist, a), lut, a, c);
 }
 
 // Hash constants of one table: its multipliers, prime and Barrett constant.
