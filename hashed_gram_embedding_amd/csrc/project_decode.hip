@@ -17,11 +17,14 @@
 // byte crosses HBM once per call, and the host sizes the grid to about one
 // workgroup per CU (one block fills most of a CU's LDS).
 //
-// Wave w of the four handles token rows [16*MI*w, 16*MI*(w+1)) of each pass
-// of 64*MI rows; lane l reads row l%16 of a 16-row block and the 8 k values
-// (l/16)*8.. of a 32-wide K step -- E arrives in that order (decode E tiles,
-// internal.h), one contiguous kilobyte per operand -- and holds C rows
-// 4*(l/16)+r, column l%16.
+// Wave w of the sixteen handles token rows [16*MI*w, 16*MI*(w+1)) of each
+// pass of 256*MI rows; lane l reads row l%16 of a 16-row block and the 8 k
+// values (l/16)*8.. of a 32-wide K step -- E arrives in that order (decode E
+// tiles, internal.h), one contiguous kilobyte per operand -- and holds C rows
+// 4*(l/16)+r, column l%16.  Sixteen waves of one 16-row block each (four per
+// SIMD) hide the E loads' L2 latency far better than four waves of four
+// blocks: at Qwen decode the kernel went from 14.3 to 10.7 us, although
+// every wave now reads the whole W block from LDS.
 #include "internal.h"
 
 namespace ngram {
@@ -30,15 +33,13 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWstatWaves = 4;
+constexpr int kWstatWaves = 16;  // one 16-row block per wave (MI = 1)
 
 __device__ __forceinline__ void copy16_to_lds(const void* src, bf16_bits* wave_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)wave_dst, 16, 0, 0);
 }
 
-// NK > 0: the slice has exactly NK K steps and the K loop is unrolled whole,
-// so no loop-carried operand registers force a drain of the ring.
-template <int NI, int MI, int RING, int NK>
+template <int NI, int MI, int RING>
 __global__ __launch_bounds__(64 * kWstatWaves, 1) void proj_wstat_kernel(WstatArgs a) {
   static_assert(RING % 2 == 0, "the B operands alternate between two register sets");
   constexpr int NT = 16 * NI;
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(64 * kWstatWaves, 1) void proj_wstat_kernel(WstatAr
   const int n0 = n_tile * NT;
   const int K = a.K, KT = a.kt, k0 = ks * KT;
   const int rch = KT / 8;            // 16-byte chunks per LDS row (a multiple of 16)
-  const int nk = NK > 0 ? NK : KT / 32;  // K steps of the slice (a multiple of RING)
+  const int nk = KT / 32;            // K steps of the slice (a multiple of RING)
   const int64_t M = a.M;
   const int64_t last_blk = (M - 1) >> 4;
   const int64_t tiles_per_blk = K / 32;
@@ -122,7 +123,6 @@ __global__ __launch_bounds__(64 * kWstatWaves, 1) void proj_wstat_kernel(WstatAr
     };
     bf16x8 b0[NI], b1[NI];
     bload(0, b0);
-#pragma unroll
     for (int kb = 0; kb < nk; kb += RING) {
 #pragma unroll
       for (int u = 0; u < RING; ++u) {
@@ -172,15 +172,11 @@ __global__ __launch_bounds__(64 * kWstatWaves, 1) void proj_wstat_kernel(WstatAr
 
 template <int NI>
 hipError_t launch_ni(int ring, unsigned blocks, const WstatArgs& a, hipStream_t s) {
-  const int nk = a.kt / 32;
   constexpr unsigned T = 64 * kWstatWaves;
-  // the unrolled K loops and the deep ring fit the register file up to 80 columns
-  if constexpr (NI <= 5) {
-    if (ring == 10 && nk == 20) return launch(proj_wstat_kernel<NI, 4, 10, 20>, blocks, T, 0, s, a);
-    if (ring == 4 && nk == 16) return launch(proj_wstat_kernel<NI, 4, 4, 16>, blocks, T, 0, s, a);
-    if (ring == 10) return launch(proj_wstat_kernel<NI, 4, 10, 0>, blocks, T, 0, s, a);
-  }
-  if (ring == 4) return launch(proj_wstat_kernel<NI, 4, 4, 0>, blocks, T, 0, s, a);
+  // four waves per SIMD leave 128 registers a lane: a four-step ring fits
+  // every tile width without spills (a ten-step ring or an unrolled K loop
+  // does not, and measured slower)
+  if (ring == 4) return launch(proj_wstat_kernel<NI, 1, 4>, blocks, T, 0, s, a);
   return hipErrorInvalidValue;
 }
 
@@ -194,7 +190,7 @@ hipError_t launch_ni(int ring, unsigned blocks, const WstatArgs& a, hipStream_t 
 WstatPlan wstat_plan(int64_t M, int32_t N, int32_t K) {
   WstatPlan best{0, 0, 0};
   double best_cost = 0.0;
-  const int nis[] = {5, 4, 6, 8, 3, 2, 10};
+  const int nis[] = {5, 4, 6, 3, 2};  // wider tiles spill at 128 registers a lane
   for (int ni : nis) {
     const int nt = 16 * ni;
     for (int split = 1; split <= 16; ++split) {
@@ -211,10 +207,7 @@ WstatPlan wstat_plan(int64_t M, int32_t N, int32_t K) {
       }
     }
   }
-  if (best.ni) {
-    const int nk = K / best.split / 32;
-    best.ring = best.ni <= 5 && nk % 10 == 0 ? 10 : 4;  // nk is a multiple of 4
-  }
+  if (best.ni) best.ring = 4;  // nk = KT / 32 is a multiple of 4
   return best;
 }
 
@@ -236,8 +229,6 @@ hipError_t launch_projection_wstat(const WstatPlan& plan, const WstatArgs& a0, h
     case 4: return launch_ni<4>(plan.ring, (unsigned)blocks, a, s);
     case 5: return launch_ni<5>(plan.ring, (unsigned)blocks, a, s);
     case 6: return launch_ni<6>(plan.ring, (unsigned)blocks, a, s);
-    case 8: return launch_ni<8>(plan.ring, (unsigned)blocks, a, s);
-    case 10: return launch_ni<10>(plan.ring, (unsigned)blocks, a, s);
     default: return hipErrorInvalidValue;
   }
 }

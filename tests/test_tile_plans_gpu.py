@@ -107,12 +107,11 @@ def decode_env(request):
         os.environ["NGRAM_DECODE_PLAN"] = old
 
 
-# "ni,split,ring": 16*ni weight columns per workgroup, K slices (each a
-# multiple of 128 wide), K steps of E loads in flight (4, or 10 up to 80
-# columns).  With K = 2560: 5,4,10, 4,4,10 and 3,5,4 take the fully unrolled K
-# loop (20 and 16 steps per slice), the others the looped one; 3 (48 columns)
-# leaves a ragged last column tile.
-DECODE_PLANS = ["default", "5,4,10", "5,4,4", "4,4,10", "2,2,4", "8,10,4", "3,5,4", "10,10,4"]
+# "ni,split,ring": 16*ni weight columns per workgroup (ni 2..6), K slices
+# (each a multiple of 128 wide), K steps of E loads in flight (4).  With
+# K = 2560: 3 (48 columns) leaves a ragged last column tile, 6 (96) another
+# one; splits 2..10 give 20- down to 8-step slices.
+DECODE_PLANS = ["default", "5,4,4", "4,4,4", "6,4,4", "2,2,4", "3,5,4", "5,10,4", "4,20,4"]
 
 
 @pytest.mark.parametrize("decode_env", DECODE_PLANS, indirect=True)
