@@ -129,87 +129,116 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
   }
 }
 
-// N of sequence position p (relative to token t at position pos) for branch
-// br, columns c..c+3: gamma_u g V / r inside the sequence, the caller's state
-// rows before it, zeros before those.
-__device__ __forceinline__ float4 n_value(const BwdArgs& a, int64_t t, int pos, int p, int br,
-                                          int c, float4 gu) {
-  if (p >= 0) {
-    const int64_t s = t - (pos - p);
-    const float4 st = ld4(a.stats + (s * a.nb + br) * kStatsStride);
-    const float4 v = ld4(a.kv + s * a.kv_ld + a.nb * a.d + c);
-    return mul(gu, mul(v, mk4(st.x * st.w)));
-  }
-  const int span = 3 * a.dil;
-  if (a.state == nullptr || span + p < 0) return mk4(0.0f);
-  const int64_t b = t / a.T;
-  return ld4(a.state + ((b * span + span + p) * a.nb + br) * (int64_t)a.d + c);
-}
+// 2. dC = dOut (.) SiLU'(C) per token and branch, C = sum_i w_i (.) N_{t-i*dil}
+// with N = gamma_u g V / r inside the sequence, the caller's state rows before
+// it (zeros without a state), and the taps' gradient d_w[i] = sum dC (.)
+// N_{t-i*dil}.  A workgroup walks a tile of kBwdTile positions of one sequence
+// and branch (plus the 3*dil positions before it) with each thread owning
+// four columns, as the forward conv does: every V row is read once into a
+// ring of the last 3*dil+1 positions, each group of positions loads its rows
+// together, and the taps' gradient sums in registers and then into the
+// workgroup's partial row [4 d] of a.part_conv (its first tile writes it, the
+// others add to it; the column sum over workgroups runs afterwards).
+constexpr int kBwdTile = 64;
 
-// 2. dC = dOut (.) SiLU'(C) per token and branch (C = sum_i w_i (.) N_{t-i*dil}),
-// and the taps' gradient d_w[i] = sum dC (.) N_{t-i*dil}: summed in registers
-// over the rows of this block, written as the block's partial row [4 d] of
-// a.part_conv (the column sum over blocks runs afterwards, no atomics).
-template <int ITEMS>
+template <int DIL>
 __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
-  const int nb = a.nb, d = a.d, dil = a.dil;
-  const Cols<ITEMS> cl(d);
-  float4 dw[4][ITEMS];
+  constexpr int HALO = 3 * DIL, R = HALO + 1;
+  __shared__ float s_sc[kBwdTile + HALO];  // g / r of each position (0 before the sequence)
+  const int nb = a.nb, d = a.d;
+  const int tiles = (a.T + kBwdTile - 1) / kBwdTile;
+  const int64_t total = a.n / a.T * tiles * nb;
+  float* __restrict__ part = a.part_conv + (int64_t)blockIdx.x * 4 * d;
+  bool first = true;
+  for (int64_t wi = blockIdx.x; wi < total; wi += gridDim.x) {
+    const int br = (int)(wi % nb);
+    const int64_t bt = wi / nb;
+    const int64_t b = bt / tiles;
+    const int p0 = (int)(bt - b * tiles) * kBwdTile;
+    const int p1 = min(p0 + kBwdTile, a.T);
+    const int qs = p0 - HALO, L = p1 - qs;
+    const int64_t seq0 = b * a.T;
+    __syncthreads();  // the previous tile's walk is done with s_sc
+    for (int i = threadIdx.x; i < L; i += blockDim.x) {
+      const int q = qs + i;
+      const float* st = a.stats + ((seq0 + (q < 0 ? 0 : q)) * nb + br) * kStatsStride;
+      s_sc[i] = q < 0 ? 0.0f : st[0] * st[3];
+    }
+    __syncthreads();
+    for (int c0 = threadIdx.x * 4; c0 < d; c0 += blockDim.x * 4) {
+      const float4 gu = gain4_nb(a.gamma_u, a.conv_w, c0);
+      const float4 w0 = Elem<bf16_bits>::load4(a.conv_w, c0);
+      const float4 w1 = Elem<bf16_bits>::load4(a.conv_w, (int64_t)d + c0);
+      const float4 w2 = Elem<bf16_bits>::load4(a.conv_w, 2 * (int64_t)d + c0);
+      const float4 w3 = Elem<bf16_bits>::load4(a.conv_w, 3 * (int64_t)d + c0);
+      // positions before the sequence (a sequence's first tile, i < HALO of
+      // the first group): the ring starts with the state rows there
+      float4 ring[R];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int u = 0; u < R; ++u) ring[u] = mk4(0.0f);
+      if (qs < 0 && a.state) {
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) dw[i][j] = mk4(0.0f);
-  // INTERIOR: every tap of the row lies inside the sequence, so the body has
-  // no branch and all of its loads go out together (columns past d read a
-  // clamped valid column and are dropped at the end)
-  auto body = [&](auto interior, int64_t row, int64_t t, int br, int pos) {
-    float4 nv[4][ITEMS], go[ITEMS], w[4][ITEMS];
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      const int c = cl.c[j];
-      const float4 gu = gain4_nb(a.gamma_u, a.conv_w, c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (decltype(interior)::value) {
-          const int64_t s = t - (int64_t)i * dil;
-          const float4 st = ld4(a.stats + (s * nb + br) * kStatsStride);
-          const float4 v = ld4(a.kv + s * a.kv_ld + nb * d + c);
-          nv[i][j] = mul(gu, mul(v, mk4(st.x * st.w)));
-        } else {
-          nv[i][j] = n_value(a, t, pos, pos - i * dil, br, c, gu);
+        for (int u = 0; u < HALO; ++u) {
+          int q = qs + u;
+          q = q < -HALO ? -HALO : (q > -1 ? -1 : q);
+          const float4 sv = ld4(a.state + ((b * HALO + HALO + q) * nb + br) * (int64_t)d + c0);
+          if (qs + u < 0) ring[u] = sv;
         }
-        w[i][j] = Elem<bf16_bits>::load4(a.conv_w, (int64_t)i * d + c);
       }
-      go[j] = Elem<bf16_bits>::load4(a.d_out, row * d + c);
+      float4 dw0 = mk4(0.0f), dw1 = mk4(0.0f), dw2 = mk4(0.0f), dw3 = mk4(0.0f);
+      for (int base = 0; base < L; base += R) {
+        // the group's V rows and output-gradient rows, loaded together from
+        // clamped positions (positions outside the tile's range are unused)
+        float4 raw[R], go[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          int q = qs + base + u;
+          q = q < 0 ? 0 : (q > p1 - 1 ? p1 - 1 : q);
+          raw[u] = ld4(a.kv + (seq0 + q) * a.kv_ld + (int64_t)nb * d + c0);
+          int qo = qs + base + u;
+          qo = qo < p0 ? p0 : (qo > p1 - 1 ? p1 - 1 : qo);
+          go[u] = Elem<bf16_bits>::load4(a.d_out, ((seq0 + qo) * nb + br) * (int64_t)d + c0);
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          const int i = base + u;
+          if (i < L) {
+            const int q = qs + i;
+            if (q >= 0) ring[u] = mul(gu, mul(raw[u], mk4(s_sc[i])));
+            if (q >= p0) {
+              const float4 n1 = ring[(u - DIL + R) % R], n2 = ring[(u - 2 * DIL + R) % R],
+                           n3 = ring[(u - 3 * DIL + R) % R];
+              float4 cc = mul(w0, ring[u]);
+              cc = fma4(w1, n1, cc);
+              cc = fma4(w2, n2, cc);
+              cc = fma4(w3, n3, cc);
+              const float4 dc = make_float4(go[u].x * silu_grad(cc.x), go[u].y * silu_grad(cc.y),
+                                            go[u].z * silu_grad(cc.z), go[u].w * silu_grad(cc.w));
+              st4(a.dc + ((seq0 + q) * nb + br) * (int64_t)d + c0, dc);
+              dw0 = fma4(dc, ring[u], dw0);
+              dw1 = fma4(dc, n1, dw1);
+              dw2 = fma4(dc, n2, dw2);
+              dw3 = fma4(dc, n3, dw3);
+            }
+          }
+        }
+      }
+      float* pc = part + c0;
+      if (!first) {
+        dw0 = add(dw0, ld4(pc));
+        dw1 = add(dw1, ld4(pc + d));
+        dw2 = add(dw2, ld4(pc + 2 * d));
+        dw3 = add(dw3, ld4(pc + 3 * d));
+      }
+      st4(pc, dw0);
+      st4(pc + d, dw1);
+      st4(pc + 2 * d, dw2);
+      st4(pc + 3 * d, dw3);
     }
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      float4 cc = mk4(0.0f);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cc = fma4(w[i][j], nv[i][j], cc);
-      float4 dc = make_float4(go[j].x * silu_grad(cc.x), go[j].y * silu_grad(cc.y),
-                              go[j].z * silu_grad(cc.z), go[j].w * silu_grad(cc.w));
-      if (cl.ok[j]) st4(a.dc + row * d + cl.c[j], dc);
-      dc = mul(dc, mk4(cl.ok[j] ? 1.0f : 0.0f));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dw[i][j] = fma4(dc, nv[i][j], dw[i][j]);
-    }
-  };
-  for (int64_t row = blockIdx.x; row < a.n * nb; row += gridDim.x) {
-    const int64_t t = row / nb;
-    const int br = (int)(row - t * nb);
-    const int pos = (int)(t % a.T);
-    if (pos >= 3 * dil)
-      body(std::true_type{}, row, t, br, pos);
-    else
-      body(std::false_type{}, row, t, br, pos);
+    first = false;
   }
-  float* part = a.part_conv + (int64_t)blockIdx.x * 4 * d;
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j)
-    if (cl.ok[j])
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st4(part + (int64_t)i * d + cl.c[j], dw[i][j]);
+  if (first)  // a workgroup without a tile leaves a zero partial row
+    for (int c = threadIdx.x * 4; c < 4 * d; c += blockDim.x * 4) st4(part + c, mk4(0.0f));
 }
 
 // 3. Per token, all branches: dN -> dU (residual + RMSNorm), dg and dV (U = g V),
@@ -459,13 +488,24 @@ hipError_t launch_bwd_rows(const BwdArgs& a, float* d_conv_w, float* d_gammas,
   if (a.n == 0) return hipSuccess;
   const int items = (a.d + 1023) / 1024;
   hipError_t e;
-  const unsigned g1 = grid_of(a.n, 4096), g2 = grid_of(a.n * a.nb, kBwdBlocks),
+  if (a.T <= 0 || a.n % a.T != 0 || a.dil < 1 || a.dil > 4 || a.d % 4 != 0)
+    return hipErrorInvalidValue;
+  const int64_t conv_work = a.n / a.T * ((a.T + kBwdTile - 1) / kBwdTile) * a.nb;
+  const unsigned g1 = grid_of(a.n, 4096), g2 = grid_of(conv_work, kBwdBlocks),
                  g3 = grid_of(a.n, kBwdBlocks);
+  auto conv = [&]() -> hipError_t {
+    switch (a.dil) {
+      case 1: return launch(bwd_conv_kernel<1>, g2, 256, 0, s, a);
+      case 2: return launch(bwd_conv_kernel<2>, g2, 256, 0, s, a);
+      case 3: return launch(bwd_conv_kernel<3>, g2, 256, 0, s, a);
+      default: return launch(bwd_conv_kernel<4>, g2, 256, 0, s, a);
+    }
+  };
 #define NGRAM_BWD_ITEMS(I)                                                        \
   case I:                                                                         \
     e = launch(bwd_stats_kernel<I>, g1, 256, 0, s, a);                            \
     if (e != hipSuccess) return e;                                                \
-    e = launch(bwd_conv_kernel<I>, g2, 256, 0, s, a);                             \
+    e = conv();                                                                   \
     if (e != hipSuccess) return e;                                                \
     e = a.nb == 1 ? launch(bwd_main_kernel<I, true>, g3, 256, 0, s, a)            \
                   : launch(bwd_main_kernel<I, false>, g3, 256, 0, s, a);          \

@@ -141,6 +141,15 @@ def test_backward_single_token_sequences_and_ragged(orc):
     _case(orc, w, 1, False, True, False, seed=10)
 
 
+@pytest.mark.parametrize("orders", [(1,), (2,), (2, 3, 4)])
+def test_backward_other_dilations(orc, orders):
+    """The conv block's backward at dilations 1, 2 and 4 (the largest order),
+    with a conv state and a ragged last tile of positions (150 = 64 + 64 + 22)."""
+    w = SMALL.replace(orders=orders, batch=2, seq_len=150)
+    print(f"[backward] orders {orders}", flush=True)
+    _case(orc, w, 1, True, True, True, seed=40 + len(orders) + max(orders))
+
+
 def test_backward_rejects_unsupported():
     H = G.H()
     w = W.get("tiny")  # fp32 activations, W stored [mem, d]
