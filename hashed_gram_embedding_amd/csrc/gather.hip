@@ -12,12 +12,26 @@
 // stores (up to 8 chunks per lane in flight) to keep enough random row
 // fetches outstanding; the table base pointers sit in LDS because the lanes
 // of one wave touch different tables.
+#include <type_traits>
+
 #include "hashing.h"
 
 namespace ngram {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Table rows as global-address-space chunks.  The table pointers are kept in
+// LDS; a plain pointer read back from LDS would be a flat one, and flat loads
+// also count against the LDS wait counter, so each chunk's pointer read would
+// wait for the previous chunk's table load.
+typedef const __attribute__((address_space(1))) u32x4 gchunk;
+
+// Wait for every vector-memory load in flight (vmcnt 0; the LDS and export
+// counters untouched).  Issued once between a batch of loads and the stores
+// that use them, so the compiler does not wait before each store behind its
+// per-lane guard (stores count against the same counter, so those waits
+// would serialise the stores).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0xF70); }
 
 // E is written once and read by the next kernel: streamed past the caches
 __device__ __forceinline__ void nt_store16(uint4* p, const uint4& v) {
@@ -39,11 +53,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
                                                      int64_t n_tok, int32_t n_tables,
                                                      int32_t row_chunks, TablePtrs tabs,
                                                      uint4* __restrict__ mem) {
-  __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
+  // FP8: global-space table pointers (see gchunk); bf16: plain ones
+  __shared__ std::conditional_t<FP8, gchunk*, const u32x4*> s_tab[NGRAM_MAX_TABLES];
   __shared__ float s_scale[NGRAM_MAX_TABLES];
   if (threadIdx.x < NGRAM_MAX_TABLES) {
     const int j = threadIdx.x < n_tables ? threadIdx.x : 0;
-    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[j]);
+    s_tab[threadIdx.x] = (std::conditional_t<FP8, gchunk*, const u32x4*>)tabs.p[j];
     s_scale[threadIdx.x] = tabs.scale[j];
   }
   __syncthreads();
@@ -56,21 +71,40 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 
   for (int64_t tok = wave0; tok < n_tok; tok += wstride) {
     const int32_t* rix = row_idx + tok * n_tables;
+    // FP8: the token's row ids, one per lane, loaded once; the chunk loads
+    // take theirs by shuffle and go out together (a lane past the last chunk
+    // re-reads the last one, unused), through global-space pointers, and the
+    // stores follow one wait (FP8 gather 0.63 -> 0.50 ms at Qwen prefill).
+    // bf16 keeps one row-id load per chunk and flat table pointers, which
+    // measured 6 % faster there for its twice as many chunks per token.
+    const int32_t my_r = FP8 ? rix[lane < n_tables ? lane : 0] : 0;
     uint4* dst = mem + tok * chunks * (FP8 ? 2 : 1);
     for (int base = 0; base < chunks; base += 64 * kGatherUnroll) {
       uint4 v[kGatherUnroll];
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
-        const int q = base + u * 64 + lane;
-        if (q < chunks) {
-          const int j = q / row_chunks;
-          const int c = q - j * row_chunks;
-          const int64_t r = rix[j];
-          const u32x4 x = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(s_tab[j] + r * row_chunks + c));
-          v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+        if (FP8) {
+          if (base + u * 64 < chunks) {  // the same for every lane
+            int q = base + u * 64 + lane;
+            q = q < chunks ? q : chunks - 1;
+            const int j = q / row_chunks;
+            const int c = q - j * row_chunks;
+            const int64_t r = __shfl(my_r, j);
+            const u32x4 x = __builtin_nontemporal_load(s_tab[j] + r * row_chunks + c);
+            v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+          }
+        } else {
+          const int q = base + u * 64 + lane;
+          if (q < chunks) {
+            const int j = q / row_chunks;
+            const int c = q - j * row_chunks;
+            const int64_t r = rix[j];
+            const u32x4 x = __builtin_nontemporal_load(s_tab[j] + r * row_chunks + c);
+            v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+          }
         }
       }
+      if (FP8) wait_loads();
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
         const int q = base + u * 64 + lane;
@@ -108,7 +142,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
                                                           int32_t row_chunks, TablePtrs tabs,
                                                           uint4* __restrict__ mem,
                                                           int32_t* __restrict__ err) {
-  __shared__ const uint4* s_tab[NGRAM_MAX_TABLES];
+  __shared__ gchunk* s_tab[NGRAM_MAX_TABLES];
   __shared__ float s_scale[NGRAM_MAX_TABLES];
   const int lane = threadIdx.x & 63;
   // this lane's table hash constants, loaded once and first, so that their
@@ -129,7 +163,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
   CtxIds ctx = ctx_of(tok0);
   if (threadIdx.x < NGRAM_MAX_TABLES) {
     const int j = threadIdx.x < h.n_tables ? threadIdx.x : 0;
-    s_tab[threadIdx.x] = static_cast<const uint4*>(tabs.p[j]);
+    s_tab[threadIdx.x] = (gchunk*)tabs.p[j];
     s_scale[threadIdx.x] = tabs.scale[j];
   }
   __syncthreads();
@@ -154,11 +188,11 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
         const int j = q / row_chunks;
         const int64_t r = __shfl(my_row, j < h.n_tables ? j : 0);
         if (q < q1) {  // random rows, read once: streamed past the caches
-          const u32x4 x = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(s_tab[j] + r * row_chunks + (q - j * row_chunks)));
+          const u32x4 x = __builtin_nontemporal_load(s_tab[j] + r * row_chunks + (q - j * row_chunks));
           v[u] = make_uint4(x[0], x[1], x[2], x[3]);
         }
       }
+      wait_loads();
 #pragma unroll
       for (int u = 0; u < kGatherUnroll; ++u) {
         const int q = base + u * 64 + lane;
