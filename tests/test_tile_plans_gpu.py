@@ -132,6 +132,15 @@ def test_decode_1100_sequences(orc):
     _decode_case(orc, "qwen_decode", 1100)
 
 
+@pytest.mark.parametrize("batch", [1, 17])
+def test_decode_small_batches(orc, batch):
+    """A single sequence and 17 (one full 16-row block and one row of the
+    next): most of the projection's sixteen waves then compute clamped
+    copies of the last row block, which they never store."""
+    print(f"[decode] {batch} sequences", flush=True)
+    _decode_case(orc, "qwen_decode", batch)
+
+
 def test_decode_invalid_ids_are_pad(orc):
     """Ids outside the vocabulary, in the new tokens and in the history, hash
     as the pad id and set the error flag."""
