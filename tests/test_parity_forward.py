@@ -177,6 +177,25 @@ def test_forward_qwen_decode_conv_state_and_residual(orc, layout):
 
 
 @pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
+def test_forward_chunk_with_conv_state(orc, layout):
+    """A prefill chunk that continues earlier ones: a populated conv state,
+    the residual flag and 150 positions per sequence (three conv tiles, the
+    first of which starts its taps on the state rows)."""
+    w = W.get("engram_small").replace(batch=2, seq_len=150, hidden=256, heads=2,
+                                      row_start=10007)
+    print(f"[forward] chunk with conv state, {layout}", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, layout=layout, random_gamma=True)
+    halo = 3 * w.max_order
+    state = rng.normal_f32(4343, np.arange(w.batch * halo * w.hidden), 1.0).reshape(
+        w.batch, halo, 1, w.hidden)
+    out, gates, err = _run(w, inp, flags=1, conv_state=torch.from_numpy(state).cuda())
+    assert err == 0
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, w.seq_len) for b in range(w.batch)],
+                   flags=1, state=state.astype(np.float64))
+
+
+@pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
 def test_forward_qwen_prefill(orc, layout):
     w = W.get("qwen_prefill")
     print(f"[forward] qwen_prefill 262144 tokens {layout}", flush=True)
