@@ -1,7 +1,9 @@
 // extern "C" entry points of libngram.so: argument validation on the host,
 // workspace layout, and the launch sequence of each operation.  Every step
-// of the layer runs in the kernels of ids.hip, gather.hip, project.hip and
-// finalize.hip; this file launches them on the caller's stream.
+// of the layer runs in the kernels of ids.hip, gather.hip, project.hip,
+// project_async.hip, project_decode.hip, finalize.hip and backward.hip (each
+// cites the passages it implements); this file launches them on the
+// caller's stream.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
