@@ -106,6 +106,13 @@ class Setup:
         s.H.ngram_forward(s.cfg, s.ids[p], s.lut, s.tables, s.hidden[p], s.hbs, s.wk, s.wv,
                           s.conv, s.out, history=s.hist[p], workspace=s.ws)
 
+    def step_timed(self, p: int, events) -> int:
+        """One step with each stage's kernels timed into ``events``."""
+        s = self
+        return s.H.ngram_forward_timed(events, s.cfg, s.ids[p], s.lut, s.tables, s.hidden[p],
+                                       s.hbs, s.wk, s.wv, s.conv, s.out, history=s.hist[p],
+                                       workspace=s.ws)
+
 
 # ---------------------------------------------------------------------------
 # algorithmic bytes / flops (what the method must move, not the design's
@@ -150,9 +157,6 @@ STAGE_SOURCES = {
     ("gather", "decode"): [_CS + "gather.hip", _CS + "hashing.h", _CS + "internal.h"],
     ("projection", "decode"): [_CS + "project_decode.hip"],
     ("gate_conv", "decode"): [_CS + "finalize.hip"],
-    ("projection", "fused"): [_CS + "project_async.hip", _CS + "epilogue.h",
-                              _CS + "hashing.h"],
-    ("gate_conv", "fused"): [_CS + "finalize.hip"],
     ("hash", "f32"): [_CS + "ids.hip", _CS + "hashing.h"],
     ("gather", "f32"): [_CS + "gather.hip"],
     ("projection", "f32"): [_CS + "project.hip"],
@@ -166,16 +170,12 @@ STAGE_SOURCES = {
 
 def route(w) -> str:
     """Kernel route of a workload's forward: fp32; decode (one new token per
-    sequence); materialised (hash, gather to E, then the projection: the
-    default); fused (the projection gathers bf16 rows itself, with
-    NGRAM_FUSED_GATHER=1 and 64-wide rows)."""
+    sequence); materialised (hash, gather to E, then the projection)."""
     if w.dtype == "f32":
         return "f32"
     if w.seq_len == 1:
         return "decode"
-    fused = (os.environ.get("NGRAM_FUSED_GATHER") == "1" and w.tdtype == "bf16"
-             and w.row_dim % 64 == 0)
-    return "fused" if fused else "materialised"
+    return "materialised"
 
 
 def stage_source_sha(stage: str, w):
@@ -336,11 +336,9 @@ def main():
     torch.cuda._sleep(int(min(0.2, 3e-4 * args.stage_steps) * 2.5e9))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)]
            for _ in range(args.stage_steps)]
+    mask = 0
     for i in range(args.stage_steps):
-        setup.H.ngram.ngram_set_timing_events(evs[i])
-        setup.step(i % setup.pool)
-    mask = setup.H.ngram.ngram_timing_stage_mask()
-    setup.H.ngram.ngram_set_timing_events(None)
+        mask = setup.step_timed(i % setup.pool, evs[i])
     torch.cuda.synchronize()
     # per-step distribution: one plain event pair around each step, no stage hook
     step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -558,11 +556,11 @@ def main_backward(args):
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * H.ngram.N_STAGES)]
            for _ in range(k)]
+    mask = 0
     for i in range(k):
-        H.ngram.ngram_set_timing_events(evs[i])
-        bwd()
-    mask = H.ngram.ngram_timing_stage_mask()
-    H.ngram.ngram_set_timing_events(None)
+        mask = H.ngram_backward_timed(evs[i], setup.cfg, setup.ids[0], setup.lut, setup.tables,
+                                      setup.hidden[0], setup.hbs, setup.wk, setup.wv, setup.conv,
+                                      d_out, d_tabs, d_wk, d_wv, d_cw, d_hidden=d_h, workspace=bws)
     torch.cuda.synchronize()
     stage_avg = {BWD_STAGES[s]: (float(np.mean([e[2 * s].elapsed_time(e[2 * s + 1])
                                                 for e in evs])) if mask >> s & 1 else 0.0)

@@ -13,11 +13,11 @@
 
 using namespace ngram;
 
-ngram::StageClock* ngram::g_open_stage = nullptr;
+thread_local ngram::StageClock* ngram::t_open_stage = nullptr;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 
 int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : dtype == NGRAM_FP8_E4M3 ? 1 : 4; }
@@ -76,7 +76,21 @@ bool is_prime_u32(uint64_t n) {
   return true;
 }
 
-int validate(const ngram_config* c) {
+// Every rows[j] has no prime factor up to 61 (or is one of them): the screen
+// each entry point runs; the proof is is_prime_u32, run by
+// ngram_config_validate.
+bool passes_small_prime_screen(uint64_t n) {
+  static const uint64_t small[] = {2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37, 41, 43, 47, 53, 59, 61};
+  for (uint64_t p : small) {
+    if (n == p) return true;
+    if (n % p == 0) return false;
+  }
+  return true;
+}
+
+// prove_primes: run the Miller-Rabin proof on every table size (otherwise
+// only the small-factor screen).  Everything else is checked either way.
+int validate(const ngram_config* c, bool prove_primes) {
   if (c == nullptr) return NGRAM_EINVAL;
   if (c->table_dtype != NGRAM_F32 && c->table_dtype != NGRAM_BF16 &&
       c->table_dtype != NGRAM_FP8_E4M3)
@@ -93,7 +107,8 @@ int validate(const ngram_config* c) {
   if (c->n_tables != c->n_orders * c->heads_per_order) return NGRAM_EINVAL;
   for (int j = 0; j < c->n_tables; ++j) {
     if (c->rows[j] < 2 || c->rows[j] > INT32_MAX) return NGRAM_ERANGE;
-    if (!is_prime_u32((uint64_t)c->rows[j])) return NGRAM_ERANGE;
+    const uint64_t n = (uint64_t)c->rows[j];
+    if (!(prove_primes ? is_prime_u32(n) : passes_small_prime_screen(n))) return NGRAM_ERANGE;
   }
   const int es = esize_of(c->table_dtype);
   if (c->row_dim < 1 || ((int64_t)c->row_dim * es) % 16 != 0) return NGRAM_ESHAPE;
@@ -112,6 +127,15 @@ int validate(const ngram_config* c) {
   if (!(c->rms_eps >= 0.0f) || !isfinite(c->rms_eps)) return NGRAM_EINVAL;
   if (c->w_layout != NGRAM_W_MEM_D && c->w_layout != NGRAM_W_D_MEM) return NGRAM_EINVAL;
   if ((int64_t)c->hidden_dim * c->mem_dim >= (int64_t(1) << 31)) return NGRAM_ESHAPE;
+  // tuning overrides
+  if (c->tune_proj_plan < 0 || c->tune_proj_plan > kAsyncPlans) return NGRAM_EINVAL;
+  if ((c->tune_decode_ni == 0) != (c->tune_decode_split == 0)) return NGRAM_EINVAL;
+  if (c->tune_decode_ni != 0) {
+    if (c->tune_decode_ni < 2 || c->tune_decode_ni > 6 || c->tune_decode_split < 1)
+      return NGRAM_EINVAL;
+    if (!wstat_plan_fits(WstatPlan{c->tune_decode_ni, c->tune_decode_split, 4}, c->mem_dim))
+      return NGRAM_EINVAL;
+  }
   return NGRAM_OK;
 }
 
@@ -119,40 +143,19 @@ int validate(const ngram_config* c) {
 bool async_path(const ngram_config* c) {
   return mem_dtype(c) == NGRAM_BF16 && c->w_layout == NGRAM_W_D_MEM;
 }
-// The forward either materialises E (hash, then a gather kernel streaming
-// the rows into E, then the projection) or lets the projection gather its
-// own A operand from the tables (possible when every 64-wide K step lies
-// inside one table row).  Materialising measured faster at every size: the
-// gather streams 2.7 GB at about 5.8 TB/s, while the gathered operand copies
-// lengthen the projection's load latency by more than that.
-// NGRAM_FUSED_GATHER=1 selects the fused route (a tuning knob: both routes
-// compute the same result).
-bool fused_gather(const ngram_config* c) {
-  const char* e = getenv("NGRAM_FUSED_GATHER");
-  if (!(e && e[0] == '1' && e[1] == 0)) return false;
-  return async_path(c) && c->table_dtype == NGRAM_BF16 && c->row_dim % 64 == 0;
-}
 
 // Decode (one new token per sequence, up to kDecodeMaxRows sequences): E is
 // materialised once by the hash + gather kernel, the weight-stationary
 // projection writes one fp32 partial per K slice, and the decode finalize
-// sums them.  Larger batches take the fused route, where the weights are
+// sums them.  Larger batches take the prefill route, where the weights are
 // reused across many more rows.
 constexpr int64_t kDecodeMaxRows = 2048;
 
-// Tile plan of the decode projection; NGRAM_DECODE_PLAN="ni,split,ring"
-// overrides it (a tuning knob; the launch rejects shapes it cannot run).
+// Tile plan of the decode projection: the configuration's override (checked
+// by validate) or the library's choice; ni == 0 when none fits.
 WstatPlan decode_plan(const ngram_config* c, int64_t n_tok) {
-  WstatPlan p = wstat_plan(n_tok, (c->n_branches + 1) * c->hidden_dim, c->mem_dim);
-  const char* e = getenv("NGRAM_DECODE_PLAN");
-  int ni = 0, split = 0, ring = 0;
-  if (e && sscanf(e, "%d,%d,%d", &ni, &split, &ring) == 3 && ni > 0 && split > 0 && ring > 0)
-    p = WstatPlan{ni, split, ring};
-  return p;
-}
-
-bool decode_path(const ngram_config* c, int32_t T, int64_t n_tok) {
-  return async_path(c) && T == 1 && n_tok <= kDecodeMaxRows && decode_plan(c, n_tok).ni > 0;
+  if (c->tune_decode_ni != 0) return WstatPlan{c->tune_decode_ni, c->tune_decode_split, 4};
+  return wstat_plan(n_tok, (c->n_branches + 1) * c->hidden_dim, c->mem_dim);
 }
 
 HashArgs hash_args(const ngram_config* c, int32_t hist_len) {
@@ -187,34 +190,39 @@ struct Layout {
   int64_t v_offset = 0;  // fp32 elements from the V buffer to row 0's values
 };
 
-// forward: the forward pass (row ids and E live in the workspace unless the
-// projection gathers them itself).  T: tokens per sequence (decode when 1).
+// forward: the forward pass (row ids and E live in the workspace).  T:
+// tokens per sequence (the decode route when 1).
 Layout layout_for(const ngram_config* c, int64_t n_tok, bool forward, int32_t T = 0) {
   Layout L;
-  if (forward && decode_path(c, T, n_tok)) {
-    L.wplan = decode_plan(c, n_tok);
-    L.k_split = L.wplan.split;
-    L.plan.np = 1;
-    size_t off = 0;
-    L.e = off;  // decode E tiles: whole 16-token blocks
-    off = align_up(off + (size_t)((n_tok + 15) / 16 * 16) * c->mem_dim * esize_of(mem_dtype(c)));
-    L.split = off;
-    off = align_up(off + (size_t)L.k_split * n_tok * (c->n_branches + 1) * c->hidden_dim *
-                             sizeof(float));
-    L.total = off;
-    return L;
+  if (forward && async_path(c) && T == 1 && n_tok <= kDecodeMaxRows) {
+    const WstatPlan wp = decode_plan(c, n_tok);
+    if (wp.ni > 0) {
+      L.wplan = wp;
+      L.k_split = wp.split;
+      L.plan.np = 1;
+      size_t off = 0;
+      L.e = off;  // decode E tiles: whole 16-token blocks
+      off = align_up(off + (size_t)((n_tok + 15) / 16 * 16) * c->mem_dim *
+                               esize_of(mem_dtype(c)));
+      L.row_idx = off;
+      off = align_up(off + (size_t)n_tok * c->n_tables * sizeof(int32_t));
+      L.split = off;
+      off = align_up(off + (size_t)L.k_split * n_tok * (c->n_branches + 1) * c->hidden_dim *
+                               sizeof(float));
+      L.total = off;
+      return L;
+    }
   }
   const int dt = mem_dtype(c);
   const int nb = c->n_branches, d = c->hidden_dim;
   L.plan = plan_projection(dt, n_tok, d);
   if (async_path(c)) {
-    L.async = async_plan(n_tok);
+    L.async = async_plan(n_tok, c->tune_proj_plan - 1);
     const int wc = async_wave_cols(L.async);
     L.plan.np = (d + wc - 1) / wc;
   }
-  const bool with_memory = forward && !fused_gather(c);
   size_t off = 0;
-  if (with_memory) {
+  if (forward) {
     L.row_idx = off;
     off = align_up(off + (size_t)n_tok * c->n_tables * sizeof(int32_t));
     L.e = off;
@@ -317,33 +325,31 @@ hipError_t raw_gemm(const bf16_bits* A, int64_t M, int32_t K, const bf16_bits* w
   return launch_projection_raw(split > 1 || M >= 8192 ? 7 : M >= 1024 ? 8 : 2, a, s);
 }
 
-// Benchmark instrumentation (ngram_set_timing_events): stage(i) closes the
-// open stage and opens stage i; the kernels launched while it is open stamp
-// the stage's event pair (launch() in internal.h).
-hipEvent_t g_stage_events[2 * NGRAM_N_STAGES];
-bool g_stage_events_on = false;
-int g_stage_mask = 0;
-int g_stage_index = -1;
-StageClock g_clock;
-
-void close_stage() {
-  if (g_open_stage != nullptr && g_clock.launches > 0) g_stage_mask |= 1 << g_stage_index;
-  g_open_stage = nullptr;
-  g_stage_index = -1;
-}
-
-void stage(int i) {
-  close_stage();
-  if (!g_stage_events_on) return;
-  g_clock = StageClock{g_stage_events[2 * i], g_stage_events[2 * i + 1], 0};
-  g_stage_index = i;
-  g_open_stage = &g_clock;
-}
-
-// Closes the last stage when a timed forward call returns, on every path.
-struct TimedCall {
-  TimedCall() { g_stage_mask = 0; }
-  ~TimedCall() { close_stage(); }
+// Stage timing of one instrumented call (ngram_forward_timed /
+// ngram_backward_timed): stage(i) closes the open stage and opens stage i,
+// whose kernels then stamp the stage's event pair (launch() in internal.h
+// reads the calling thread's open stage).  Untimed calls carry a Timer
+// without events, which opens nothing.
+struct Timer {
+  const hipEvent_t* ev = nullptr;
+  int mask = 0;
+  int index = -1;
+  StageClock clock{};
+  void close() {
+    if (index >= 0) {
+      if (clock.launches > 0) mask |= 1 << index;
+      t_open_stage = nullptr;
+      index = -1;
+    }
+  }
+  void stage(int i) {
+    close();
+    if (ev == nullptr) return;
+    clock = StageClock{ev[2 * i], ev[2 * i + 1], 0};
+    index = i;
+    t_open_stage = &clock;
+  }
+  ~Timer() { close(); }
 };
 
 int check_tables(const ngram_config* c, const void* const* tables, TablePtrs* out) {
@@ -387,7 +393,7 @@ ProjArgs proj_args(const ngram_config* c, const void* e, const void* w_k, const 
   return a;
 }
 
-AsyncProjArgs async_args(const ngram_config* c, const ProjArgs& p) {
+AsyncProjArgs async_args(const ProjArgs& p) {
   AsyncProjArgs a;
   memset(&a, 0, sizeof a);
   a.e = static_cast<const bf16_bits*>(p.e);
@@ -405,7 +411,6 @@ AsyncProjArgs async_args(const ngram_config* c, const ProjArgs& p) {
   a.epi.nb = p.nb;
   a.epi.np = p.np;
   a.K = p.K;
-  a.row_dim = c->row_dim;
   a.group_m = 4;
   return a;
 }
@@ -414,7 +419,7 @@ AsyncProjArgs async_args(const ngram_config* c, const ProjArgs& p) {
 hipError_t run_projection(const ngram_config* c, const Layout& L, const ProjArgs& p,
                           hipStream_t s) {
   if (L.async < 0) return launch_projection(mem_dtype(c), L.plan, p, s);
-  return launch_projection_async(false, L.async, async_args(c, p), s);
+  return launch_projection_async(L.async, async_args(p), s);
 }
 
 ConvArgs conv_args_base(const ngram_config* c) {
@@ -424,6 +429,242 @@ ConvArgs conv_args_base(const ngram_config* c) {
   a.d = c->hidden_dim;
   a.eps = c->rms_eps;
   return a;
+}
+
+
+// Shared by ngram_forward, ngram_forward_timed and ngram_forward_noalloc.
+int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                 const int32_t* history, const int32_t* lut, const void* const* tables,
+                 const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                 const void* w_v, const void* conv_w, const void* gamma_q, const void* gamma_k,
+                 const void* gamma_u, float* conv_state, const int32_t* state_pos,
+                 int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
+                 size_t workspace_bytes, hipStream_t s, Timer& tm) {
+  int st = validate(cfg, false);
+  if (st) return st;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_UPDATE_STATE)) return NGRAM_EINVAL;
+  if ((flags & NGRAM_UPDATE_STATE) && conv_state == nullptr) return NGRAM_EINVAL;
+  int64_t h_tok = 0;
+  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
+  if (st) return st;
+  const int64_t n_tok = (int64_t)B * T;
+  if (n_tok == 0) return NGRAM_OK;
+  if (!raw_ids || !lut || !hidden || !w_k || !w_v || !conv_w || !out) return NGRAM_EINVAL;
+  TablePtrs tp;
+  st = check_tables(cfg, tables, &tp);
+  if (st) return st;
+  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut) || !aligned4(err_flag) ||
+      !aligned4(state_pos))
+    return NGRAM_EALIGN;
+  for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u,
+                        (const void*)conv_state, (const void*)out, (const void*)gates})
+    if (!aligned16(p)) return NGRAM_EALIGN;
+  const Layout L = layout_for(cfg, n_tok, true, T);
+  if (!workspace) return NGRAM_EWORKSPACE;
+  if (workspace_bytes < L.total) return NGRAM_EWORKSPACE;
+  if (!aligned16(workspace)) return NGRAM_EALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
+  void* e = ws + L.e;
+  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+  ConvArgs ca = conv_args_base(cfg);
+  ca.conv_w = conv_w;
+  ca.gamma_u = gamma_u;
+  ca.state = conv_state;
+  ca.state_pos = state_pos;
+  ca.update_state = (flags & NGRAM_UPDATE_STATE) ? 1 : 0;
+  ca.hidden = hidden;
+  ca.h_tok_stride = h_tok;
+  ca.h_branch_stride = hidden_branch_stride;
+  ca.out = out;
+  ca.gates = gates;
+  ca.B = B;
+  ca.T = T;
+  ca.dil = cfg->conv_dilation;
+  ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
+  if (L.k_split > 0) {
+    // decode: hash + gather -> E, weight-stationary projection, decode finalize
+    // (which reads the ring's taps and writes this position's row)
+    float* split = reinterpret_cast<float*>(ws + L.split);
+    tm.stage(1);
+    st = hip_status(launch_hash_gather(cfg->table_dtype, raw_ids, B, T, history, lut, ha,
+                                       cfg->n_tables, cfg->row_dim, tp, e, row_idx, err_flag, s));
+    if (st) return st;
+    tm.stage(2);
+    WstatArgs wa{};
+    wa.e = static_cast<const bf16_bits*>(e);
+    wa.wk = static_cast<const bf16_bits*>(w_k);
+    wa.wv = static_cast<const bf16_bits*>(w_v);
+    wa.M = n_tok;
+    wa.K = cfg->mem_dim;
+    wa.nb = cfg->n_branches;
+    wa.d = cfg->hidden_dim;
+    wa.split_out = split;
+    st = hip_status(launch_projection_wstat(L.wplan, wa, s));
+    if (st) return st;
+    tm.stage(3);
+    ca.gamma_q = gamma_q;
+    ca.gamma_k = gamma_k;
+    return hip_status(launch_decode_finalize(cfg->act_dtype, L.k_split, split, ca, s));
+  }
+  const ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
+                                gamma_k, ws, L, n_tok);
+  tm.stage(0);
+  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
+  if (st) return st;
+  tm.stage(1);
+  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim,
+                                tp, e, s));
+  if (st) return st;
+  tm.stage(2);
+  st = hip_status(run_projection(cfg, L, pa, s));
+  if (st) return st;
+  tm.stage(3);
+  ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
+  ca.v_stride = L.v_stride;
+  ca.parts = reinterpret_cast<const float*>(ws + L.parts);
+  ca.np = L.plan.np;
+  ca.tile = conv_tile_for(T);
+  st = hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+  if (st) return st;
+  // the ring's new rows, after every read of it by the conv
+  if (ca.update_state)
+    return hip_status(launch_state_update(cfg->act_dtype, true, cfg->conv_dilation, ca, s));
+  return NGRAM_OK;
+}
+
+int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                  const int32_t* history, const int32_t* lut, const void* const* tables,
+                  const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                  const void* w_v, const void* conv_w, const void* gamma_q, const void* gamma_k,
+                  const void* gamma_u, const float* conv_state, const int32_t* state_pos,
+                  int32_t flags, const void* d_out, float* const* d_tables, float* d_w_k,
+                  float* d_w_v, float* d_conv_w, float* d_hidden, float* d_gammas,
+                  void* workspace, size_t workspace_bytes, hipStream_t s, Timer& tm) {
+  int st = validate(cfg, false);
+  if (st) return st;
+  if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM) return NGRAM_EDTYPE;
+  if (cfg->hidden_dim % 64 != 0 || cfg->hidden_dim > 4096) return NGRAM_ESHAPE;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if (flags & ~NGRAM_ADD_RESIDUAL) return NGRAM_EINVAL;
+  int64_t h_tok = 0;
+  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
+  if (st) return st;
+  const int64_t n = (int64_t)B * T;
+  if (n == 0) return NGRAM_OK;
+  if (!raw_ids || !lut || !hidden || !w_k || !w_v || !conv_w || !d_out || !d_tables || !d_w_k ||
+      !d_w_v || !d_conv_w)
+    return NGRAM_EINVAL;
+  TablePtrs tp;
+  st = check_tables(cfg, tables, &tp);
+  if (st) return st;
+  GradTablePtrs gp;
+  memset(&gp, 0, sizeof gp);
+  for (int j = 0; j < cfg->n_tables; ++j) {
+    if (d_tables[j] == nullptr) return NGRAM_EINVAL;
+    if (!aligned16(d_tables[j])) return NGRAM_EALIGN;
+    gp.p[j] = d_tables[j];
+  }
+  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut) || !aligned4(state_pos))
+    return NGRAM_EALIGN;
+  for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, d_out,
+                        (const void*)conv_state, (const void*)d_w_k, (const void*)d_w_v,
+                        (const void*)d_conv_w, (const void*)d_hidden, (const void*)d_gammas})
+    if (!aligned16(p)) return NGRAM_EALIGN;
+  const BwdLayout L = bwd_layout(cfg, n);
+  const int nb = cfg->n_branches, d = cfg->hidden_dim, mem = cfg->mem_dim;
+  const int64_t N64 = (int64_t)(nb + 1) * d;
+  // the products index their operands with 32-bit offsets: the dW operands
+  // [., n_pad], and the dE product's weights transposed to [mem, (nb+1) d]
+  // (whose split sums also take (nb+1) d mem as a 32-bit stride)
+  if (N64 * L.n_pad >= (int64_t(1) << 31) || (int64_t)mem * L.n_pad >= (int64_t(1) << 31) ||
+      N64 * mem >= (int64_t(1) << 31))
+    return NGRAM_ESHAPE;
+  if (!workspace || workspace_bytes < L.total) return NGRAM_EWORKSPACE;
+  if (!aligned16(workspace)) return NGRAM_EALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  const int32_t N = (int32_t)N64;
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
+  bf16_bits* e = reinterpret_cast<bf16_bits*>(ws + L.e);
+  float* kv = reinterpret_cast<float*>(ws + L.kv);
+  bf16_bits* dkv = reinterpret_cast<bf16_bits*>(ws + L.dkv);
+  bf16_bits* wt = reinterpret_cast<bf16_bits*>(ws + L.wt);
+  float* de = reinterpret_cast<float*>(ws + L.de);
+  bf16_bits* dkvt = reinterpret_cast<bf16_bits*>(ws + L.dkvt);
+  bf16_bits* et = reinterpret_cast<bf16_bits*>(ws + L.et);
+  const bf16_bits* wk = static_cast<const bf16_bits*>(w_k);
+  const bf16_bits* wv = static_cast<const bf16_bits*>(w_v);
+
+  // recompute: row ids, E, and K / V in fp32
+  tm.stage(0);
+  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, nullptr, s));
+  if (st) return st;
+  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n, cfg->n_tables, cfg->row_dim, tp, e, s));
+  if (st) return st;
+  st = hip_status(raw_gemm(e, n, mem, wk, wv, nb, d, kv, N, s));
+  if (st) return st;
+  // the per-row backward: gates, conv, RMSNorms -> dK, dV (bf16), d_hidden, d_conv_w, d_gammas
+  tm.stage(1);
+  BwdArgs ba;
+  memset(&ba, 0, sizeof ba);
+  ba.n = n;
+  ba.T = T;
+  ba.nb = nb;
+  ba.d = d;
+  ba.dil = cfg->conv_dilation;
+  ba.eps = cfg->rms_eps;
+  ba.hidden = static_cast<const bf16_bits*>(hidden);
+  ba.h_tok = h_tok;
+  ba.h_br = hidden_branch_stride;
+  ba.kv = kv;
+  ba.kv_ld = N;
+  ba.stats = reinterpret_cast<float*>(ws + L.stats);
+  ba.dc = reinterpret_cast<float*>(ws + L.dc);
+  ba.d_out = static_cast<const bf16_bits*>(d_out);
+  ba.conv_w = static_cast<const bf16_bits*>(conv_w);
+  ba.gamma_q = static_cast<const bf16_bits*>(gamma_q);
+  ba.gamma_k = static_cast<const bf16_bits*>(gamma_k);
+  ba.gamma_u = static_cast<const bf16_bits*>(gamma_u);
+  ba.state = conv_state;
+  ba.state_pos = state_pos;
+  ba.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
+  ba.dkv = dkv;
+  ba.dkv_ld = N;
+  ba.d_hidden = d_hidden;
+  ba.part_conv = reinterpret_cast<float*>(ws + L.part);
+  ba.part_gain = d_gammas ? ba.part_conv + (size_t)kBwdBlocks * 4 * d : nullptr;
+  st = hip_status(launch_bwd_rows(ba, d_conv_w, d_gammas, reinterpret_cast<float*>(ws + L.rtmp),
+                                  s));
+  if (st) return st;
+  // dE = [dK dV] [W_K; W_V]: the weights transposed to [mem, N] feed the product
+  tm.stage(2);
+  st = hip_status(launch_transpose_bf16(wk, (int64_t)nb * d, mem, mem, wt, (int64_t)nb * d, N, s));
+  if (st) return st;
+  st = hip_status(launch_transpose_bf16(wv, d, mem, mem, wt + (int64_t)nb * d, d, N, s));
+  if (st) return st;
+  st = hip_status(raw_gemm(dkv, n, N, nullptr, wt, 0, mem, de, mem, s));
+  if (st) return st;
+  // dW = [dK dV]^T E: both operands transposed to [., n_pad], tokens padded with zeros
+  tm.stage(3);
+  st = hip_status(launch_transpose_bf16(dkv, n, N, N, dkvt, L.n_pad, L.n_pad, s));
+  if (st) return st;
+  st = hip_status(launch_transpose_bf16(e, n, mem, mem, et, L.n_pad, L.n_pad, s));
+  if (st) return st;
+  // one split-K product for every row of [dK dV]^T, the splits summed into d_w_k and d_w_v
+  float* dw = reinterpret_cast<float*>(ws + L.dw);
+  st = hip_status(raw_gemm(dkvt, N, (int32_t)L.n_pad, nullptr, et, 0, mem, dw, mem, s, L.dw_split));
+  if (st) return st;
+  const int64_t kw = (int64_t)nb * d * mem;
+  st = hip_status(launch_sum_splits(dw, L.dw_split, N64 * mem, kw, d_w_k, s));
+  if (st) return st;
+  st = hip_status(launch_sum_splits(dw + kw, L.dw_split, N64 * mem, (int64_t)d * mem, d_w_v, s));
+  if (st) return st;
+  // the gather's adjoint
+  return hip_status(launch_scatter_add(row_idx, n, cfg->n_tables, cfg->row_dim, de, gp, s));
 }
 
 }  // namespace
@@ -446,27 +687,11 @@ const char* ngram_status_str(int status) {
 
 int ngram_abi_version(void) { return kAbiVersion; }
 
-int ngram_config_validate(const ngram_config* cfg) { return validate(cfg); }
-
-int ngram_set_timing_events(void* const* events, int n) {
-  if (n == 0) {
-    g_stage_events_on = false;
-    return NGRAM_OK;
-  }
-  if (n != 2 * NGRAM_N_STAGES || events == nullptr) return NGRAM_EINVAL;
-  for (int i = 0; i < 2 * NGRAM_N_STAGES; ++i) {
-    if (events[i] == nullptr) return NGRAM_EINVAL;
-    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
-  }
-  g_stage_events_on = true;
-  return NGRAM_OK;
-}
-
-int ngram_timing_stage_mask(void) { return g_stage_mask; }
+int ngram_config_validate(const ngram_config* cfg) { return validate(cfg, true); }
 
 int ngram_compress_ids(const ngram_config* cfg, const int32_t* raw_ids, int64_t n,
                        const int32_t* lut, int32_t* comp_ids, int32_t* err_flag, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, false);
   if (st) return st;
   if (n < 0) return NGRAM_ESHAPE;
   if (n == 0) return NGRAM_OK;
@@ -480,7 +705,7 @@ int ngram_compress_ids(const ngram_config* cfg, const int32_t* raw_ids, int64_t 
 
 int ngram_hash(const ngram_config* cfg, const int32_t* comp_ids, int32_t B, int32_t T,
                const int32_t* history, int32_t* row_idx, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
   if ((int64_t)B * T == 0) return NGRAM_OK;
@@ -493,7 +718,7 @@ int ngram_hash(const ngram_config* cfg, const int32_t* comp_ids, int32_t B, int3
 
 int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
                  const void* const* tables, void* mem, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, false);
   if (st) return st;
   if (n_tok < 0 || n_tok > kMaxTokens) return NGRAM_ESHAPE;
   if (n_tok == 0) return NGRAM_OK;
@@ -507,7 +732,7 @@ int ngram_gather(const ngram_config* cfg, const int32_t* row_idx, int64_t n_tok,
 }
 
 size_t ngram_gate_workspace_size(const ngram_config* cfg, int64_t n_tok) {
-  if (validate(cfg) != NGRAM_OK || n_tok < 0 || n_tok > kMaxTokens) return 0;
+  if (validate(cfg, false) != NGRAM_OK || n_tok < 0 || n_tok > kMaxTokens) return 0;
   return layout_for(cfg, n_tok, false).total;
 }
 
@@ -515,7 +740,7 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
                const void* mem, const void* w_k, const void* w_v, const void* gamma_q,
                const void* gamma_k, int64_t n_tok, float* gates, void* u, void* workspace,
                size_t workspace_bytes, void* stream) {
-  int st = validate(cfg);
+  int st = validate(cfg, false);
   if (st) return st;
   if (n_tok < 0 || n_tok > kMaxTokens) return NGRAM_ESHAPE;
   int64_t h_tok = 0;
@@ -546,164 +771,97 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
 }
 
 int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t T,
-                      const void* conv_w, const void* gamma_u, const float* conv_state,
-                      void* out, void* stream) {
-  int st = validate(cfg);
+                      const void* conv_w, const void* gamma_u, float* conv_state,
+                      const int32_t* state_pos, int32_t flags, void* out, void* stream) {
+  int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if (flags & ~NGRAM_UPDATE_STATE) return NGRAM_EINVAL;
+  if ((flags & NGRAM_UPDATE_STATE) && conv_state == nullptr) return NGRAM_EINVAL;
   if ((int64_t)B * T == 0) return NGRAM_OK;
   if (!u || !conv_w || !out) return NGRAM_EINVAL;
   for (const void* p : {u, conv_w, gamma_u, (const void*)conv_state, (const void*)out})
     if (!aligned16(p)) return NGRAM_EALIGN;
+  if (!aligned4(state_pos)) return NGRAM_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   ConvArgs ca = conv_args_base(cfg);
   ca.u = u;
   ca.conv_w = conv_w;
   ca.gamma_u = gamma_u;
   ca.state = conv_state;
+  ca.state_pos = state_pos;
+  ca.update_state = (flags & NGRAM_UPDATE_STATE) ? 1 : 0;
   ca.out = out;
   ca.B = B;
   ca.T = T;
   ca.tile = conv_tile_for(T);
-  return hip_status(
-      launch_op_conv(cfg->act_dtype, cfg->conv_dilation, ca, static_cast<hipStream_t>(stream)));
+  st = hip_status(launch_op_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+  if (st || !ca.update_state) return st;
+  return hip_status(launch_state_update(cfg->act_dtype, false, cfg->conv_dilation, ca, s));
 }
 
 size_t ngram_forward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T) {
-  if (validate(cfg) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
+  if (validate(cfg, false) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
   return layout_for(cfg, (int64_t)B * T, true, T).total;
+}
+
+int ngram_forward_workspace_view(const ngram_config* cfg, int32_t B, int32_t T,
+                                 ngram_workspace_view* view) {
+  int st = validate(cfg, false);
+  if (st) return st;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  if (view == nullptr) return NGRAM_EINVAL;
+  const Layout L = layout_for(cfg, (int64_t)B * T, true, T);
+  view->row_idx_offset = (int64_t)L.row_idx;
+  view->mem_offset = (int64_t)L.e;
+  view->mem_layout = L.k_split > 0 ? NGRAM_MEM_TILES16 : NGRAM_MEM_ROWS;
+  view->reserved = 0;
+  return NGRAM_OK;
 }
 
 int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
                   const int32_t* history, const int32_t* lut, const void* const* tables,
                   const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                   const void* w_v, const void* conv_w, const void* gamma_q,
-                  const void* gamma_k, const void* gamma_u, const float* conv_state,
-                  int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
-                  size_t workspace_bytes, void* stream) {
-  const TimedCall timed;
-  int st = validate(cfg);
-  if (st) return st;
-  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
-  if (flags & ~NGRAM_ADD_RESIDUAL) return NGRAM_EINVAL;
-  int64_t h_tok = 0;
-  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
-  if (st) return st;
-  const int64_t n_tok = (int64_t)B * T;
-  if (n_tok == 0) return NGRAM_OK;
-  if (!raw_ids || !lut || !hidden || !w_k || !w_v || !conv_w || !out) return NGRAM_EINVAL;
-  TablePtrs tp;
-  st = check_tables(cfg, tables, &tp);
-  if (st) return st;
-  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut) || !aligned4(err_flag))
-    return NGRAM_EALIGN;
-  for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u,
-                        (const void*)conv_state, (const void*)out, (const void*)gates})
-    if (!aligned16(p)) return NGRAM_EALIGN;
-  const Layout L = layout_for(cfg, n_tok, true, T);
-  if (!workspace) return NGRAM_EWORKSPACE;
-  if (workspace_bytes < L.total) return NGRAM_EWORKSPACE;
-  if (!aligned16(workspace)) return NGRAM_EALIGN;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if (L.k_split > 0) {
-    // decode: hash + gather -> E, weight-stationary projection, decode finalize
-    const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
-    void* e = ws + L.e;
-    float* split = reinterpret_cast<float*>(ws + L.split);
-    stage(1);
-    st = hip_status(launch_hash_gather(cfg->table_dtype, raw_ids, B, T, history, lut, ha,
-                                       cfg->n_tables, cfg->row_dim, tp, e, err_flag, s));
-    if (st) return st;
-    stage(2);
-    WstatArgs wa{};
-    wa.e = static_cast<const bf16_bits*>(e);
-    wa.wk = static_cast<const bf16_bits*>(w_k);
-    wa.wv = static_cast<const bf16_bits*>(w_v);
-    wa.M = n_tok;
-    wa.K = cfg->mem_dim;
-    wa.nb = cfg->n_branches;
-    wa.d = cfg->hidden_dim;
-    wa.split_out = split;
-    st = hip_status(launch_projection_wstat(L.wplan, wa, s));
-    if (st) return st;
-    stage(3);
-    ConvArgs ca = conv_args_base(cfg);
-    ca.conv_w = conv_w;
-    ca.gamma_u = gamma_u;
-    ca.gamma_q = gamma_q;
-    ca.gamma_k = gamma_k;
-    ca.state = conv_state;
-    ca.hidden = hidden;
-    ca.h_tok_stride = h_tok;
-    ca.h_branch_stride = hidden_branch_stride;
-    ca.out = out;
-    ca.gates = gates;
-    ca.B = B;
-    ca.T = T;
-    ca.dil = cfg->conv_dilation;
-    ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
-    return hip_status(launch_decode_finalize(cfg->act_dtype, L.k_split, split, ca, s));
-  }
-  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
-  void* e = ws + L.e;
-
-  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
-  const ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
-                                gamma_k, ws, L, n_tok);
-  if (fused_gather(cfg)) {
-    // hash + gather + projection in one launch
-    AsyncProjArgs aa = async_args(cfg, pa);
-    aa.e = nullptr;
-    aa.ids = raw_ids;
-    aa.hist = history;
-    aa.lut = lut;
-    aa.err = err_flag;
-    aa.T = T;
-    aa.hash = ha;
-    aa.tabs = tp;
-    stage(2);
-    st = hip_status(launch_projection_async(true, L.async, aa, s));
-    if (st) return st;
-  } else {
-    stage(0);
-    st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
-    if (st) return st;
-    stage(1);
-    st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim,
-                                  tp, e, s));
-    if (st) return st;
-    stage(2);
-    st = hip_status(run_projection(cfg, L, pa, s));
-    if (st) return st;
-  }
-  stage(3);
-  ConvArgs ca = conv_args_base(cfg);
-  ca.v = reinterpret_cast<const float*>(ws + L.v) + L.v_offset;
-  ca.v_stride = L.v_stride;
-  ca.parts = reinterpret_cast<const float*>(ws + L.parts);
-  ca.np = L.plan.np;
-  ca.conv_w = conv_w;
-  ca.gamma_u = gamma_u;
-  ca.state = conv_state;
-  ca.hidden = hidden;
-  ca.h_tok_stride = h_tok;
-  ca.h_branch_stride = hidden_branch_stride;
-  ca.out = out;
-  ca.gates = gates;
-  ca.B = B;
-  ca.T = T;
-  ca.tile = conv_tile_for(T);
-  ca.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
-  return hip_status(launch_fused_conv(cfg->act_dtype, cfg->conv_dilation, ca, s));
+                  const void* gamma_k, const void* gamma_u, float* conv_state,
+                  const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                  int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream) {
+  Timer tm;
+  return forward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
+                      w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
+                      out, gates, err_flag, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream), tm);
 }
 
-// ---------------------------------------------------------------------------
-// backward
-// ---------------------------------------------------------------------------
+int ngram_forward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                        const int32_t* history, const int32_t* lut, const void* const* tables,
+                        const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                        const void* w_v, const void* conv_w, const void* gamma_q,
+                        const void* gamma_k, const void* gamma_u, float* conv_state,
+                        const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                        int32_t* err_flag, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* stage_events, int32_t* stage_mask) {
+  if (stage_events == nullptr) return NGRAM_EINVAL;
+  for (int i = 0; i < 2 * NGRAM_N_STAGES; ++i)
+    if (stage_events[i] == nullptr) return NGRAM_EINVAL;
+  int st;
+  int mask;
+  {
+    Timer tm;
+    tm.ev = reinterpret_cast<const hipEvent_t*>(stage_events);
+    st = forward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
+                      w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
+                      out, gates, err_flag, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream), tm);
+    tm.close();
+    mask = tm.mask;
+  }
+  if (stage_mask) *stage_mask = mask;
+  return st;
+}
 
 size_t ngram_backward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T) {
-  if (validate(cfg) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
+  if (validate(cfg, false) != NGRAM_OK || B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return 0;
   return bwd_layout(cfg, (int64_t)B * T).total;
 }
 
@@ -712,128 +870,44 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
                    const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                    const void* w_v, const void* conv_w, const void* gamma_q,
                    const void* gamma_k, const void* gamma_u, const float* conv_state,
-                   int32_t flags, const void* d_out, float* const* d_tables, float* d_w_k,
-                   float* d_w_v, float* d_conv_w, float* d_hidden, float* d_gammas,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  const TimedCall timed;
-  int st = validate(cfg);
-  if (st) return st;
-  if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM) return NGRAM_EDTYPE;
-  if (cfg->hidden_dim % 64 != 0 || cfg->hidden_dim > 4096) return NGRAM_ESHAPE;
-  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
-  if (flags & ~NGRAM_ADD_RESIDUAL) return NGRAM_EINVAL;
-  int64_t h_tok = 0;
-  st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
-  if (st) return st;
-  const int64_t n = (int64_t)B * T;
-  if (n == 0) return NGRAM_OK;
-  if (!raw_ids || !lut || !hidden || !w_k || !w_v || !conv_w || !d_out || !d_tables || !d_w_k ||
-      !d_w_v || !d_conv_w)
-    return NGRAM_EINVAL;
-  TablePtrs tp;
-  st = check_tables(cfg, tables, &tp);
-  if (st) return st;
-  GradTablePtrs gp;
-  memset(&gp, 0, sizeof gp);
-  for (int j = 0; j < cfg->n_tables; ++j) {
-    if (d_tables[j] == nullptr) return NGRAM_EINVAL;
-    if (!aligned16(d_tables[j])) return NGRAM_EALIGN;
-    gp.p[j] = d_tables[j];
+                   const int32_t* state_pos, int32_t flags, const void* d_out,
+                   float* const* d_tables, float* d_w_k, float* d_w_v, float* d_conv_w,
+                   float* d_hidden, float* d_gammas, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  Timer tm;
+  return backward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
+                       w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
+                       d_out, d_tables, d_w_k, d_w_v, d_conv_w, d_hidden, d_gammas, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream), tm);
+}
+
+int ngram_backward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                         const int32_t* history, const int32_t* lut, const void* const* tables,
+                         const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                         const void* w_v, const void* conv_w, const void* gamma_q,
+                         const void* gamma_k, const void* gamma_u, const float* conv_state,
+                         const int32_t* state_pos, int32_t flags, const void* d_out,
+                         float* const* d_tables, float* d_w_k, float* d_w_v, float* d_conv_w,
+                         float* d_hidden, float* d_gammas, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* stage_events,
+                         int32_t* stage_mask) {
+  if (stage_events == nullptr) return NGRAM_EINVAL;
+  for (int i = 0; i < 2 * NGRAM_N_STAGES; ++i)
+    if (stage_events[i] == nullptr) return NGRAM_EINVAL;
+  int st;
+  int mask;
+  {
+    Timer tm;
+    tm.ev = reinterpret_cast<const hipEvent_t*>(stage_events);
+    st = backward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
+                       w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
+                       d_out, d_tables, d_w_k, d_w_v, d_conv_w, d_hidden, d_gammas, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream), tm);
+    tm.close();
+    mask = tm.mask;
   }
-  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut)) return NGRAM_EALIGN;
-  for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, d_out,
-                        (const void*)conv_state, (const void*)d_w_k, (const void*)d_w_v,
-                        (const void*)d_conv_w, (const void*)d_hidden, (const void*)d_gammas})
-    if (!aligned16(p)) return NGRAM_EALIGN;
-  const BwdLayout L = bwd_layout(cfg, n);
-  // the dW products index their [., n_pad] operands with 32-bit offsets
-  if ((int64_t)(cfg->n_branches + 1) * cfg->hidden_dim * L.n_pad >= (int64_t(1) << 31) ||
-      (int64_t)cfg->mem_dim * L.n_pad >= (int64_t(1) << 31))
-    return NGRAM_ESHAPE;
-  if (!workspace || workspace_bytes < L.total) return NGRAM_EWORKSPACE;
-  if (!aligned16(workspace)) return NGRAM_EALIGN;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const int nb = cfg->n_branches, d = cfg->hidden_dim, mem = cfg->mem_dim;
-  const int32_t N = (nb + 1) * d;
-  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
-  bf16_bits* e = reinterpret_cast<bf16_bits*>(ws + L.e);
-  float* kv = reinterpret_cast<float*>(ws + L.kv);
-  bf16_bits* dkv = reinterpret_cast<bf16_bits*>(ws + L.dkv);
-  bf16_bits* wt = reinterpret_cast<bf16_bits*>(ws + L.wt);
-  float* de = reinterpret_cast<float*>(ws + L.de);
-  bf16_bits* dkvt = reinterpret_cast<bf16_bits*>(ws + L.dkvt);
-  bf16_bits* et = reinterpret_cast<bf16_bits*>(ws + L.et);
-  const bf16_bits* wk = static_cast<const bf16_bits*>(w_k);
-  const bf16_bits* wv = static_cast<const bf16_bits*>(w_v);
-
-  // recompute: row ids, E, and K / V in fp32
-  stage(0);
-  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
-  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, nullptr, s));
-  if (st) return st;
-  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n, cfg->n_tables, cfg->row_dim, tp, e, s));
-  if (st) return st;
-  st = hip_status(raw_gemm(e, n, mem, wk, wv, nb, d, kv, N, s));
-  if (st) return st;
-  // the per-row backward: gates, conv, RMSNorms -> dK, dV (bf16), d_hidden, d_conv_w, d_gammas
-  stage(1);
-  BwdArgs ba;
-  memset(&ba, 0, sizeof ba);
-  ba.n = n;
-  ba.T = T;
-  ba.nb = nb;
-  ba.d = d;
-  ba.dil = cfg->conv_dilation;
-  ba.eps = cfg->rms_eps;
-  ba.hidden = static_cast<const bf16_bits*>(hidden);
-  ba.h_tok = h_tok;
-  ba.h_br = hidden_branch_stride;
-  ba.kv = kv;
-  ba.kv_ld = N;
-  ba.stats = reinterpret_cast<float*>(ws + L.stats);
-  ba.dc = reinterpret_cast<float*>(ws + L.dc);
-  ba.d_out = static_cast<const bf16_bits*>(d_out);
-  ba.conv_w = static_cast<const bf16_bits*>(conv_w);
-  ba.gamma_q = static_cast<const bf16_bits*>(gamma_q);
-  ba.gamma_k = static_cast<const bf16_bits*>(gamma_k);
-  ba.gamma_u = static_cast<const bf16_bits*>(gamma_u);
-  ba.state = conv_state;
-  ba.add_residual = (flags & NGRAM_ADD_RESIDUAL) ? 1 : 0;
-  ba.dkv = dkv;
-  ba.dkv_ld = N;
-  ba.d_hidden = d_hidden;
-  ba.part_conv = reinterpret_cast<float*>(ws + L.part);
-  ba.part_gain = d_gammas ? ba.part_conv + (size_t)kBwdBlocks * 4 * d : nullptr;
-  st = hip_status(launch_bwd_rows(ba, d_conv_w, d_gammas, reinterpret_cast<float*>(ws + L.rtmp),
-                                  s));
-  if (st) return st;
-  // dE = [dK dV] [W_K; W_V]: the weights transposed to [mem, N] feed the product
-  stage(2);
-  st = hip_status(launch_transpose_bf16(wk, (int64_t)nb * d, mem, mem, wt, (int64_t)nb * d, N, s));
-  if (st) return st;
-  st = hip_status(launch_transpose_bf16(wv, d, mem, mem, wt + (int64_t)nb * d, d, N, s));
-  if (st) return st;
-  st = hip_status(raw_gemm(dkv, n, N, nullptr, wt, 0, mem, de, mem, s));
-  if (st) return st;
-  // dW = [dK dV]^T E: both operands transposed to [., n_pad], tokens padded with zeros
-  stage(3);
-  st = hip_status(launch_transpose_bf16(dkv, n, N, N, dkvt, L.n_pad, L.n_pad, s));
-  if (st) return st;
-  st = hip_status(launch_transpose_bf16(e, n, mem, mem, et, L.n_pad, L.n_pad, s));
-  if (st) return st;
-  // one split-K product for every row of [dK dV]^T, the splits summed into d_w_k and d_w_v
-  float* dw = reinterpret_cast<float*>(ws + L.dw);
-  st = hip_status(raw_gemm(dkvt, N, (int32_t)L.n_pad, nullptr, et, 0, mem, dw, mem, s, L.dw_split));
-  if (st) return st;
-  const int64_t kw = (int64_t)nb * d * mem;
-  st = hip_status(launch_sum_splits(dw, L.dw_split, N * mem, kw, d_w_k, s));
-  if (st) return st;
-  st = hip_status(launch_sum_splits(dw + kw, L.dw_split, N * mem, (int64_t)d * mem, d_w_v, s));
-  if (st) return st;
-  // the gather's adjoint
-  return hip_status(launch_scatter_add(row_idx, n, cfg->n_tables, cfg->row_dim, de, gp, s));
+  if (stage_mask) *stage_mask = mask;
+  return st;
 }
 
 }  // extern "C"

@@ -130,8 +130,8 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a) {
 }
 
 // 2. dC = dOut (.) SiLU'(C) per token and branch, C = sum_i w_i (.) N_{t-i*dil}
-// with N = gamma_u g V / r inside the sequence, the caller's state rows before
-// it (zeros without a state), and the taps' gradient d_w[i] = sum dC (.)
+// with N = gamma_u g V / r inside the sequence, the caller's ring rows before
+// it (zeros without a ring, or before the sequence's start), and the taps' gradient d_w[i] = sum dC (.)
 // N_{t-i*dil}.  A workgroup walks a tile of kBwdTile positions of one sequence
 // and branch (plus the 3*dil positions before it) with each thread owning
 // four columns, as the forward conv does: every V row is read once into a
@@ -177,12 +177,15 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < R; ++u) ring[u] = mk4(0.0f);
       if (qs < 0 && a.state) {
+        const int pos = ring_pos(a.state_pos, b, HALO);
 #pragma unroll
         for (int u = 0; u < HALO; ++u) {
           int q = qs + u;
           q = q < -HALO ? -HALO : (q > -1 ? -1 : q);
-          const float4 sv = ld4(a.state + ((b * HALO + HALO + q) * nb + br) * (int64_t)d + c0);
-          if (qs + u < 0) ring[u] = sv;
+          const int slot = ring_slot(pos, q, HALO);
+          const float4 sv =
+              ld4(a.state + ((b * HALO + (slot < 0 ? 0 : slot)) * nb + br) * (int64_t)d + c0);
+          if (qs + u < 0 && slot >= 0) ring[u] = sv;
         }
       }
       float4 dw0 = mk4(0.0f), dw1 = mk4(0.0f), dw2 = mk4(0.0f), dw3 = mk4(0.0f);

@@ -44,6 +44,54 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
+// Row partials of one position folded by a 16-lane group (lane sub of 16):
+// the gate's dot product, sum k^2, sum h^2 of branch br and sum v^2, summed
+// over the np partials in a fixed order and combined across the group.
+struct RowSums {
+  float dot, kk, hh, vv;
+};
+__device__ __forceinline__ RowSums fold_partials16(const float* pr, int np, int br, int nb,
+                                                   int sub) {
+  RowSums r{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p = sub; p < np; p += 16) {
+    r.dot += pr[(3 * br) * np + p];
+    r.kk += pr[(3 * br + 1) * np + p];
+    r.hh += pr[(3 * br + 2) * np + p];
+    r.vv += pr[(3 * nb) * np + p];
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) {
+    r.dot += __shfl_xor(r.dot, off);
+    r.kk += __shfl_xor(r.kk, off);
+    r.hh += __shfl_xor(r.hh, off);
+    r.vv += __shfl_xor(r.vv, off);
+  }
+  return r;
+}
+
+// Gate of a position and the factor that turns its V row into the
+// normalised row N = gamma_u (.) U / rms(U) (with U = g V, rms(U)^2 =
+// g^2 mean(v^2) + eps, so N = gamma_u (.) V * g / sqrt(g^2 mean(v^2) + eps)).
+__device__ __forceinline__ void gate_and_scale(const RowSums& r, float fd, float eps, float& al,
+                                               float& sc) {
+  const float z = r.dot / (sqrtf(r.hh / fd + eps) * sqrtf(r.kk / fd + eps) * sqrtf(fd));
+  al = 1.0f / (1.0f + expf(-z));
+  sc = al / sqrtf(al * al * (r.vv / fd) + eps);
+}
+
+// 1 / rms of a U row, one wave (lane of 64) over d columns.
+template <typename T>
+__device__ __forceinline__ float inv_rms_row(const T* row, int d, float eps, int lane) {
+  float ss = 0.0f;
+  for (int c = lane * 4; c < d; c += 256) {
+    const float4 x = Elem<T>::load4(row, c);
+    ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  return 1.0f / sqrtf(ss / (float)d + eps);
+}
+
 // ngram_gate: gates and U = g V in the activation dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_values_kernel(ConvArgs a, int64_t M) {
@@ -120,30 +168,16 @@ __global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
       const int q = qs + i;
       const bool live = i < L && q >= 0;
       const int64_t tok = seq0 + (live ? q : 0);  // any valid row when not live
-      const float* pr = a.parts + tok * nq * a.np;
-      float dot = 0.0f, kk = 0.0f, hh = 0.0f, vv = 0.0f;
-      for (int p = sub; p < a.np; p += 16) {
-        dot += pr[(3 * br) * a.np + p];
-        kk += pr[(3 * br + 1) * a.np + p];
-        hh += pr[(3 * br + 2) * a.np + p];
-        vv += pr[(3 * nb) * a.np + p];
-      }
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        dot += __shfl_xor(dot, off);
-        kk += __shfl_xor(kk, off);
-        hh += __shfl_xor(hh, off);
-        vv += __shfl_xor(vv, off);
-      }
+      const RowSums r = fold_partials16(a.parts + tok * nq * a.np, a.np, br, nb, sub);
       if (sub == 0 && i < L) {
         if (q < 0) {
           s_alpha[i] = 0.0f;
           s_scale[i] = 0.0f;
         } else {
-          const float z = dot / (sqrtf(hh / fd + a.eps) * sqrtf(kk / fd + a.eps) * sqrtf(fd));
-          const float al = 1.0f / (1.0f + expf(-z));
+          float al, sc;
+          gate_and_scale(r, fd, a.eps, al, sc);
           s_alpha[i] = al;
-          s_scale[i] = al / sqrtf(al * al * (vv / fd) + a.eps);
+          s_scale[i] = sc;
           if (a.gates && q >= p0) a.gates[tok * nb + br] = al;
         }
       }
@@ -153,17 +187,7 @@ __global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
     for (int i = wave; i < L; i += nw) {
       const int q = qs + i;
       float sc = 0.0f;
-      if (q >= 0) {
-        const T* row = U + ((seq0 + q) * nb + br) * d;
-        float ss = 0.0f;
-        for (int c = lane * 4; c < d; c += 256) {
-          const float4 x = Elem<T>::load4(row, c);
-          ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-        sc = 1.0f / sqrtf(ss / (float)d + a.eps);
-      }
+      if (q >= 0) sc = inv_rms_row(U + ((seq0 + q) * nb + br) * d, d, a.eps, lane);
       if (lane == 0) {
         s_alpha[i] = 1.0f;
         s_scale[i] = sc;
@@ -177,6 +201,7 @@ __global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
   const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
   T* __restrict__ OUT = static_cast<T*>(a.out);
   const T* __restrict__ H = static_cast<const T*>(a.hidden);
+  const int pos = qs < 0 && a.state ? ring_pos(a.state_pos, b, HALO) : 0;
   for (int c0 = threadIdx.x * 4; c0 < d; c0 += blockDim.x * 4) {
     const float4 w0 = Elem<T>::load4(CW, c0);
     const float4 w1 = Elem<T>::load4(CW, d + c0);
@@ -185,9 +210,10 @@ __global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
     const float4 gu = GU ? Elem<T>::load4(GU, c0) : f4(1.0f);
     // Positions before the sequence occur only in its first tile (qs < 0,
     // p0 == 0), at i < HALO of the first group: the ring starts with the
-    // caller's state rows there (zeros without a state), and the walk
-    // assigns positions q >= 0 only.  No load then sits behind a branch of
-    // the walk, which would make the compiler wait for every load in flight.
+    // caller's state rows there (zeros without a state, or for positions
+    // before the sequence's start), and the walk assigns positions q >= 0
+    // only.  No load then sits behind a branch of the walk, which would make
+    // the compiler wait for every load in flight.
     float4 ring[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) ring[u] = f4(0.0f);
@@ -196,9 +222,10 @@ __global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
       for (int u = 0; u < HALO; ++u) {
         int q = qs + u;
         q = q < -HALO ? -HALO : (q > -1 ? -1 : q);
+        const int slot = ring_slot(pos, q, HALO);
         const float4 st = *reinterpret_cast<const float4*>(
-            a.state + (((int64_t)b * HALO + HALO + q) * nb + br) * d + c0);
-        if (qs + u < 0) ring[u] = st;
+            a.state + (((int64_t)b * HALO + (slot < 0 ? 0 : slot)) * nb + br) * d + c0);
+        if (qs + u < 0 && slot >= 0) ring[u] = st;
       }
     }
     for (int base = 0; base < L; base += R) {
@@ -314,29 +341,35 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
   __syncthreads();
 
   const float fd = (float)d;
-  const float mv = s_tot[3 * NGRAM_MAX_BRANCHES] / fd;
   const T* __restrict__ CW = static_cast<const T*>(a.conv_w);
   const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
   T* __restrict__ OUT = static_cast<T*>(a.out);
   const int halo = 3 * dil;
+  const int pos = a.state ? ring_pos(a.state_pos, tok, halo) : 0;
   for (int br = 0; br < nb; ++br) {
-    const float z = s_tot[3 * br] /
-                    (sqrtf(s_tot[3 * br + 2] / fd + a.eps) * sqrtf(s_tot[3 * br + 1] / fd + a.eps) *
-                     sqrtf(fd));
-    const float al = 1.0f / (1.0f + expf(-z));
-    const float sc = al / sqrtf(al * al * mv + a.eps);
+    RowSums r{s_tot[3 * br], s_tot[3 * br + 1], s_tot[3 * br + 2], s_tot[3 * NGRAM_MAX_BRANCHES]};
+    float al, sc;
+    gate_and_scale(r, fd, a.eps, al, sc);
     if (a.gates && threadIdx.x == 0) a.gates[tok * nb + br] = al;
     // pass 2: outputs
     for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
       const float4 v = col4((int64_t)nb * d, c);
       const float4 gu = GU ? Elem<T>::load4(GU, c) : f4(1.0f);
-      float4 C = mul4(Elem<T>::load4(CW, c), mul4(mul4(gu, v), f4(sc)));
+      const float4 nrm = mul4(mul4(gu, v), f4(sc));  // this position's normalised row
+      float4 C = mul4(Elem<T>::load4(CW, c), nrm);
       if (a.state) {
+        // taps at positions -dil, -2 dil, -3 dil from the ring, zero before
+        // the sequence's start; every read precedes the write below
         for (int i = 1; i < 4; ++i) {
-          const float4 st = *reinterpret_cast<const float4*>(
-              a.state + ((tok * halo + halo - i * dil) * nb + br) * d + c);
-          C = fma4(Elem<T>::load4(CW, (int64_t)i * d + c), st, C);
+          const int slot = ring_slot(pos, -i * dil, halo);
+          if (slot >= 0) {
+            const float4 st = *reinterpret_cast<const float4*>(
+                a.state + ((tok * halo + slot) * nb + br) * d + c);
+            C = fma4(Elem<T>::load4(CW, (int64_t)i * d + c), st, C);
+          }
         }
+        if (a.update_state)
+          *reinterpret_cast<float4*>(a.state + ((tok * halo + pos % halo) * nb + br) * d + c) = nrm;
       }
       float4 D = make_float4(fmaf(al, v.x, silu(C.x)), fmaf(al, v.y, silu(C.y)),
                              fmaf(al, v.z, silu(C.z)), fmaf(al, v.w, silu(C.w)));
@@ -457,36 +490,96 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
   __syncthreads();
 
   const float fd = (float)d;
-  const float mv = s_tot[3 * NB] / fd;
   T* __restrict__ OUT = static_cast<T*>(a.out);
   const int halo = 3 * dil;
-  float4 w0[ITEMS];
+  const int pos = a.state ? ring_pos(a.state_pos, tok, halo) : 0;
+  float4 gun[ITEMS];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    w0[i] = mul4(cw0[i], gain(gu[i], has_gu));
-  }
+  for (int i = 0; i < ITEMS; ++i) gun[i] = gain(gu[i], has_gu);
 #pragma unroll
   for (int br = 0; br < NB; ++br) {
-    const float z = s_tot[3 * br] /
-                    (sqrtf(s_tot[3 * br + 2] / fd + a.eps) * sqrtf(s_tot[3 * br + 1] / fd + a.eps) *
-                     sqrtf(fd));
-    const float al = 1.0f / (1.0f + expf(-z));
-    const float sc = al / sqrtf(al * al * mv + a.eps);
+    RowSums r{s_tot[3 * br], s_tot[3 * br + 1], s_tot[3 * br + 2], s_tot[3 * NB]};
+    float al, sc;
+    gate_and_scale(r, fd, a.eps, al, sc);
     if (a.gates && threadIdx.x == 0) a.gates[tok * NB + br] = al;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      float4 C = mul4(w0[i], mul4(v[i], f4(sc)));
+      const float4 nrm = mul4(mul4(gun[i], v[i]), f4(sc));  // this position's normalised row
+      float4 C = mul4(cw0[i], nrm);
       if (a.state) {
+        // taps at positions -dil, -2 dil, -3 dil from the ring, zero before
+        // the sequence's start; every read precedes the write below
         for (int t = 1; t < 4; ++t) {
-          const float4 st = *reinterpret_cast<const float4*>(
-              a.state + ((tok * halo + halo - t * dil) * NB + br) * d + col[i]);
-          C = fma4(Elem<T>::load4(CW, (int64_t)t * d + col[i]), st, C);
+          const int slot = ring_slot(pos, -t * dil, halo);
+          if (slot >= 0) {
+            const float4 st = *reinterpret_cast<const float4*>(
+                a.state + ((tok * halo + slot) * NB + br) * d + col[i]);
+            C = fma4(Elem<T>::load4(CW, (int64_t)t * d + col[i]), st, C);
+          }
         }
+        if (a.update_state && ok[i])
+          *reinterpret_cast<float4*>(a.state + ((tok * halo + pos % halo) * NB + br) * d + col[i]) =
+              nrm;
       }
       float4 D = make_float4(fmaf(al, v[i].x, silu(C.x)), fmaf(al, v[i].y, silu(C.y)),
                              fmaf(al, v[i].z, silu(C.z)), fmaf(al, v[i].w, silu(C.w)));
       if (a.add_residual) D = add4(D, h[br][i]);
       if (ok[i]) Elem<T>::store4(OUT, (tok * NB + br) * d + col[i], D);
+    }
+  }
+}
+
+// Ring update after a conv over a [B, T] grid: the normalised rows of the last
+// min(T, 3*DIL) positions of sequence blockIdx.x, branch blockIdx.y, into
+// their slots.  The scalars come from the same folds as the conv's (so the
+// rows equal the ones the conv used): from V and the partials (FUSED) or
+// from the U rows.
+template <int DIL, typename T, bool FUSED>
+__global__ __launch_bounds__(256) void state_update_kernel(ConvArgs a) {
+  constexpr int HALO = 3 * DIL;
+  __shared__ float s_scale[HALO];
+  const int64_t b = blockIdx.x;
+  const int br = blockIdx.y;
+  const int nb = a.nb, d = a.d;
+  const int n = a.T < HALO ? a.T : HALO;  // rows written
+  const int q0 = a.T - n;                  // first position written
+  const int64_t seq0 = b * a.T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (FUSED) {
+    const int sub = lane & 15, grp = lane >> 4;
+    for (int i0 = wave * 4; i0 < n; i0 += nw * 4) {
+      const int i = i0 + grp;
+      const int64_t tok = seq0 + q0 + (i < n ? i : 0);
+      const RowSums r = fold_partials16(a.parts + tok * (3 * nb + 1) * a.np, a.np, br, nb, sub);
+      if (sub == 0 && i < n) {
+        float al, sc;
+        gate_and_scale(r, (float)d, a.eps, al, sc);
+        s_scale[i] = sc;
+      }
+    }
+  } else {
+    const T* U = static_cast<const T*>(a.u);
+    for (int i = wave; i < n; i += nw) {
+      const float sc = inv_rms_row(U + ((seq0 + q0 + i) * nb + br) * d, d, a.eps, lane);
+      if (lane == 0) s_scale[i] = sc;
+    }
+  }
+  __syncthreads();
+  const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
+  const int pos = ring_pos(a.state_pos, b, HALO);
+  for (int c0 = threadIdx.x * 4; c0 < d; c0 += blockDim.x * 4) {
+    const float4 gu = GU ? Elem<T>::load4(GU, c0) : f4(1.0f);
+    for (int i = 0; i < n; ++i) {
+      const int64_t tok = seq0 + q0 + i;
+      float4 src;
+      if (FUSED) {
+        src = *reinterpret_cast<const float4*>(a.v + tok * a.v_stride + c0);
+      } else {
+        src = Elem<T>::load4(static_cast<const T*>(a.u), (tok * nb + br) * d + c0);
+      }
+      const int slot = (pos + q0 + i) % HALO;
+      *reinterpret_cast<float4*>(a.state + ((b * HALO + slot) * nb + br) * d + c0) =
+          mul4(mul4(gu, src), f4(s_scale[i]));
     }
   }
 }
@@ -591,6 +684,26 @@ hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split
     return launch(decode_finalize_kernel<bf16_bits>, (unsigned)a.B, 256, 0, s, a, split, k_split,
                   a.dil);
   return launch(decode_finalize_kernel<float>, (unsigned)a.B, 256, 0, s, a, split, k_split, a.dil);
+}
+
+hipError_t launch_state_update(int dtype, bool fused, int32_t dil, const ConvArgs& a,
+                               hipStream_t s) {
+  if (a.B == 0 || a.T == 0 || a.state == nullptr) return hipSuccess;
+  const dim3 grid((unsigned)a.B, (unsigned)a.nb);
+#define NGRAM_SU(D)                                                                         \
+  if (dtype == NGRAM_BF16)                                                                  \
+    return fused ? launch(state_update_kernel<D, bf16_bits, true>, grid, 256, 0, s, a)      \
+                 : launch(state_update_kernel<D, bf16_bits, false>, grid, 256, 0, s, a);    \
+  return fused ? launch(state_update_kernel<D, float, true>, grid, 256, 0, s, a)            \
+               : launch(state_update_kernel<D, float, false>, grid, 256, 0, s, a)
+  switch (dil) {
+    case 1: NGRAM_SU(1);
+    case 2: NGRAM_SU(2);
+    case 3: NGRAM_SU(3);
+    case 4: NGRAM_SU(4);
+    default: return hipErrorInvalidValue;
+  }
+#undef NGRAM_SU
 }
 
 int conv_tile_for(int32_t T) { return T < kMaxTile ? T : kMaxTile; }

@@ -129,7 +129,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 // table's row id from lane j with a cross-lane read before the loads above.
 // E is written in the decode projection's operand order (internal.h,
 // "decode E tiles"), so that kernel reads each 16-row x 32-k operand of
-// v_mfma_f32_16x16x32_bf16 as one contiguous kilobyte.
+// v_mfma_f32_16x16x32_bf16 as one contiguous kilobyte.  The row ids go to
+// row_idx as well (32 bytes a token), when it is given.
 //
 // WPT waves share one token (a few hundred tokens cannot otherwise occupy
 // every CU): each hashes all of the token's tables and fetches 1 / WPT of its
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
                                                           const int32_t* __restrict__ lut, HashArgs h,
                                                           int32_t row_chunks, TablePtrs tabs,
                                                           uint4* __restrict__ mem,
+                                                          int32_t* __restrict__ row_idx,
                                                           int32_t* __restrict__ err) {
   __shared__ gchunk* s_tab[NGRAM_MAX_TABLES];
   __shared__ float s_scale[NGRAM_MAX_TABLES];
@@ -177,6 +179,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
     const bool bad = compress_context<true>(ctx, lut, h, c);
     ctx = ctx_of(tok + tstride);  // the next token's ids, in flight during this one
     const int32_t my_row = (int32_t)table_row(rh, c);
+    if (row_idx && part == 0 && lane < h.n_tables) row_idx[tok * h.n_tables + lane] = my_row;
     uint4* dst = mem + (tok >> 4) * n_kk * 64 + (tok & 15);
     // E chunk e (16 bytes, 8 bf16): K step e/4, quarter e%4
     auto put = [&](int e, const uint4& x) { dst[(e >> 2) * 64 + (e & 3) * 16] = x; };
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
 hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t T,
                               const int32_t* hist, const int32_t* lut, const HashArgs& h,
                               int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,
-                              int32_t* err, hipStream_t s) {
+                              int32_t* row_idx, int32_t* err, hipStream_t s) {
   // the tiled E layout is defined for bf16 E of whole 32-wide K steps
   if ((dtype != NGRAM_BF16 && dtype != NGRAM_FP8_E4M3) || (n_tables * row_dim) % 32 != 0)
     return hipErrorInvalidValue;
@@ -234,7 +237,7 @@ hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t 
   uint4* m = static_cast<uint4*>(mem);
 #define NGRAM_HG(F, W)                                                                     \
   return launch(hash_gather_kernel<F, W>, (unsigned)blocks, 256, 0, s, ids, B, T, hist, lut, h, \
-                row_chunks, t, m, err)
+                row_chunks, t, m, row_idx, err)
 #define NGRAM_HG_W(F)       \
   switch (wpt) {            \
     case 4: NGRAM_HG(F, 4); \

@@ -152,18 +152,10 @@ struct EpiArgs {
   int32_t d, nb, np;
 };
 
-// Projection with operands copied global -> LDS (W stored [d, mem]).  The A
-// operand is E [M, K] (e != nullptr) or gathered from the tables after
-// hashing raw ids in-kernel (e == nullptr).
+// Projection with operands copied global -> LDS (W stored [d, mem]); the A
+// operand is E [M, K].
 struct AsyncProjArgs {
   const bf16_bits* e;
-  const int32_t* ids;        // raw ids [B, T]
-  const int32_t* hist;       // raw history [B, max_order-1] or nullptr
-  const int32_t* lut;
-  int32_t* err;
-  int32_t T, row_dim;
-  HashArgs hash;
-  TablePtrs tabs;
   const bf16_bits* wk;       // [nb, d, K]
   const bf16_bits* wv;       // [d, K]
   EpiArgs epi;
@@ -190,7 +182,13 @@ struct ConvArgs {
   const void* u;          // op: [M, nb, d] act dtype
   const void* conv_w;     // [4, d] act dtype
   const void* gamma_u;    // [d] nullable
-  const float* state;     // [B, 3*dil, nb, d] nullable
+  // conv-state ring [B, 3*dil, nb, d] (nullable): the normalised row of
+  // absolute position p in slot p mod 3*dil; state_pos[b] (nullable = 3*dil)
+  // positions of sequence b precede this call's first token; update_state:
+  // the call writes its last rows into the ring
+  float* state;
+  const int32_t* state_pos;
+  int32_t update_state;
   const void* hidden;     // residual source (flag)
   int64_t h_tok_stride, h_branch_stride;
   void* out;              // [M, nb, d] act dtype
@@ -203,19 +201,34 @@ struct ConvArgs {
   const void* gamma_k;
 };
 
+// Ring slot of the row at position q (< 0, relative to the call's first
+// token) of a sequence whose ring position is pos (state_pos, >= 0), or -1
+// when that position lies before the start of the sequence.
+__device__ __forceinline__ int ring_slot(int pos, int q, int ring) {
+  const int p = pos + q;
+  return p < 0 ? -1 : p % ring;
+}
+__device__ __forceinline__ int ring_pos(const int32_t* state_pos, int64_t b, int ring) {
+  if (state_pos == nullptr) return ring;
+  const int p = state_pos[b];
+  return p < 0 ? 0 : p;
+}
+
 // ---------------------------------------------------------------------------
 // kernel launch
 // ---------------------------------------------------------------------------
-// Every kernel goes through launch(): a plain launch unless a timed stage is
-// open (benchmark instrumentation, ngram_set_timing_events), in which case
-// the stage's first kernel stamps its begin time into the stage's start event
-// and each of its kernels stamps its end time into the stop event, so the
-// event pair spans exactly the stage's kernels.
+// Every kernel goes through launch(): a plain launch unless the calling
+// thread is inside an instrumented entry point (ngram_forward_timed /
+// ngram_backward_timed) with a stage open, in which case the stage's first
+// kernel stamps its begin time into the stage's start event and each of its
+// kernels stamps its end time into the stop event, so the event pair spans
+// exactly the stage's kernels.  The open stage is thread-local and set only
+// for the duration of such a call.
 struct StageClock {
   hipEvent_t start, stop;
   int launches;
 };
-extern StageClock* g_open_stage;
+extern thread_local StageClock* t_open_stage;
 
 template <typename T>
 struct same_type {
@@ -227,7 +240,7 @@ inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t s
                          hipStream_t s, typename same_type<P>::type... args) {
   void* argv[] = {static_cast<void*>(&args)...};
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (StageClock* c = g_open_stage) {
+  if (StageClock* c = t_open_stage) {
     e0 = c->launches == 0 ? c->start : nullptr;
     e1 = c->stop;
     ++c->launches;
@@ -258,7 +271,8 @@ struct BwdArgs {
   const bf16_bits* gamma_q;         // nullable (= 1)
   const bf16_bits* gamma_k;
   const bf16_bits* gamma_u;
-  const float* state;               // [B, 3*dil, nb, d] normalised rows, or nullptr
+  const float* state;               // conv-state ring [B, 3*dil, nb, d], or nullptr
+  const int32_t* state_pos;         // ring positions [B] (nullptr = 3*dil)
   int32_t add_residual;
   bf16_bits* dkv;                   // [n, dkv_ld]: dK of each branch, then dV (bf16)
   int64_t dkv_ld;
@@ -304,10 +318,11 @@ struct ProjPlan {
 ProjPlan plan_projection(int dtype, int64_t M, int32_t d);
 hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a, hipStream_t s);
 
-// plan 0: 256x256 tiles, 1: 128x128, 2: 64x64; wave_cols = partial width.
-int async_plan(int64_t M);
+// Tile plan for M rows (override: a plan id >= 0); wave_cols = partial width.
+constexpr int kAsyncPlans = 12;
+int async_plan(int64_t M, int override_plan);
 int async_wave_cols(int plan);
-hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s);
+hipError_t launch_projection_async(int plan, const AsyncProjArgs& a, hipStream_t s);
 hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s);
 // split-K raw-tile variant for small M (decode); E given densely
 // Decode E tiles: the decode step's E [M, K] bf16 is stored as 1 KB tiles of
@@ -337,17 +352,26 @@ struct WstatArgs {
   float* split_out;
 };
 WstatPlan wstat_plan(int64_t M, int32_t N, int32_t K);
+// whether the kernel can run a plan (LDS block, K slices, ring steps)
+bool wstat_plan_fits(const WstatPlan& plan, int32_t K);
 hipError_t launch_projection_wstat(const WstatPlan& plan, const WstatArgs& a, hipStream_t s);
+// row_idx (nullable): the token's row ids, [n_tok, n_tables]
 hipError_t launch_hash_gather(int dtype, const int32_t* ids, int32_t B, int32_t T,
                               const int32_t* hist, const int32_t* lut, const HashArgs& h,
                               int32_t n_tables, int32_t row_dim, const TablePtrs& t, void* mem,
-                              int32_t* err, hipStream_t s);
+                              int32_t* row_idx, int32_t* err, hipStream_t s);
 hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split, const ConvArgs& a,
                                   hipStream_t s);
 
 hipError_t launch_gate_values(int dtype, const ConvArgs& a, int64_t M, hipStream_t s);
 hipError_t launch_fused_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s);
 hipError_t launch_op_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t s);
+// The ring update after a conv over a [B, T] grid (update_state): the last
+// min(T, 3*dil) normalised rows of each sequence and branch into their slots,
+// recomputed from V and the partials (fused) or from U (op); launched after
+// the conv, whose reads of the ring it must follow.
+hipError_t launch_state_update(int dtype, bool fused, int32_t dil, const ConvArgs& a,
+                               hipStream_t s);
 int conv_tile_for(int32_t T);
 
 }  // namespace ngram

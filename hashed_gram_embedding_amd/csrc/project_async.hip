@@ -11,11 +11,11 @@
 // keeps up to STAGES-1 K steps of copies in flight while the matrix cores
 // work on the current one.
 //
-// GATHER: the kernel hashes its own BM tokens (compression, n-gram keys,
-// multi-head mod-prime hashing) into LDS row ids and the A-operand copies read
-// the table rows directly -- E_t is never materialised, so hash + gather +
-// projection is one launch.  Each 64-wide K step lies inside one table row
-// (row_dim % BK == 0), so a step reads one aligned 128-byte line per token.
+// The A operand is the memory vector E, materialised by the gather kernel.
+// A variant that hashed and gathered its own A operand straight from the
+// tables (E never written) measured slower at every prefill size: the
+// gathered copies lengthen the ring's load latency by more than the E round
+// trip costs.
 //
 // Each ring slot is its own __shared__ array and the K loop is unrolled by
 // the ring depth, so every copy and every operand read names its slot at
@@ -33,9 +33,7 @@
 // gets a contiguous range of tiles, walked in groups of group_m M-tiles with
 // the M index fastest -- concurrently running workgroups of one XCD share A
 // and B slabs in its L2.
-#include <stdlib.h>
-
-#include "hashing.h"
+#include "epilogue.h"
 
 namespace ngram {
 namespace {
@@ -97,7 +95,7 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int ti
   n = sn - seg * tiles_n;
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool GATHER, bool RAW = false>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool RAW = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProjArgs a) {
   constexpr int NW = WGM * WGN;          // waves per workgroup
   constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
@@ -117,7 +115,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   __shared__ __attribute__((aligned(16))) bf16_bits ring1[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_bits ring2[STAGES > 2 ? STAGE_ELEMS : 8];
   __shared__ __attribute__((aligned(16))) bf16_bits ring3[STAGES > 3 ? STAGE_ELEMS : 8];
-  __shared__ int32_t s_rid[GATHER ? BM * NGRAM_MAX_TABLES : 1];
   // slot index is a compile-time constant at every use (unrolled loops)
   auto slot = [&](int sl) -> bf16_bits* {
     // (the placeholder arrays of absent slots stay unreferenced)
@@ -143,25 +140,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   const int K = a.K, d = ep.d;
   const bf16_bits* __restrict__ W = seg < ep.nb ? a.wk + (int64_t)seg * d * K : a.wv;
 
-  if (GATHER) {
-    for (int i = tid; i < BM; i += 64 * NW) {
-      int64_t tok = m0 + i;
-      if (tok > M - 1) tok = M - 1;
-      const int32_t b = (int32_t)(tok / a.T);
-      const int32_t t = (int32_t)(tok - (int64_t)b * a.T);
-      uint64_t c[NGRAM_MAX_ORDER];
-      const bool bad = context_ids<true>(a.ids, tok, b, t, a.hist, a.lut, a.hash, c);
-      for (int o = 0; o < a.hash.n_orders; ++o)
-        for (int k = 0; k < a.hash.heads; ++k) {
-          const int j = o * a.hash.heads + k;
-          s_rid[i * NGRAM_MAX_TABLES + j] = (int32_t)table_row(a.hash, j, a.hash.orders[o], c);
-        }
-      if (bad && a.err) *a.err = 1;
-    }
-    __syncthreads();
-  }
-
-
   const int kt_first = split > 1 ? ksl * (K / BK) / split : 0;
 
   // Copy lanes: lane -> (row lrow of the copy's RPI-row block, 16-byte chunk
@@ -184,26 +162,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     bf16_bits* As = slot(sl);
     bf16_bits* Bs = As + A_ELEMS;
     const int k0 = (kt_first + kt) * BK;
-    int j = 0, cofs = 0;
-    const bf16_bits* tab = nullptr;
-    if (GATHER) {
-      j = k0 / a.row_dim;
-      cofs = k0 - j * a.row_dim;
-      tab = static_cast<const bf16_bits*>(a.tabs.p[j]);
-    }
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int rblk = (wave * A_INS + i) * RPI;
       const int ch8 = lch8 ^ (swz_block<BK>(rblk) << 3);
-      const bf16_bits* src;
-      if (GATHER) {
-        src = tab + (int64_t)s_rid[(rblk + lrow) * NGRAM_MAX_TABLES + j] * a.row_dim + cofs + ch8;
-      } else {
-        int64_t grow = m0 + rblk + lrow;
-        if (grow > M - 1) grow = M - 1;
-        src = a.e + grow * K + k0 + ch8;
-      }
-      copy16_to_lds(src, As + rblk * BK);
+      int64_t grow = m0 + rblk + lrow;
+      if (grow > M - 1) grow = M - 1;
+      copy16_to_lds(a.e + grow * K + k0 + ch8, As + rblk * BK);
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
@@ -345,12 +310,12 @@ hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
   if (split > a.K / BK) return hipErrorInvalidValue;  // every split needs a K step
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n * split;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, true>, (unsigned)blocks,
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>, (unsigned)blocks,
                 64 * WGM * WGN, 0, s, a);
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
-hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
+hipError_t launch_async_t(const AsyncProjArgs& a0, hipStream_t s) {
   constexpr int WTN = BN / WGN;  // columns per wave = width of one row partial
   AsyncProjArgs a = a0;
   // the host sized the partials for this tile's wave width; refuse to launch
@@ -359,10 +324,7 @@ hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
   a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
   a.tiles_n = (a.epi.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
-  if (gather)
-    return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>, (unsigned)blocks,
-                  64 * WGM * WGN, 0, s, a);
-  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false>, (unsigned)blocks,
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN>, (unsigned)blocks,
                 64 * WGM * WGN, 0, s, a);
 }
 
@@ -385,15 +347,10 @@ hipError_t launch_async_t(bool gather, const AsyncProjArgs& a0, hipStream_t s) {
 }  // namespace
 
 // Tile plans (id, BM, BN, K step, ring depth, wave rows, wave columns): see
-// NGRAM_ASYNC_PLANS.  NGRAM_ASYNC_TILE=<id> overrides the choice (a tuning
-// knob).
-int async_plan(int64_t M) {
-  const char* e = getenv("NGRAM_ASYNC_TILE");
-  if (e && *e) {
-    char* end = nullptr;
-    const long v = strtol(e, &end, 10);
-    if (*end == 0 && v >= 0 && v <= 11) return (int)v;
-  }
+// NGRAM_ASYNC_PLANS.  A plan id in [0, kAsyncPlans) overrides the choice (the
+// configuration's tuning field).
+int async_plan(int64_t M, int override_plan) {
+  if (override_plan >= 0 && override_plan < kAsyncPlans) return override_plan;
   // 256 x 256 tiles from 8,192 rows: waves as 4 x 2 (64 x 128 each; 1 %
   // faster than 2 x 4 at Qwen prefill, multibranch and engram sizes)
   if (M >= 8192) return 11;
@@ -410,7 +367,7 @@ int async_wave_cols(int plan) {
 }
 
 // The raw product serves the backward pass; it is built for the default
-// plans only (async_plan without a NGRAM_ASYNC_TILE override).
+// plans only (async_plan without an override).
 hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s) {
   if (a.epi.M == 0) return hipSuccess;
   switch (plan) {
@@ -421,10 +378,10 @@ hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s
   }
 }
 
-hipError_t launch_projection_async(bool gather, int plan, const AsyncProjArgs& a, hipStream_t s) {
+hipError_t launch_projection_async(int plan, const AsyncProjArgs& a, hipStream_t s) {
   if (a.epi.M == 0) return hipSuccess;
 #define NGRAM_LAUNCH_PLAN(id, bm, bn, bk, st, wgm, wgn) \
-  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm, wgn>(gather, a, s);
+  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm, wgn>(a, s);
   NGRAM_ASYNC_PLANS(NGRAM_LAUNCH_PLAN)
 #undef NGRAM_LAUNCH_PLAN
   return hipErrorInvalidValue;

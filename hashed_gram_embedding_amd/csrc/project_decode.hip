@@ -211,15 +211,21 @@ WstatPlan wstat_plan(int64_t M, int32_t N, int32_t K) {
   return best;
 }
 
+// The kernel's copy loop and K-step ring assume these.
+bool wstat_plan_fits(const WstatPlan& plan, int32_t K) {
+  if (plan.ni < 2 || plan.ni > 6 || plan.ring != 4) return false;
+  if (plan.split < 1 || K % plan.split != 0) return false;
+  const int kt = K / plan.split;
+  return kt % 128 == 0 && (int64_t)16 * plan.ni * kt * 2 <= kWstatLdsBytes &&
+         (kt / 32) % plan.ring == 0;
+}
+
 hipError_t launch_projection_wstat(const WstatPlan& plan, const WstatArgs& a0, hipStream_t s) {
   WstatArgs a = a0;
   const int N = (a.nb + 1) * a.d;
   const int nt = 16 * plan.ni;
-  if (plan.split < 1 || a.K % plan.split != 0) return hipErrorInvalidValue;
+  if (!wstat_plan_fits(plan, a.K)) return hipErrorInvalidValue;
   a.kt = a.K / plan.split;
-  // the kernel's copy loop and K-step ring assume these; refuse otherwise
-  if (a.kt % 128 != 0 || (int64_t)nt * a.kt * 2 > kWstatLdsBytes || (a.kt / 32) % plan.ring != 0)
-    return hipErrorInvalidValue;
   a.tiles_n = (N + nt - 1) / nt;
   const int64_t blocks = (int64_t)a.tiles_n * plan.split;
   if (a.M == 0) return hipSuccess;

@@ -16,6 +16,8 @@ MAX_TABLES = 16
 MAX_ORDER = 4
 MAX_BRANCHES = 4
 ADD_RESIDUAL = 1
+UPDATE_STATE = 2
+MEM_ROWS, MEM_TILES16 = 0, 1  # layouts of E in the forward workspace
 F32, BF16, FP8_E4M3 = 0, 1, 2  # FP8_E4M3: table storage only
 W_MEM_D, W_D_MEM = 0, 1  # projection storage: [mem, d] or [d, mem] (fast path)
 
@@ -54,6 +56,19 @@ class NgramConfig(ctypes.Structure):
         ("act_dtype", ctypes.c_int32),
         ("w_layout", ctypes.c_int32),
         ("table_scale", ctypes.c_float * MAX_TABLES),
+        ("tune_proj_plan", ctypes.c_int32),
+        ("tune_decode_ni", ctypes.c_int32),
+        ("tune_decode_split", ctypes.c_int32),
+    ]
+
+
+class NgramWorkspaceView(ctypes.Structure):
+    """Mirror of ``ngram_workspace_view`` (include/ngram.h)."""
+    _fields_ = [
+        ("row_idx_offset", ctypes.c_int64),
+        ("mem_offset", ctypes.c_int64),
+        ("mem_layout", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -62,10 +77,13 @@ def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_
                 vocab_compressed: int, dtype: int, pad_id: int = 0, rms_eps: float = 1e-6,
                 conv_kernel: int = 4, conv_dilation: Optional[int] = None,
                 w_layout: int = W_MEM_D, table_dtype: Optional[int] = None,
-                table_scales: Optional[Sequence[float]] = None) -> NgramConfig:
+                table_scales: Optional[Sequence[float]] = None, proj_plan: Optional[int] = None,
+                decode_plan: Optional[Sequence[int]] = None) -> NgramConfig:
     """Fill an NgramConfig; ``hash_mult`` is indexable as [table][slot].
     ``dtype`` is the activation dtype and, unless ``table_dtype`` says
-    otherwise (FP8_E4M3 with one scale per table), the tables' too."""
+    otherwise (FP8_E4M3 with one scale per table), the tables' too.
+    ``proj_plan`` (a prefill projection tile plan id) and ``decode_plan``
+    ((ni, split) of the decode projection) override the library's tiling."""
     c = NgramConfig()
     c.n_orders = len(orders)
     for i, o in enumerate(orders):
@@ -92,6 +110,9 @@ def make_config(*, orders: Sequence[int], heads: int, rows: Sequence[int], hash_
     c.w_layout = w_layout
     for j, sc in enumerate(table_scales or ()):
         c.table_scale[j] = float(sc)
+    c.tune_proj_plan = 0 if proj_plan is None else int(proj_plan) + 1
+    if decode_plan is not None:
+        c.tune_decode_ni, c.tune_decode_split = int(decode_plan[0]), int(decode_plan[1])
     return c
 
 
@@ -103,22 +124,25 @@ _SIGS = {
     "ngram_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ngram_abi_version": (ctypes.c_int, []),
     "ngram_config_validate": (ctypes.c_int, [_cfgp]),
-    "ngram_set_timing_events": (ctypes.c_int, [_p, ctypes.c_int]),
-    "ngram_timing_stage_mask": (ctypes.c_int, []),
     "ngram_compress_ids": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p]),
     "ngram_hash": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p]),
     "ngram_gather": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p]),
     "ngram_gate_workspace_size": (_sz, [_cfgp, _i64]),
     "ngram_gate": (ctypes.c_int, [_cfgp, _p, _i64, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _sz, _p]),
-    "ngram_causal_conv": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _p]),
+    "ngram_causal_conv": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i32, _p, _p]),
     "ngram_forward_workspace_size": (_sz, [_cfgp, _i32, _i32]),
+    "ngram_forward_workspace_view": (ctypes.c_int, [_cfgp, _i32, _i32,
+                                                    ctypes.POINTER(NgramWorkspaceView)]),
     "ngram_backward_workspace_size": (_sz, [_cfgp, _i32, _i32]),
-    "ngram_backward": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p,
-                                      _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
-                                      _sz, _p]),
-    "ngram_forward": (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p,
-                                     _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
 }
+_FWD_ARGS = [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
+             _p, _p, _p, _p, _sz, _p]
+_BWD_ARGS = [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
+             _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_SIGS["ngram_forward"] = (ctypes.c_int, _FWD_ARGS)
+_SIGS["ngram_forward_timed"] = (ctypes.c_int, _FWD_ARGS + [_p, _p])
+_SIGS["ngram_backward"] = (ctypes.c_int, _BWD_ARGS)
+_SIGS["ngram_backward_timed"] = (ctypes.c_int, _BWD_ARGS + [_p, _p])
 
 
 def lib():
@@ -153,23 +177,15 @@ N_STAGES = 4
 STAGE_NAMES = ("hash", "gather", "projection", "gate_conv")
 
 
-def ngram_set_timing_events(events) -> None:
-    """Benchmark hook: ``events`` is a list of 2 * N_STAGES torch.cuda.Event
-    (created with enable_timing=True) -- the (start, stop) pair of each stage --
-    or None to turn the hook off."""
-    if events is None:
-        _check(lib().ngram_set_timing_events(None, 0), "ngram_set_timing_events")
-        return
-    for e in events:  # torch creates the underlying hipEvent on first record
+def _event_array(events):
+    """2 * N_STAGES torch.cuda.Event (enable_timing=True) -> a HOST array of
+    their hipEvent_t handles (torch creates a handle on its first record)."""
+    if len(events) != 2 * N_STAGES:
+        raise ValueError(f"need {2 * N_STAGES} events")
+    for e in events:
         if not e.cuda_event:
             e.record()
-    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
-    _check(lib().ngram_set_timing_events(arr, len(events)), "ngram_set_timing_events")
-
-
-def ngram_timing_stage_mask() -> int:
-    """Bit i set: stage i launched a kernel in the last timed ngram_forward."""
-    return int(lib().ngram_timing_stage_mask())
+    return (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
 
 
 # ---------------------------------------------------------------------------
@@ -253,10 +269,10 @@ def ngram_gate(cfg, hidden, hidden_branch_stride, mem, w_k, w_v, gates, u=None, 
 
 
 def ngram_causal_conv(cfg, u, B: int, T: int, conv_w, out, gamma_u=None, conv_state=None,
-                      stream=None):
+                      state_pos=None, flags: int = 0, stream=None):
     _check(lib().ngram_causal_conv(ctypes.byref(cfg), _ptr(u), B, T, _ptr(conv_w), _ptr(gamma_u),
-                                   _ptr(conv_state), _ptr(out), _stream(stream)),
-           "ngram_causal_conv")
+                                   _ptr(conv_state), _ptr(state_pos), flags, _ptr(out),
+                                   _stream(stream)), "ngram_causal_conv")
     return out
 
 
@@ -264,38 +280,101 @@ def ngram_forward_workspace_size(cfg, B: int, T: int) -> int:
     return int(lib().ngram_forward_workspace_size(ctypes.byref(cfg), B, T))
 
 
-def ngram_forward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w, out,
-                  history=None, gamma_q=None, gamma_k=None, gamma_u=None, conv_state=None,
-                  flags: int = 0, gates=None, err_flag=None, workspace=None, stream=None):
+def ngram_forward_workspace_view(cfg, B: int, T: int) -> NgramWorkspaceView:
+    """Where ngram_forward leaves the call's row ids and memory vector E in
+    its workspace (byte offsets and the layout of E)."""
+    v = NgramWorkspaceView()
+    _check(lib().ngram_forward_workspace_view(ctypes.byref(cfg), B, T, ctypes.byref(v)),
+           "ngram_forward_workspace_view")
+    return v
+
+
+def _forward_args(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w, out,
+                  history, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags, gates,
+                  err_flag, workspace, stream):
     B, T = raw_ids.shape
     if workspace is None:
         workspace = _workspace(ngram_forward_workspace_size(cfg, B, T), raw_ids.device)
-    _check(lib().ngram_forward(ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history), _ptr(lut),
-                               _table_array(tables), _ptr(hidden), hidden_branch_stride, _ptr(w_k),
-                               _ptr(w_v), _ptr(conv_w), _ptr(gamma_q), _ptr(gamma_k),
-                               _ptr(gamma_u), _ptr(conv_state), flags, _ptr(out), _ptr(gates),
-                               _ptr(err_flag), _ptr(workspace), workspace.numel(),
-                               _stream(stream)), "ngram_forward")
+    return (ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history), _ptr(lut), _table_array(tables),
+            _ptr(hidden), hidden_branch_stride, _ptr(w_k), _ptr(w_v), _ptr(conv_w), _ptr(gamma_q),
+            _ptr(gamma_k), _ptr(gamma_u), _ptr(conv_state), _ptr(state_pos), flags, _ptr(out),
+            _ptr(gates), _ptr(err_flag), _ptr(workspace), workspace.numel(), _stream(stream))
+
+
+def ngram_forward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w, out,
+                  history=None, gamma_q=None, gamma_k=None, gamma_u=None, conv_state=None,
+                  state_pos=None, flags: int = 0, gates=None, err_flag=None, workspace=None,
+                  stream=None):
+    _check(lib().ngram_forward(*_forward_args(cfg, raw_ids, lut, tables, hidden,
+                                              hidden_branch_stride, w_k, w_v, conv_w, out,
+                                              history, gamma_q, gamma_k, gamma_u, conv_state,
+                                              state_pos, flags, gates, err_flag, workspace,
+                                              stream)), "ngram_forward")
     return out
+
+
+def ngram_forward_timed(events, cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v,
+                        conv_w, out, history=None, gamma_q=None, gamma_k=None, gamma_u=None,
+                        conv_state=None, state_pos=None, flags: int = 0, gates=None,
+                        err_flag=None, workspace=None, stream=None) -> int:
+    """ngram_forward with each stage's kernels timed into ``events`` (2 *
+    N_STAGES torch.cuda.Event); returns the mask of the stages that ran."""
+    mask = ctypes.c_int32(0)
+    _check(lib().ngram_forward_timed(*_forward_args(cfg, raw_ids, lut, tables, hidden,
+                                                    hidden_branch_stride, w_k, w_v, conv_w, out,
+                                                    history, gamma_q, gamma_k, gamma_u,
+                                                    conv_state, state_pos, flags, gates, err_flag,
+                                                    workspace, stream),
+                                     _event_array(events), ctypes.byref(mask)),
+           "ngram_forward_timed")
+    return int(mask.value)
 
 
 def ngram_backward_workspace_size(cfg, B: int, T: int) -> int:
     return int(lib().ngram_backward_workspace_size(ctypes.byref(cfg), B, T))
 
 
-def ngram_backward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w,
-                   d_out, d_tables, d_w_k, d_w_v, d_conv_w, history=None, gamma_q=None,
-                   gamma_k=None, gamma_u=None, conv_state=None, flags: int = 0, d_hidden=None,
-                   d_gammas=None, workspace=None, stream=None):
-    """Gradients of sum(d_out * out); ``d_tables`` (fp32, one per table) are
-    accumulated, the other gradient tensors written."""
+def _backward_args(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w,
+                   d_out, d_tables, d_w_k, d_w_v, d_conv_w, history, gamma_q, gamma_k, gamma_u,
+                   conv_state, state_pos, flags, d_hidden, d_gammas, workspace, stream):
     B, T = raw_ids.shape
     if workspace is None:
         workspace = _workspace(ngram_backward_workspace_size(cfg, B, T), raw_ids.device)
-    _check(lib().ngram_backward(ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history), _ptr(lut),
-                                _table_array(tables), _ptr(hidden), hidden_branch_stride,
-                                _ptr(w_k), _ptr(w_v), _ptr(conv_w), _ptr(gamma_q), _ptr(gamma_k),
-                                _ptr(gamma_u), _ptr(conv_state), flags, _ptr(d_out),
-                                _table_array(d_tables), _ptr(d_w_k), _ptr(d_w_v), _ptr(d_conv_w),
-                                _ptr(d_hidden), _ptr(d_gammas), _ptr(workspace),
-                                workspace.numel(), _stream(stream)), "ngram_backward")
+    return (ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history), _ptr(lut), _table_array(tables),
+            _ptr(hidden), hidden_branch_stride, _ptr(w_k), _ptr(w_v), _ptr(conv_w), _ptr(gamma_q),
+            _ptr(gamma_k), _ptr(gamma_u), _ptr(conv_state), _ptr(state_pos), flags, _ptr(d_out),
+            _table_array(d_tables), _ptr(d_w_k), _ptr(d_w_v), _ptr(d_conv_w), _ptr(d_hidden),
+            _ptr(d_gammas), _ptr(workspace), workspace.numel(), _stream(stream))
+
+
+def ngram_backward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v, conv_w,
+                   d_out, d_tables, d_w_k, d_w_v, d_conv_w, history=None, gamma_q=None,
+                   gamma_k=None, gamma_u=None, conv_state=None, state_pos=None, flags: int = 0,
+                   d_hidden=None, d_gammas=None, workspace=None, stream=None):
+    """Gradients of sum(d_out * out); ``d_tables`` (fp32, one per table) are
+    accumulated, the other gradient tensors written."""
+    _check(lib().ngram_backward(*_backward_args(cfg, raw_ids, lut, tables, hidden,
+                                                hidden_branch_stride, w_k, w_v, conv_w, d_out,
+                                                d_tables, d_w_k, d_w_v, d_conv_w, history,
+                                                gamma_q, gamma_k, gamma_u, conv_state, state_pos,
+                                                flags, d_hidden, d_gammas, workspace, stream)),
+           "ngram_backward")
+
+
+def ngram_backward_timed(events, cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k,
+                         w_v, conv_w, d_out, d_tables, d_w_k, d_w_v, d_conv_w, history=None,
+                         gamma_q=None, gamma_k=None, gamma_u=None, conv_state=None,
+                         state_pos=None, flags: int = 0, d_hidden=None, d_gammas=None,
+                         workspace=None, stream=None) -> int:
+    """ngram_backward with its four stages timed into ``events``; returns the
+    mask of the stages that ran."""
+    mask = ctypes.c_int32(0)
+    _check(lib().ngram_backward_timed(*_backward_args(cfg, raw_ids, lut, tables, hidden,
+                                                      hidden_branch_stride, w_k, w_v, conv_w,
+                                                      d_out, d_tables, d_w_k, d_w_v, d_conv_w,
+                                                      history, gamma_q, gamma_k, gamma_u,
+                                                      conv_state, state_pos, flags, d_hidden,
+                                                      d_gammas, workspace, stream),
+                                      _event_array(events), ctypes.byref(mask)),
+           "ngram_backward_timed")
+    return int(mask.value)

@@ -23,7 +23,8 @@
  *    scratch comes from the caller's workspace.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream), never synchronises, keeps no state between calls and is
- *    reentrant.
+ *    reentrant.  The library reads no environment variables: tuning overrides
+ *    are fields of ngram_config.
  *  - All arrays are dense row-major.  Device pointers must be 16-byte aligned.
  *  - Arguments are validated on the host before any launch; a failed check
  *    returns a negative ngram_status and launches nothing.  A failed launch
@@ -50,8 +51,9 @@ extern "C" {
 #define NGRAM_MAX_ORDER 4
 #define NGRAM_MAX_BRANCHES 4
 
-/* flags for ngram_forward */
-#define NGRAM_ADD_RESIDUAL 1 /* out = hidden (the branch's query row) + Delta */
+/* flags for ngram_forward / ngram_causal_conv */
+#define NGRAM_ADD_RESIDUAL 1 /* out = hidden (the branch's query row) + Delta (forward only) */
+#define NGRAM_UPDATE_STATE 2 /* write this call's normalised rows into the conv-state ring */
 
 typedef enum ngram_status {
   NGRAM_OK = 0,
@@ -124,6 +126,15 @@ typedef struct ngram_config {
   int32_t act_dtype;                                     /* == table_dtype; bf16 for fp8 tables */
   int32_t w_layout;                                      /* ngram_w_layout */
   float table_scale[NGRAM_MAX_TABLES];                   /* fp8 tables: finite, > 0 */
+  /* Tile-plan overrides; 0 everywhere = the library's own choice.  They change
+     how the work is tiled, never the result beyond fp32 summation order.
+     tune_proj_plan: 1 + id of the prefill projection's tile plan (0..11) for
+     bf16 with W stored [d, mem].  tune_decode_ni / tune_decode_split: the decode
+     projection's 16-column blocks per workgroup (2..6) and K slices; both or
+     neither, and the pair must fit (see ngram_config_validate). */
+  int32_t tune_proj_plan;
+  int32_t tune_decode_ni;
+  int32_t tune_decode_split;
 } ngram_config;
 
 /* Human-readable name of a status code (static string). */
@@ -139,6 +150,14 @@ int ngram_abi_version(void);
  * hidden_dim % 32 == 0; for fp32, hidden_dim % 4 == 0.  fp8 tables take bf16
  * activations, and the memory vector E is bf16.  conv_kernel must be 4 (the pages' kernel)
  * and conv_dilation the largest order.
+ *
+ * This is the only call that proves every rows[j] prime (deterministic
+ * Miller-Rabin); call it once when a configuration is built.  The other entry
+ * points repeat every check except that proof, screening rows[j] only for
+ * small factors: primality shapes the hash's spread, while row ids stay below
+ * rows[j] (the bound that keeps the table reads in range) for any value.
+ * A decode tile-plan override must satisfy: split divides mem_dim,
+ * (mem_dim / split) % 128 == 0 and 32 * ni * (mem_dim / split) <= 131072.
  */
 int ngram_config_validate(const ngram_config* cfg);
 
@@ -204,6 +223,27 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
                size_t workspace_bytes, void* stream);
 
 /*
+ * The conv-state ring (decode, and prefill in chunks).  The convolution at
+ * position t reads the normalised rows N of positions t, t - dil, t - 2 dil,
+ * t - 3 dil, so a sequence that arrives in pieces needs the last R =
+ * (conv_kernel - 1) * dil rows of the earlier pieces.  conv_state holds them
+ * as a ring, device float[B, R, n_branches, d], together with
+ * state_pos, device int32[B]: the number of positions of sequence b that came
+ * before this call's first token.  The row of absolute position p lives in
+ * slot p mod R.  A position before the start of the sequence (p < 0) reads
+ * zeros whatever its slot holds, so the ring of a new sequence need not be
+ * cleared (state_pos = 0).  A negative state_pos is read as 0.
+ * state_pos NULL means state_pos = R for every sequence: slot s holds position
+ * s - R, oldest first.
+ * With NGRAM_UPDATE_STATE the call also writes the normalised rows of its last
+ * min(T, R) positions into their slots (position state_pos[b] + t goes to slot
+ * (state_pos[b] + t) mod R), in place, after every read of the ring it needs:
+ * the caller then advances state_pos[b] by T, and decode becomes one call per
+ * token that costs one ring row written and three read per sequence and
+ * branch.
+ */
+
+/*
  * Convolution block -- Engram's fourth component (kernel 4, dilation = the
  * largest n-gram order, depthwise, causal) and §2.3's
  * Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))):
@@ -212,13 +252,15 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
  *   u          device [B, T, n_branches, d] act_dtype
  *   conv_w     device [conv_kernel, d] act_dtype; tap i multiplies position t - i*dil
  *   gamma_u    device [d] act_dtype, nullable (= 1)
- *   conv_state device float[B, (conv_kernel-1)*dil, n_branches, d] normalised rows
- *              N for positions -(k-1)*dil .. -1 (last row = position -1), nullable
+ *   conv_state device float[B, R, n_branches, d] ring of normalised rows (see
+ *              above), nullable (zeros before position 0)
+ *   state_pos  device int32[B], nullable (see above)
+ *   flags      0 or NGRAM_UPDATE_STATE (which needs conv_state)
  *   out        device [B, T, n_branches, d] act_dtype (output)
  */
 int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t T,
-                      const void* conv_w, const void* gamma_u, const float* conv_state,
-                      void* out, void* stream);
+                      const void* conv_w, const void* gamma_u, float* conv_state,
+                      const int32_t* state_pos, int32_t flags, void* out, void* stream);
 
 /*
  * The whole layer in one call (steps 1-8 above), intermediates in fp32: K is
@@ -231,22 +273,52 @@ int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t
  *   tables    HOST array of n_tables device pointers (see ngram_gather)
  *   hidden, hidden_branch_stride, w_k, w_v, gamma_q, gamma_k: as ngram_gate,
  *             hidden indexed by token b*T + t
- *   conv_w, gamma_u, conv_state: as ngram_causal_conv
- *   flags     0 or NGRAM_ADD_RESIDUAL
+ *   conv_w, gamma_u, conv_state, state_pos: as ngram_causal_conv (with the
+ *             ring, one call per new token gives the Delta_t that one call over
+ *             the whole sequence gives)
+ *   flags     0 or NGRAM_ADD_RESIDUAL and / or NGRAM_UPDATE_STATE
  *   out       device [B, T, n_branches, d] act_dtype (output): Delta_t, or
  *             hidden + Delta_t with NGRAM_ADD_RESIDUAL
  *   gates     device float[B, T, n_branches] (output), nullable
  *   err_flag  device int32, nullable (see conventions)
- *   workspace device scratch of at least ngram_forward_workspace_size() bytes
+ *   workspace device scratch of at least ngram_forward_workspace_size() bytes;
+ *             when the call's work is done it holds the call's row ids and
+ *             memory vector E (ngram_forward_workspace_view)
  */
 size_t ngram_forward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T);
 int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
                   const int32_t* history, const int32_t* lut, const void* const* tables,
                   const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                   const void* w_v, const void* conv_w, const void* gamma_q,
-                  const void* gamma_k, const void* gamma_u, const float* conv_state,
-                  int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
-                  size_t workspace_bytes, void* stream);
+                  const void* gamma_k, const void* gamma_u, float* conv_state,
+                  const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                  int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Where ngram_forward leaves the row ids and the memory vector of its tokens
+ * in the workspace (offsets in bytes from the workspace's start; the layout
+ * depends only on cfg, B and T).  After the call's work is done (stream
+ * order), until the workspace is reused:
+ *   row_idx_offset  int32[B*T, n_tables]: the row of table j for token b*T + t
+ *   mem_offset      E, bf16 (fp8 tables widened) or fp32, in mem_layout:
+ *     NGRAM_MEM_ROWS     [B*T, mem_dim] row-major
+ *     NGRAM_MEM_TILES16  1 KB tiles of 16 tokens x 32 values (the decode
+ *                        route, bf16): value k of token i sits at element
+ *                        ((i/16) * (mem_dim/32) + k/32) * 512
+ *                        + (16 * ((k%32)/8) + i%16) * 8 + k%8,
+ *                        for i < 16 * ceil(B*T / 16)
+ * Returns NGRAM_OK, or the status ngram_forward would return for these sizes.
+ */
+#define NGRAM_MEM_ROWS 0
+#define NGRAM_MEM_TILES16 1
+typedef struct ngram_workspace_view {
+  int64_t row_idx_offset;
+  int64_t mem_offset;
+  int32_t mem_layout;
+  int32_t reserved;
+} ngram_workspace_view;
+int ngram_forward_workspace_view(const ngram_config* cfg, int32_t B, int32_t T,
+                                 ngram_workspace_view* view);
 
 /*
  * Backward of ngram_forward (training): the gradients of L = sum(d_out (.) out)
@@ -260,8 +332,10 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
  * a multiple of 64 and at most 4096; the tables may be bf16 or fp8.  The
  * forward intermediates (E, K, V, gates, norms) are recomputed.
  *
- *   raw_ids ... conv_state, flags  as for ngram_forward (NGRAM_ADD_RESIDUAL:
- *              out = hidden + Delta, so d_hidden also receives d_out)
+ *   raw_ids ... conv_state, state_pos, flags  as for ngram_forward
+ *              (NGRAM_ADD_RESIDUAL: out = hidden + Delta, so d_hidden also
+ *              receives d_out; the ring is only read, NGRAM_UPDATE_STATE is
+ *              rejected)
  *   d_out      device [B, T, n_branches, d] bf16: dL/d(out)
  *   d_tables   HOST array of n_tables device pointers, table j an fp32
  *              [rows[j], row_dim] gradient, ACCUMULATED (+=); rows named by
@@ -283,30 +357,47 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
                    const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                    const void* w_v, const void* conv_w, const void* gamma_q,
                    const void* gamma_k, const void* gamma_u, const float* conv_state,
-                   int32_t flags, const void* d_out, float* const* d_tables, float* d_w_k,
-                   float* d_w_v, float* d_conv_w, float* d_hidden, float* d_gammas,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   const int32_t* state_pos, int32_t flags, const void* d_out,
+                   float* const* d_tables, float* d_w_k, float* d_w_v, float* d_conv_w,
+                   float* d_hidden, float* d_gammas, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
- * Benchmark instrumentation (not part of the layer).  With n == 2 * NGRAM_N_STAGES, every
- * following ngram_forward times its stages on the device -- 0 hash, 1 gather, 2 projection,
- * 3 gate + conv: the first kernel of stage i stamps its begin time into events[2i] and every
- * kernel of the stage stamps its end time into events[2i + 1] (hipExtLaunchKernel), so
- * hipEventElapsedTime(events[2i], events[2i + 1]) is the stage's kernel time, with no event
- * packet between the kernels.  A kernel that covers several stages counts in the last of them
- * (the decode path hashes and gathers in one kernel; the fused path hashes, gathers and
- * projects in one); the stages it absorbs launch nothing and leave their events untouched.
- * ngram_backward times four stages the same way: 0 the recompute (hash, gather, K / V
- * product), 1 the per-row backward, 2 the dE product (with its transposes), 3 the dW products
- * and the table scatter-add.
- * ngram_timing_stage_mask() returns the bit mask (bit i = stage i) of the stages that launched
- * a kernel in the last ngram_forward or ngram_backward call.  n == 0 turns timing off.  The setting is
- * process-wide and not synchronised: set it only while no other thread calls ngram_forward.
- * Returns NGRAM_EINVAL for other n or NULL events.
+ * Instrumented variants for benchmarks (not part of the layer): the same work
+ * as ngram_forward / ngram_backward, and each stage's kernels timed on the
+ * device.  stage_events is a HOST array of 2 * NGRAM_N_STAGES hipEvent_t:
+ * the first kernel of stage i stamps its begin time into stage_events[2i]
+ * and every kernel of the stage its end time into stage_events[2i + 1]
+ * (hipExtLaunchKernel), so hipEventElapsedTime of the pair is the stage's
+ * kernel time with no event packet between the kernels.  Forward stages:
+ * 0 hash, 1 gather, 2 projection, 3 gate + conv; a kernel that covers several
+ * stages counts in the last of them (decode hashes and gathers in one kernel)
+ * and the stages it absorbs leave their events untouched.  Backward stages:
+ * 0 the recompute (hash, gather, K / V product), 1 the per-row backward, 2 the
+ * dE product (with its transposes), 3 the dW products and the table
+ * scatter-add.  *stage_mask (host, nullable) receives the bit mask of the
+ * stages that launched a kernel.  The events are used for the duration of
+ * the call only; nothing is kept.
  */
 #define NGRAM_N_STAGES 4
-int ngram_set_timing_events(void* const* events, int n);
-int ngram_timing_stage_mask(void);
+int ngram_forward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                        const int32_t* history, const int32_t* lut, const void* const* tables,
+                        const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                        const void* w_v, const void* conv_w, const void* gamma_q,
+                        const void* gamma_k, const void* gamma_u, float* conv_state,
+                        const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                        int32_t* err_flag, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* stage_events, int32_t* stage_mask);
+int ngram_backward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                         const int32_t* history, const int32_t* lut, const void* const* tables,
+                         const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                         const void* w_v, const void* conv_w, const void* gamma_q,
+                         const void* gamma_k, const void* gamma_u, const float* conv_state,
+                         const int32_t* state_pos, int32_t flags, const void* d_out,
+                         float* const* d_tables, float* d_w_k, float* d_w_v, float* d_conv_w,
+                         float* d_hidden, float* d_gammas, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* stage_events,
+                         int32_t* stage_mask);
 
 #ifdef __cplusplus
 }

@@ -330,6 +330,25 @@ void orc_conv_block(const double* u, int32_t B, int32_t T, int32_t nb, int32_t d
   free(nrm);
 }
 
+/* The normalised rows the convolution reads ([B] §2.3, RMSNorm(U_t)):
+ * out[r] = gamma (.) u[r] / sqrt(mean(u[r]^2) + eps) for each of the rows
+ * rows of d values; gamma (nullable = 1) in dtype.  A caller that feeds a
+ * sequence in pieces keeps the last (kernel-1)*dil of these rows as the
+ * state of the next piece. */
+void orc_normalise_rows(const double* u, int64_t rows, int32_t d, const void* gamma,
+                        int32_t dtype, double eps, double* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* x = u + r * d;
+    double ss = 0.0;
+    for (int32_t n = 0; n < d; ++n) ss += x[n] * x[n];
+    const double inv = 1.0 / sqrt(ss / d + eps);
+    for (int32_t n = 0; n < d; ++n) {
+      const double g = gamma ? load_value(gamma, dtype, n) : 1.0;
+      out[r * d + n] = g * x[n] * inv;
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------
  * Backward of the layer (the gradients a training step needs: tables, W_K,
  * W_V, conv taps, query, RMSNorm gains), each step the chain rule of the

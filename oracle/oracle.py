@@ -72,6 +72,7 @@ def _load(path: str):
                                     _p, _p, _p, _p]
     L.orc_project_backward.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p, _p, _p]
     L.orc_scatter_add.argtypes = [_p, _i64, _i32, _p, _i32, _p]
+    L.orc_normalise_rows.argtypes = [_p, _i64, _i32, _p, _i32, _f64, _p]
     return L
 
 
@@ -203,6 +204,18 @@ def conv_block(u, conv_w, dtype: str, dilation: int, gamma_u=None, eps: float = 
     lib().orc_conv_block(_ptr(u), B, T, nb, d, _ptr(w), _DT[dtype], kernel, dilation,
                          _ptr(_storage(gamma_u, dtype) if gamma_u is not None else None),
                          eps, _ptr(st), _ptr(out))
+    return out
+
+
+def normalised_rows(u, gamma_u=None, dtype: str = "f32", eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm of each row of u (float64[..., d]): gamma_u (.) u / rms(u), the
+    rows the convolution reads (and a conv-state ring holds)."""
+    u = _c(u, np.float64)
+    d = u.shape[-1]
+    out = np.empty_like(u)
+    lib().orc_normalise_rows(_ptr(u), u.size // d, d,
+                             _ptr(_storage(gamma_u, dtype) if gamma_u is not None else None),
+                             _DT[dtype], eps, _ptr(out))
     return out
 
 

@@ -90,6 +90,41 @@ def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
 
 
 TOL = 2e-3  # normwise relative error bound for floating-point outputs
+# Per row (one token and branch) and per element: bf16 keeps 8 significand
+# bits, so rounding to nearest moves an element by at most half an ulp, at
+# most 2^-8 = 3.9e-3 of its own magnitude (at the bottom of a binade; 1.66e-3
+# rms over a uniform spread of significands).  No row's normwise error, and no
+# element's error relative to the largest reference element, can exceed that
+# beyond the fp32 arithmetic's error (~1e-6); an element whose fp32 value
+# lies next to a rounding midpoint rounds to the neighbour of the exact
+# value's rounding, still within half an ulp plus that error.
+ROW_TOL = 4e-3    # max over rows of the row's normwise relative error
+MAX_TOL = 4e-3    # max |y - ref| / max |ref|
+
+
+def errors(got, want):
+    """(normwise, worst row's normwise, max-abs over max |ref|) errors of got
+    against want; rows run along the last axis."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    e = rel_err(got, want)
+    g2 = got.reshape(-1, want.shape[-1]) if want.ndim else got.reshape(1, 1)
+    w2 = want.reshape(g2.shape)
+    den = np.linalg.norm(w2, axis=1)
+    num = np.linalg.norm(g2 - w2, axis=1)
+    row = float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+    peak = float(np.max(np.abs(want))) if want.size else 0.0
+    mx = float(np.max(np.abs(got - want)) / (peak if peak > 0 else 1.0)) if want.size else 0.0
+    return e, row, mx
+
+
+def check(got, want, label: str = "", tol: float = TOL, row_tol: float = ROW_TOL,
+          max_tol: float = MAX_TOL):
+    """Assert the normwise, per-row and per-element bounds above."""
+    e, row, mx = errors(got, want)
+    print(f"   {label} rel_err {e:.3e} worst row {row:.3e} max-abs/max {mx:.3e}")
+    assert e < tol and row < row_tol and mx < max_tol, (label, e, row, mx)
 
 
 def oracle_table_kw(w: W.Workload) -> dict:
@@ -141,3 +176,69 @@ def oracle_backward(orc, w, ids, hist, hidden_storage, wk_host, wv_host, conv_ho
                         wv_host, conv_host, w.dtype, d_out, gamma_q=gam_storage["q"],
                         gamma_k=gam_storage["k"], gamma_u=gam_storage["u"], eps=w.rms_eps,
                         conv_state=conv_state, add_residual=residual, **oracle_table_kw(w))
+
+
+# ---------------------------------------------------------------------------
+# the row ids and memory vector ngram_forward itself produced
+# ---------------------------------------------------------------------------
+
+def forward_ids_and_memory(cfg, w: W.Workload, B: int, T: int, ws: torch.Tensor):
+    """Row ids [n, n_tables] (int32) and E [n, mem_dim] (the memory dtype) that
+    the last ngram_forward left in its workspace ``ws`` (a uint8 tensor), as
+    ngram_forward_workspace_view places them; decode's 16-token MFMA tiles
+    are put back into rows."""
+    v = H().ngram_forward_workspace_view(cfg, B, T)
+    n = B * T
+    rows = ws[v.row_idx_offset:v.row_idx_offset + 4 * n * w.n_tables].view(torch.int32)
+    rows = rows.view(n, w.n_tables)
+    mdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    es = 4 if w.dtype == "f32" else 2
+    if v.mem_layout == H().MEM_TILES16:
+        nblk = (n + 15) // 16
+        raw = ws[v.mem_offset:v.mem_offset + nblk * 16 * w.mem_dim * es].view(mdt)
+        # element ((blk * K/32 + kk) * 4 + q) * 128 + r * 8 + c holds token
+        # 16 blk + r, value 32 kk + 8 q + c
+        e = raw.view(nblk, w.mem_dim // 32, 4, 16, 8).permute(0, 3, 1, 2, 4)
+        e = e.reshape(nblk * 16, w.mem_dim)[:n]
+    else:
+        e = ws[v.mem_offset:v.mem_offset + n * w.mem_dim * es].view(mdt).view(n, w.mem_dim)
+    return rows, e
+
+
+def oracle_row_ids(orc, w: W.Workload, ids, hist):
+    """The oracle's compression and hashing of raw ids [B, T] (history raw
+    [B, H] or None): row ids [B*T, n_tables]."""
+    lut = W.make_lut(w)
+    comp, _ = orc.compress(ids, lut, w.vocab, w.vocab_compressed)
+    hc = orc.compress(hist, lut, w.vocab, w.vocab_compressed)[0] if hist is not None else None
+    return orc.hash_rows(comp, hc, w.orders, w.heads, w.rows(), W.hash_multipliers(w))
+
+
+def check_forward_ids_and_memory(orc, w: W.Workload, ids, hist, cfg, ws, sample: int = 160):
+    """Bit-exact check of what the forward's own kernels produced: every
+    token's row ids equal the oracle's hashing of its raw ids (compression,
+    n-gram windows, history, pad); every token's E equals the concatenation
+    of the table rows at those ids (fetched by torch on the device; fp8 rows
+    decoded and scaled by torch's float8_e4m3fn conversion, then rounded to
+    bf16); and a sample of tokens equals the oracle's own gather of rows
+    regenerated on the host."""
+    B, T = ids.shape
+    got_rows, e = forward_ids_and_memory(cfg, w, B, T, ws)
+    ref_rows = oracle_row_ids(orc, w, ids, hist)
+    assert np.array_equal(got_rows.cpu().numpy(), ref_rows), "row ids"
+    tabs = tables(w)
+    d_rows = torch.from_numpy(ref_rows).cuda()
+    bits = torch.int32 if w.dtype == "f32" else torch.int16
+    for j in range(w.n_tables):
+        want = tabs[j].index_select(0, d_rows[:, j].long())
+        if w.tdtype == "fp8":
+            want = (want.view(torch.float8_e4m3fn).float() * float(w.table_scales()[j])).bfloat16()
+        got = e[:, j * w.row_dim:(j + 1) * w.row_dim]
+        assert torch.equal(got.contiguous().view(bits), want.view(bits)), f"E table {j}"
+    n = ref_rows.shape[0]
+    rs = np.random.default_rng(11)
+    pick = np.unique(np.concatenate([[0, n - 1], rs.integers(0, n, sample)]))
+    e_ref = orc.gather_from_rows(ref_rows[pick], oracle_rows(w), w.tdtype,
+                                 w.table_scales() if w.tdtype == "fp8" else None)
+    assert np.array_equal(to_f64(e[torch.from_numpy(pick).cuda()]), e_ref), "E sample"
+    print(f"   row ids and E of all {n} tokens bit-exact ({len(pick)} also against host rows)")

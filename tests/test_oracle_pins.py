@@ -452,6 +452,32 @@ def test_conv_causal_and_state_streaming(orc):
     assert np.allclose(half, full[:, 30:], rtol=1e-12, atol=1e-14)
 
 
+def test_normalised_rows(orc):
+    """The rows a conv state holds: RMSNorm(U) with gain gamma_u.  Pinned by
+    its closed forms -- mean(N^2) = m / (m + eps) with m = mean(U^2) when
+    gamma = 1, invariance under scaling U when eps = 0, N parallel to
+    gamma (.) U -- and by the conv it feeds: with taps (1, 0, 0, 0),
+    Delta - U = SiLU(N) exactly."""
+    u = _u()
+    eps = 1e-6
+    n = orc.normalised_rows(u, eps=eps)
+    m = (u ** 2).mean(axis=-1)
+    assert np.allclose((n ** 2).mean(axis=-1), m / (m + eps), rtol=1e-13, atol=0)
+    n0 = orc.normalised_rows(u, eps=0.0)
+    assert np.allclose(orc.normalised_rows(37.5 * u, eps=0.0), n0, rtol=1e-13, atol=1e-15)
+    g = np.random.default_rng(9).standard_normal(32).astype(np.float32)
+    ng = orc.normalised_rows(u, g, "f32", eps)
+    x = (g.astype(np.float64) * u).reshape(-1, 32)
+    y = ng.reshape(-1, 32)
+    cos = (x * y).sum(1) / np.linalg.norm(x, axis=1) / np.linalg.norm(y, axis=1)
+    assert np.allclose(cos, 1.0, rtol=0, atol=1e-13)
+    assert np.all((x * y).sum(1) > 0)
+    w = np.zeros((4, 32), dtype=np.float32)
+    w[0] = 1.0
+    delta = orc.conv_block(u, w, "f32", 3, eps=eps)
+    assert np.allclose(delta - u, _silu(n), rtol=1e-12, atol=1e-15)
+
+
 # --------------------------------------------------------------------------
 # the composed forward pass
 # --------------------------------------------------------------------------

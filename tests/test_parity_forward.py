@@ -32,20 +32,31 @@ def _device_inputs(w, ids, hist, random_gamma=False, layout="mem_d"):
 
 
 def _run(w, inp, flags=0, conv_state=None):
+    """One ngram_forward; its configuration and workspace stay in ``inp``
+    for _check_ids."""
     H = G.H()
     B, T = inp["ids"].shape
     cfg = G.config(w, inp["layout"])
     out = torch.empty((B, T, w.n_branches, w.hidden), dtype=G.tdtype(w), device="cuda")
     gates = torch.empty((B, T, w.n_branches), dtype=torch.float32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(H.ngram_forward_workspace_size(cfg, B, T), 1), dtype=torch.uint8,
+                     device="cuda")
     hbs = 0 if w.n_branches == 1 else w.hidden
     g = inp["gam"]
     H.ngram_forward(cfg, inp["ids"], inp["lut"], inp["tables"], inp["hidden"], hbs, inp["wk"],
                     inp["wv"], inp["conv_w"], out, history=inp["hist"], gamma_q=g["q"],
                     gamma_k=g["k"], gamma_u=g["u"], conv_state=conv_state, flags=flags,
-                    gates=gates, err_flag=err)
+                    gates=gates, err_flag=err, workspace=ws)
     torch.cuda.synchronize()
+    inp["cfg"], inp["ws"] = cfg, ws
     return out, gates, err.item()
+
+
+def _check_ids(orc, w, ids, hist, inp):
+    """The row ids and E that this forward's own kernels produced, bit-exact
+    on every token."""
+    G.check_forward_ids_and_memory(orc, w, ids, hist, inp["cfg"], inp["ws"])
 
 
 def _host_params(w, inp):
@@ -66,11 +77,9 @@ def _check_windows(orc, w, ids, hist, inp, out, gates, windows, flags=0, state=N
         want = ref["delta"]
         if flags:
             want = want + W.to_f64(W.hidden_values(w, toks), w.dtype)
-        e_out = G.rel_err(got, want)
-        e_gate = G.rel_err(gates.reshape(-1, w.n_branches)[torch.from_numpy(toks).cuda()].cpu().numpy(),
-                           ref["gate"])
-        print(f"   window b={b} [{start},{start + length}) rel_err out={e_out:.3e} gate={e_gate:.3e}")
-        assert e_out < G.TOL and e_gate < G.TOL, (b, start, e_out, e_gate)
+        G.check(got, want, f"window b={b} [{start},{start + length}) out")
+        G.check(gates.reshape(-1, w.n_branches)[torch.from_numpy(toks).cuda()].cpu().numpy(),
+                ref["gate"], "gates")
 
 
 @pytest.mark.parametrize("random_gamma,flags", [(False, 0), (True, 1)])
@@ -81,6 +90,7 @@ def test_forward_tiny_full(orc, random_gamma, flags):
     inp = _device_inputs(w, ids, hist, random_gamma)
     out, gates, err = _run(w, inp, flags)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, w.seq_len)], flags)
 
 
@@ -92,6 +102,7 @@ def test_forward_engram_small(orc, layout):
     inp = _device_inputs(w, ids, hist, random_gamma=True, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     T = w.seq_len
     _check_windows(orc, w, ids, hist, inp, out, gates,
                    [(0, 0, 40), (0, 1000, 40), (7, 2049, 40), (7, T - 40, 40)])
@@ -105,15 +116,14 @@ def test_forward_qwen_decode_full(orc, layout):
     inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     wk, wv, cw, gam = _host_params(w, inp)
     ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
                       w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
                       W.hidden_values(w, np.arange(ids.size)), wk, wv, cw, w.dtype,
                       gamma_q=gam["q"], gamma_k=gam["k"], gamma_u=gam["u"], eps=w.rms_eps)
-    e_out = G.rel_err(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"])
-    e_gate = G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"])
-    print(f"   decode rel_err out={e_out:.3e} gate={e_gate:.3e}")
-    assert e_out < G.TOL and e_gate < G.TOL
+    G.check(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"], "decode out")
+    G.check(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"], "decode gates")
 
 
 def test_forward_qwen_decode_fp8_full(orc):
@@ -125,15 +135,14 @@ def test_forward_qwen_decode_fp8_full(orc):
     inp = _device_inputs(w, ids, hist, layout="d_mem")
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     wk, wv, cw, gam = _host_params(w, inp)
     ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
                       w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
                       W.hidden_values(w, np.arange(ids.size)), wk, wv, cw, w.dtype,
                       eps=w.rms_eps, **G.oracle_table_kw(w))
-    e_out = G.rel_err(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"])
-    e_gate = G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"])
-    print(f"   decode fp8 rel_err out={e_out:.3e} gate={e_gate:.3e}")
-    assert e_out < G.TOL and e_gate < G.TOL
+    G.check(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"], "decode fp8 out")
+    G.check(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"], "decode fp8 gates")
 
 
 @pytest.mark.parametrize("layout", ["mem_d", "d_mem"])
@@ -146,6 +155,7 @@ def test_forward_engram_small_fp8(orc, layout):
     inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 300), (1, 650, 350)])
 
 
@@ -156,6 +166,7 @@ def test_forward_qwen_prefill_fp8(orc):
     inp = _device_inputs(w, ids, hist, layout="d_mem")
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     T = w.seq_len
     _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 24), (0, 98765, 24), (0, T - 24, 24)])
 
@@ -203,27 +214,25 @@ def test_forward_qwen_prefill(orc, layout):
     inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     T = w.seq_len
     _check_windows(orc, w, ids, hist, inp, out, gates,
                    [(0, 0, 24), (0, 7, 24), (0, 131071, 24), (0, T - 24, 24)])
     assert bool(((gates > 0) & (gates < 1)).all())
 
 
-@pytest.mark.parametrize("name,layout,fused", [("qwen_multibranch_uniform", "d_mem", False),
-                                               ("qwen_multibranch_zipf13", "d_mem", False),
-                                               ("qwen_multibranch_zipf13", "mem_d", False),
-                                               ("qwen_multibranch_zipf13", "d_mem", True)])
-def test_forward_multibranch(orc, name, layout, fused, monkeypatch):
-    """Four branches; the last case takes the fused-gather route (the
-    projection hashes and gathers its own operand, four key segments)."""
-    if fused:
-        monkeypatch.setenv("NGRAM_FUSED_GATHER", "1")
+@pytest.mark.parametrize("name,layout", [("qwen_multibranch_uniform", "d_mem"),
+                                         ("qwen_multibranch_zipf13", "d_mem"),
+                                         ("qwen_multibranch_zipf13", "mem_d")])
+def test_forward_multibranch(orc, name, layout):
+    """Four branches: four key segments and per-branch queries."""
     w = W.get(name)
-    print(f"[forward] {name} {layout} fused={fused}", flush=True)
+    print(f"[forward] {name} {layout}", flush=True)
     ids, hist = W.make_ids(w)
     inp = _device_inputs(w, ids, hist, layout=layout)
     out, gates, err = _run(w, inp)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     T = w.seq_len
     _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 16), (9, 4000, 16), (15, T - 16, 16)])
 
@@ -235,6 +244,7 @@ def test_forward_ragged_and_short(orc, B, T):
     ids, hist = W.make_ids(w)
     inp = _device_inputs(w, ids, hist, random_gamma=True)
     out, gates, err = _run(w, inp)
+    _check_ids(orc, w, ids, hist, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, T) for b in range(B)])
 
 
@@ -259,6 +269,7 @@ def test_forward_other_order_sets(orc, variant):
     ids, hist = W.make_ids(w)
     inp = _device_inputs(w, ids, hist, layout="d_mem" if "dmem" in variant else "mem_d")
     out, gates, err = _run(w, inp)
+    _check_ids(orc, w, ids, hist, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates,
                    [(b, 0, w.seq_len) for b in range(w.batch)])
 
@@ -276,6 +287,7 @@ def test_forward_wide_hidden(orc, d, T):
     inp = _device_inputs(w, ids, hist, random_gamma=True, layout="d_mem")
     out, gates, err = _run(w, inp, flags=1)
     assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates, [(b, 0, T) for b in range(w.batch)],
                    flags=1)
 
@@ -288,6 +300,7 @@ def test_forward_invalid_ids_are_pad(orc):
     inp = _device_inputs(w, ids, hist)
     out, gates, err = _run(w, inp)
     assert err == 1
+    _check_ids(orc, w, ids, hist, inp)
     _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 40), (1, 0, 40)])
 
 

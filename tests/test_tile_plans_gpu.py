@@ -1,9 +1,7 @@
 """Every tile plan of the projection kernel that streams operands straight
-into LDS (W stored [d, mem]) against the oracle, at ragged token counts:
-the op-level gate on a dense memory matrix and the forward pass that hashes
-and gathers inside the projection.  NGRAM_ASYNC_TILE selects the plan."""
-import os
-
+into LDS (W stored [d, mem]) against the oracle, at ragged token counts: the
+op-level gate on a dense memory matrix and the forward pass.  The
+configuration's tuning fields select the plan."""
 import numpy as np
 import pytest
 import torch
@@ -15,27 +13,16 @@ from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-PLANS = ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"]
+PLANS = list(range(12))
 
 
-@pytest.fixture
-def plan_env(request):
-    old = os.environ.get("NGRAM_ASYNC_TILE")
-    os.environ["NGRAM_ASYNC_TILE"] = request.param
-    yield request.param
-    if old is None:
-        del os.environ["NGRAM_ASYNC_TILE"]
-    else:
-        os.environ["NGRAM_ASYNC_TILE"] = old
-
-
-@pytest.mark.parametrize("plan_env", PLANS, indirect=True)
+@pytest.mark.parametrize("plan", PLANS)
 @pytest.mark.parametrize("n", [77, 1000, 4133])
-def test_gate_each_plan(orc, plan_env, n):
+def test_gate_each_plan(orc, plan, n):
     H = G.H()
     w = W.get("qwen_multibranch_zipf13")
-    print(f"[plan {plan_env}] gate n={n}", flush=True)
-    cfg = G.config(w, "d_mem")
+    print(f"[plan {plan}] gate n={n}", flush=True)
+    cfg = G.config(w, "d_mem", proj_plan=plan)
     e = rng.normal_values(31 + n, np.arange(n * w.mem_dim), 0.02, "bf16").reshape(n, w.mem_dim)
     hid = rng.normal_values(32 + n, np.arange(n * 4 * w.hidden), 1.0, "bf16").reshape(n, 4, w.hidden)
     wk, wv = G.weights(w, "d_mem")
@@ -48,33 +35,18 @@ def test_gate_each_plan(orc, plan_env, n):
     k = np.stack([orc.project(e64, wk_h[b], "bf16") for b in range(4)], axis=1)
     v = orc.project(e64, wv_h, "bf16")
     g_ref = orc.gate(hid, "bf16", k, eps=w.rms_eps)
-    assert G.rel_err(gates.cpu().numpy(), g_ref) < G.TOL
-    assert G.rel_err(G.to_f64(u), orc.gated_value(g_ref, v)) < G.TOL
+    G.check(gates.cpu().numpy(), g_ref, "gates")
+    G.check(G.to_f64(u), orc.gated_value(g_ref, v), "U")
 
 
-@pytest.fixture
-def fused_env(request):
-    old = os.environ.get("NGRAM_FUSED_GATHER")
-    if request.param:
-        os.environ["NGRAM_FUSED_GATHER"] = "1"
-    else:
-        os.environ.pop("NGRAM_FUSED_GATHER", None)
-    yield request.param
-    if old is None:
-        os.environ.pop("NGRAM_FUSED_GATHER", None)
-    else:
-        os.environ["NGRAM_FUSED_GATHER"] = old
-
-
-@pytest.mark.parametrize("fused_env", [False, True], indirect=True, ids=["materialised", "fused"])
-@pytest.mark.parametrize("plan_env", PLANS, indirect=True)
-def test_forward_each_plan(orc, plan_env, fused_env):
-    """Every tile plan on both forward routes: E materialised by the gather
-    kernel, or gathered by the projection itself."""
+@pytest.mark.parametrize("plan", PLANS)
+def test_forward_each_plan(orc, plan):
+    """Every tile plan in the forward pass (hash, gather to E, projection,
+    conv)."""
     H = G.H()
     w = W.get("qwen_prefill").replace(batch=3, seq_len=1100)
-    print(f"[plan {plan_env}] forward, fused gather {fused_env}", flush=True)
-    cfg = G.config(w, "d_mem")
+    print(f"[plan {plan}] forward", flush=True)
+    cfg = G.config(w, "d_mem", proj_plan=plan)
     ids, _ = W.make_ids(w)
     wk, wv = G.weights(w, "d_mem")
     hidden = SD.make_hidden(w, ids.size)
@@ -89,40 +61,27 @@ def test_forward_each_plan(orc, plan_env, fused_env):
                                       lambda toks: W.hidden_values(w, toks), wk_h, wv_h,
                                       W.conv_weight_values(w))
         got = G.to_f64(out[b, start:start + 20])
-        assert G.rel_err(got, ref["delta"]) < G.TOL
-        assert G.rel_err(gates[b, start:start + 20].cpu().numpy(), ref["gate"]) < G.TOL
+        G.check(got.reshape(ref["delta"].shape), ref["delta"], f"b={b} [{start}, +20)")
+        G.check(gates[b, start:start + 20].cpu().numpy().reshape(ref["gate"].shape), ref["gate"],
+                "gates")
 
 
-@pytest.fixture
-def decode_env(request):
-    old = os.environ.get("NGRAM_DECODE_PLAN")
-    if request.param == "default":
-        os.environ.pop("NGRAM_DECODE_PLAN", None)
-    else:
-        os.environ["NGRAM_DECODE_PLAN"] = request.param
-    yield request.param
-    if old is None:
-        os.environ.pop("NGRAM_DECODE_PLAN", None)
-    else:
-        os.environ["NGRAM_DECODE_PLAN"] = old
+# (ni, split): 16*ni weight columns per workgroup (ni 2..6), K slices (each a
+# multiple of 128 wide).  With K = 2560: 3 (48 columns) leaves a ragged last
+# column tile, 6 (96) another one; splits 2..20 give 40- down to 4-step slices.
+DECODE_PLANS = [None, (5, 4), (4, 4), (6, 4), (2, 2), (3, 5), (5, 10), (4, 20)]
 
 
-# "ni,split,ring": 16*ni weight columns per workgroup (ni 2..6), K slices
-# (each a multiple of 128 wide), K steps of E loads in flight (4).  With
-# K = 2560: 3 (48 columns) leaves a ragged last column tile, 6 (96) another
-# one; splits 2..10 give 20- down to 8-step slices.
-DECODE_PLANS = ["default", "5,4,4", "4,4,4", "6,4,4", "2,2,4", "3,5,4", "5,10,4", "4,20,4"]
-
-
-@pytest.mark.parametrize("decode_env", DECODE_PLANS, indirect=True)
+@pytest.mark.parametrize("plan", DECODE_PLANS, ids=lambda p: "default" if p is None else
+                         f"{p[0]}x{p[1]}")
 @pytest.mark.parametrize("name,batch", [("qwen_decode", 64), ("qwen_decode", 300),
                                         ("qwen_multibranch_zipf13", 64)])
-def test_decode_path_plans(orc, decode_env, name, batch):
+def test_decode_path_plans(orc, plan, name, batch):
     """One new token per sequence (T = 1): hash+gather, the weight-stationary
     projection and the decode finalize, with a populated conv state, the
     residual flag and random RMSNorm gains (300 rows: two ragged passes)."""
-    print(f"[decode plan {decode_env}] {name} batch {batch}", flush=True)
-    _decode_case(orc, name, batch)
+    print(f"[decode plan {plan}] {name} batch {batch}", flush=True)
+    _decode_case(orc, name, batch, plan=plan)
 
 
 def test_decode_1100_sequences(orc):
@@ -148,10 +107,10 @@ def test_decode_invalid_ids_are_pad(orc):
     _decode_case(orc, "qwen_decode", 300, bad_ids=True)
 
 
-def _decode_case(orc, name, batch, bad_ids=False):
+def _decode_case(orc, name, batch, bad_ids=False, plan=None):
     H = G.H()
     w = W.get(name).replace(batch=batch, seq_len=1, history_len=2)
-    cfg = G.config(w, "d_mem")
+    cfg = G.config(w, "d_mem", decode_plan=plan)
     ids, hist = W.make_ids(w)
     if bad_ids:
         ids[3, 0], ids[290, 0] = -5, w.vocab + 11
@@ -164,13 +123,16 @@ def _decode_case(orc, name, batch, bad_ids=False):
     state = rng.normal_f32(77, np.arange(w.batch * halo * nb * d), 1.0).reshape(w.batch, halo, nb, d)
     out = torch.empty((w.batch, 1, nb, d), dtype=torch.bfloat16, device="cuda")
     gates = torch.empty((w.batch, 1, nb), dtype=torch.float32, device="cuda")
+    ws = torch.empty(H.ngram_forward_workspace_size(cfg, w.batch, 1), dtype=torch.uint8,
+                     device="cuda")
     H.ngram_forward(cfg, torch.from_numpy(ids).cuda(), torch.from_numpy(W.make_lut(w)).cuda(),
                     G.tables(w), hidden, 0 if nb == 1 else d, wk, wv, G.conv_w(w), out,
                     history=torch.from_numpy(hist).cuda(), gamma_q=gam["q"], gamma_k=gam["k"],
                     gamma_u=gam["u"], conv_state=torch.from_numpy(state).cuda(), flags=1,
-                    gates=gates, err_flag=err)
+                    gates=gates, err_flag=err, workspace=ws)
     torch.cuda.synchronize()
     assert err.item() == (1 if bad_ids else 0)
+    G.check_forward_ids_and_memory(orc, w, ids, hist, cfg, ws)
     wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
     gh = {k: G.to_storage(v) for k, v in gam.items()}
     ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
@@ -181,8 +143,8 @@ def _decode_case(orc, name, batch, bad_ids=False):
     want = ref["delta"] + W.to_f64(W.hidden_values(w, np.arange(ids.size)), "bf16").reshape(
         w.batch, -1, d)[:, :1 if nb == 1 else nb]
     got = G.to_f64(out).reshape(want.shape)
-    assert G.rel_err(got, want) < G.TOL
-    assert G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"]) < G.TOL
+    G.check(got, want, "decode out")
+    G.check(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"], "decode gates")
 
 
 def test_single_token_large_batch_takes_prefill_route(orc):
@@ -208,5 +170,5 @@ def test_single_token_large_batch_takes_prefill_route(orc):
                       w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
                       W.hidden_values(w, np.arange(ids.size)), wk_h, wv_h,
                       W.conv_weight_values(w), "bf16", eps=w.rms_eps)
-    assert G.rel_err(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"]) < G.TOL
-    assert G.rel_err(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"]) < G.TOL
+    G.check(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"], "out")
+    G.check(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"], "gates")
