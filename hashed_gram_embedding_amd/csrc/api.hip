@@ -9,11 +9,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 using namespace ngram;
 
 thread_local ngram::StageClock* ngram::t_open_stage = nullptr;
+
+// The scratch of ngram_forward_noalloc: one copy per GPU, reserved with the
+// library's code object.  Host code never names it directly (the name is a
+// host-side stand-in there): it uses the device address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+static __device__ __align__(256) unsigned char scratch[NGRAM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -432,14 +441,36 @@ ConvArgs conv_args_base(const ngram_config* c) {
 }
 
 
-// Shared by ngram_forward, ngram_forward_timed and ngram_forward_noalloc.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up once per device
+// (nullptr if the device or the lookup fails).
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// Shared by ngram_forward, ngram_forward_timed and ngram_forward_noalloc
+// (static_scratch: the current device's static scratch replaces the
+// workspace, taken once every argument has passed its checks).
 int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
                  const int32_t* history, const int32_t* lut, const void* const* tables,
                  const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                  const void* w_v, const void* conv_w, const void* gamma_q, const void* gamma_k,
                  const void* gamma_u, float* conv_state, const int32_t* state_pos,
                  int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
-                 size_t workspace_bytes, hipStream_t s, Timer& tm) {
+                 size_t workspace_bytes, hipStream_t s, Timer& tm, bool static_scratch = false) {
   int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
@@ -461,6 +492,12 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
                         (const void*)conv_state, (const void*)out, (const void*)gates})
     if (!aligned16(p)) return NGRAM_EALIGN;
   const Layout L = layout_for(cfg, n_tok, true, T);
+  if (static_scratch) {  // ngram_forward_noalloc, after every other check
+    if (L.total > NGRAM_NOALLOC_SCRATCH_BYTES) return NGRAM_ESCRATCH;
+    workspace = device_scratch();
+    if (workspace == nullptr) return NGRAM_EHIP;
+    workspace_bytes = NGRAM_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace) return NGRAM_EWORKSPACE;
   if (workspace_bytes < L.total) return NGRAM_EWORKSPACE;
   if (!aligned16(workspace)) return NGRAM_EALIGN;
@@ -681,6 +718,9 @@ const char* ngram_status_str(int status) {
     case NGRAM_ERANGE: return "NGRAM_ERANGE: table rows not prime or out of range";
     case NGRAM_EHIP: return "NGRAM_EHIP: HIP launch failed";
     case NGRAM_EWORKSPACE: return "NGRAM_EWORKSPACE: workspace missing or too small";
+    case NGRAM_ESCRATCH:
+      return "NGRAM_ESCRATCH: the call needs more scratch than ngram_forward_noalloc holds "
+             "(NGRAM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown ngram status";
   }
 }
@@ -831,6 +871,20 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                       w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
                       out, gates, err_flag, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream), tm);
+}
+
+int ngram_forward_noalloc(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                          const int32_t* history, const int32_t* lut, const void* const* tables,
+                          const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                          const void* w_v, const void* conv_w, const void* gamma_q,
+                          const void* gamma_k, const void* gamma_u, float* conv_state,
+                          const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                          int32_t* err_flag, void* stream) {
+  Timer tm;
+  return forward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
+                      w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
+                      out, gates, err_flag, nullptr, 0, static_cast<hipStream_t>(stream), tm,
+                      true);
 }
 
 int ngram_forward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,

@@ -141,6 +141,8 @@ _BWD_ARGS = [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p
              _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 _SIGS["ngram_forward"] = (ctypes.c_int, _FWD_ARGS)
 _SIGS["ngram_forward_timed"] = (ctypes.c_int, _FWD_ARGS + [_p, _p])
+_SIGS["ngram_forward_noalloc"] = (ctypes.c_int, _FWD_ARGS[:-3] + [_p])
+NOALLOC_SCRATCH_BYTES = 64 << 20  # NGRAM_NOALLOC_SCRATCH_BYTES
 _SIGS["ngram_backward"] = (ctypes.c_int, _BWD_ARGS)
 _SIGS["ngram_backward_timed"] = (ctypes.c_int, _BWD_ARGS + [_p, _p])
 
@@ -310,6 +312,23 @@ def ngram_forward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, 
                                               history, gamma_q, gamma_k, gamma_u, conv_state,
                                               state_pos, flags, gates, err_flag, workspace,
                                               stream)), "ngram_forward")
+    return out
+
+
+def ngram_forward_noalloc(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v,
+                          conv_w, out, history=None, gamma_q=None, gamma_k=None, gamma_u=None,
+                          conv_state=None, state_pos=None, flags: int = 0, gates=None,
+                          err_flag=None, stream=None):
+    """ngram_forward without a workspace: the library's static per-GPU
+    scratch serves instead (calls on one GPU must not overlap)."""
+    B, T = raw_ids.shape
+    _check(lib().ngram_forward_noalloc(ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history),
+                                       _ptr(lut), _table_array(tables), _ptr(hidden),
+                                       hidden_branch_stride, _ptr(w_k), _ptr(w_v), _ptr(conv_w),
+                                       _ptr(gamma_q), _ptr(gamma_k), _ptr(gamma_u),
+                                       _ptr(conv_state), _ptr(state_pos), flags, _ptr(out),
+                                       _ptr(gates), _ptr(err_flag), _stream(stream)),
+           "ngram_forward_noalloc")
     return out
 
 

@@ -63,7 +63,8 @@ typedef enum ngram_status {
   NGRAM_EALIGN = -4,     /* a device pointer is not 16-byte aligned */
   NGRAM_ERANGE = -5,     /* a table row count is not prime / too large, ids out of range */
   NGRAM_EHIP = -6,       /* a HIP launch failed */
-  NGRAM_EWORKSPACE = -7  /* workspace missing or smaller than required */
+  NGRAM_EWORKSPACE = -7, /* workspace missing or smaller than required */
+  NGRAM_ESCRATCH = -8    /* ngram_forward_noalloc: the call needs more than its static scratch */
 } ngram_status;
 
 /*
@@ -361,6 +362,34 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
                    float* const* d_tables, float* d_w_k, float* d_w_v, float* d_conv_w,
                    float* d_hidden, float* d_gammas, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * ngram_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same work and the same kernels as ngram_forward, with the scratch taken
+ * from an array the library holds in device memory (NGRAM_NOALLOC_SCRATCH_BYTES
+ * per GPU, reserved when the library's code is loaded on that GPU and held
+ * until the process ends) instead of a caller's workspace.  The caller still
+ * passes every input and output.  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine; the first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress) on the current device,
+ * which must be the stream's.
+ * Returns NGRAM_ESCRATCH, launching nothing, when the call's scratch (what
+ * ngram_forward_workspace_size would ask for) exceeds the array: e.g. more
+ * than about 4,000 tokens of a prefill at the Qwen dimensions.
+ * Every call on one GPU shares that GPU's array and finds the previous call's
+ * contents there (no kernel needs it cleared): calls that may overlap on one
+ * GPU -- on different streams, or from different threads -- race and must be
+ * serialised by the caller.  ngram_forward_workspace_view does not apply.
+ */
+#define NGRAM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ngram_forward_noalloc(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                          const int32_t* history, const int32_t* lut, const void* const* tables,
+                          const void* hidden, int64_t hidden_branch_stride, const void* w_k,
+                          const void* w_v, const void* conv_w, const void* gamma_q,
+                          const void* gamma_k, const void* gamma_u, float* conv_state,
+                          const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                          int32_t* err_flag, void* stream);
 
 /*
  * Instrumented variants for benchmarks (not part of the layer): the same work

@@ -60,7 +60,7 @@ def test_config_layout_matches_c(H):
 
 def test_status_strings_and_version(H):
     assert H.ngram.abi_version() == 4
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert H.ngram.status_str(code).startswith("NGRAM_")
 
 
@@ -233,6 +233,21 @@ def test_entry_points_reject_before_launch(H):
     bad = list(args)
     bad[2], bad[3] = 0, 256
     assert L.ngram_forward_timed(*bad, events, ctypes.byref(mask)) == 0 and mask.value == 0
+    # the no-allocation forward: the same checks, then its static scratch's size
+    na = args[:21] + [None]
+    assert L.ngram_forward_noalloc(*na) != 0                 # no GPU here: the lookup fails
+    bad = list(na)
+    bad[17] = 4
+    assert L.ngram_forward_noalloc(*bad) == -1
+    bad = list(na)
+    bad[2], bad[3] = 0, 256
+    assert L.ngram_forward_noalloc(*bad) == 0
+    q = _cfg(H, "qwen_prefill")
+    big = [ctypes.byref(q)] + na[1:]
+    big[2], big[3] = 1, 8192                                 # ~16 KB per token > 64 MiB
+    big[6] = (ctypes.c_void_p * 16)(*([0x10000] * 8))
+    assert L.ngram_forward_workspace_size(ctypes.byref(q), 1, 8192) > H.ngram.NOALLOC_SCRATCH_BYTES
+    assert L.ngram_forward_noalloc(*big) == -8
 
 
 def test_workspace_sizes_scale(H):
