@@ -11,7 +11,13 @@ inputs are resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s, the step's share of the HBM roofline, the
 roofline of the dominant kernel (HIP-event timing of each stage, measured in
-this run), and the CPU oracle timed on this host on a bounded sample.
+this run), the attainable HBM bandwidth of a plain device copy, and the CPU
+oracle timed on this host on a bounded sample (all cores and one thread).
+Extra keys of the same line: the decode step with a conv-state ring (the
+realistic long-running decode), the step replayed from a HIP graph and the
+host cost of one call, and -- over the same resident tables -- the long
+prefill and the multi-branch sweep under both id distributions (with their
+row-reuse fractions), each with its own roofline figures.
 
 ``--pass backward`` measures a training step of the layer instead
 (ngram_forward then ngram_backward, default workload qwen_train: 16 x 4,096
@@ -49,8 +55,13 @@ def parse():
     ap.add_argument("--pool", type=int, default=64, help="distinct batches (decode)")
     ap.add_argument("--stage-steps", type=int, default=200,
                     help="steps of the per-stage event timing region")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time on all threads (a one-thread run takes 0.4x more)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the ring / graph / host extras and the other workloads")
+    ap.add_argument("--other-steps", type=int, default=6,
+                    help="timed steps of each other workload (long prefill, multi-branch)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -59,6 +70,19 @@ def parse():
 # ---------------------------------------------------------------------------
 # workload setup
 # ---------------------------------------------------------------------------
+
+_TABLES = {}
+
+
+def shared_tables(w):
+    """Device tables of a workload, built once per parameter set (the Qwen
+    workloads share one 95 GiB set)."""
+    from synth import device as SD
+    key = (w.param_seed, tuple(w.rows()), w.row_dim, w.tdtype)
+    if key not in _TABLES:
+        _TABLES[key] = SD.make_tables(w)
+    return _TABLES[key]
+
 
 class Setup:
     def __init__(self, name: str, pool: int):
@@ -72,11 +96,11 @@ class Setup:
         w = W.get(name)
         self.w = w
         # projection weights stored [d, mem] (torch.nn.Linear layout): the
-        # library's fast path, where the projection also hashes and gathers
+        # library's fast path
         self.cfg = H.make_config(**W.layer_config(w, "d_mem"))
         self.pool = pool if w.history_len else 1
         dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-        self.tables = SD.make_tables(w)
+        self.tables = shared_tables(w)
         self.wk, self.wv = SD.make_weights(w, layout="d_mem")
         conv = W.conv_weight_values(w)
         self.conv = (torch.from_numpy(conv).cuda() if w.dtype == "f32" else
@@ -99,6 +123,10 @@ class Setup:
         ws = H.ngram_forward_workspace_size(self.cfg, w.batch, w.seq_len)
         self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
         self.hbs = 0 if w.n_branches == 1 else w.hidden
+        # the conv-state ring of a long-running decode (step_ring): the last
+        # 3 * dil normalised rows of every sequence, updated in place
+        self.ring = None
+        self.ring_pos = None
         torch.cuda.synchronize()
 
     def step(self, p: int):
@@ -113,13 +141,51 @@ class Setup:
                                        s.hbs, s.wk, s.wv, s.conv, s.out, history=s.hist[p],
                                        workspace=s.ws)
 
+    def step_ring(self, p: int):
+        """One decode step of a long-running sequence batch: the ring supplies
+        the conv taps of the three earlier positions and receives this one's
+        normalised row (NGRAM_UPDATE_STATE, which also advances the
+        positions), and the output is the residual stream plus Delta
+        (NGRAM_ADD_RESIDUAL)."""
+        import torch
+        s = self
+        if s.ring is None:
+            w = s.w
+            s.ring = torch.zeros((w.batch, 3 * w.max_order, w.n_branches, w.hidden),
+                                 dtype=torch.float32, device="cuda")
+            s.ring_pos = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+        s.H.ngram_forward(s.cfg, s.ids[p], s.lut, s.tables, s.hidden[p], s.hbs, s.wk, s.wv,
+                          s.conv, s.out, history=s.hist[p], conv_state=s.ring,
+                          state_pos=s.ring_pos, flags=s.H.ADD_RESIDUAL | s.H.UPDATE_STATE,
+                          workspace=s.ws)
+
+    def row_reuse(self) -> float:
+        """Of the last step's row lookups, the fraction that named a row some
+        earlier token of the step had already named (per table, averaged over
+        the tables): the locality the caches can exploit.  The row ids are the
+        ones the forward itself left in its workspace."""
+        import torch
+        w = self.w
+        v = self.H.ngram_forward_workspace_view(self.cfg, w.batch, w.seq_len)
+        n = w.n_tokens
+        rows = self.ws[v.row_idx_offset:v.row_idx_offset + 4 * n * w.n_tables]
+        rows = rows.view(torch.int32).view(n, w.n_tables)
+        uniq = [int(torch.unique(rows[:, j]).numel()) for j in range(w.n_tables)]
+        return float(np.mean([1.0 - u / n for u in uniq]))
+
 
 # ---------------------------------------------------------------------------
 # algorithmic bytes / flops (what the method must move, not the design's
 # intermediates): ids in, gathered rows, query in, output out, weights once
 # ---------------------------------------------------------------------------
 
-def algorithmic(w):
+def algorithmic(w, ring: bool = False):
+    """Algorithmic bytes and FLOPs of one step, and their split over the
+    stages by the kernel that moves them: ids and gathered rows to the
+    hash / gather kernels, the weights to the projection, the query rows,
+    the output, the conv taps (and a ring's three taps read and one row
+    written, fp32) to the gate + conv kernel.  Intermediates of this design
+    (E, V, partial sums) are not algorithmic bytes."""
     es = 4 if w.dtype == "f32" else 2              # activations, weights, E
     tes = {"f32": 4, "bf16": 2, "fp8": 1}[w.tdtype]  # table storage
     n = w.n_tokens
@@ -130,16 +196,20 @@ def algorithmic(w):
     out_b = n * w.n_branches * w.hidden * es
     w_b = (w.n_branches + 1) * w.mem_dim * w.hidden * es
     conv_b = 4 * w.hidden * es
+    ring_b = 4 * 4 * n * w.n_branches * w.hidden if ring else 0
     flops = 2.0 * n * w.mem_dim * w.hidden * (w.n_branches + 1)
-    mem_b = n * w.mem_dim * es
     stages = {
-        "hash": dict(bytes=ids_b + 4 * n * w.n_tables, flops=0.0),
-        "gather": dict(bytes=4 * n * w.n_tables + rows_b + mem_b, flops=0.0),
-        "projection": dict(bytes=mem_b + w_b + hid_b, flops=flops),
-        "gate_conv": dict(bytes=out_b + conv_b, flops=0.0),
+        "hash": dict(bytes=ids_b, flops=0.0),
+        "gather": dict(bytes=rows_b, flops=0.0),
+        "projection": dict(bytes=w_b, flops=flops),
+        "gate_conv": dict(bytes=hid_b + out_b + conv_b + ring_b, flops=0.0),
     }
-    total = dict(bytes=ids_b + rows_b + hid_b + out_b + w_b + conv_b, flops=flops,
-                 per_token=(ids_b + rows_b + hid_b + out_b) / n, weights=w_b + conv_b)
+    if route(w) == "decode":  # one kernel hashes and gathers
+        stages["gather"]["bytes"] += ids_b
+        stages["hash"]["bytes"] = 0
+    total = dict(bytes=ids_b + rows_b + hid_b + out_b + w_b + conv_b + ring_b, flops=flops,
+                 per_token=(ids_b + rows_b + hid_b + out_b + ring_b) / n,
+                 weights=w_b + conv_b)
     return stages, total
 
 
@@ -204,6 +274,23 @@ def counter_traffic(stage: str, w):
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(setup: Setup, seconds: float):
+    """The oracle on all of the host's threads, then on one thread (for 40 %
+    of that time)."""
+    from oracle import oracle as O
+    O.lib()
+    cores = O.num_threads()
+    res = cpu_baseline_run(setup, seconds)
+    O.set_num_threads(1)
+    try:
+        one = cpu_baseline_run(setup, max(1.0, 0.4 * seconds))
+    finally:
+        O.set_num_threads(cores)
+    res["value_1thread"] = one["value"]
+    res["sample_1thread"] = one["sample"]
+    return res
+
+
+def cpu_baseline_run(setup: Setup, seconds: float):
     from oracle import oracle as O
 
     W, w = setup.W, setup.w
@@ -281,6 +368,183 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}), flush=True)
 
 
+def attainable_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """HBM bandwidth a plain device copy reaches: bytes read + bytes written
+    per second, over a copy much larger than the caches."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def prequeue(seconds: float):
+    """Hold the GPU with a spin kernel while the host enqueues the next region,
+    so that its steps then run back to back."""
+    import torch
+    torch.cuda._sleep(int(seconds * 2.5e9))
+
+
+def time_region(fn, steps: int, stream, pre: float = 0.0) -> float:
+    """Milliseconds per call of fn(i) over ``steps`` calls between two events
+    (synchronised on both sides)."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if pre:
+        prequeue(pre)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def stage_timing(setup: Setup, steps: int):
+    """Average kernel time of each stage (begin of its first kernel to the end
+    of its last, HIP events stamped by the kernels themselves) over ``steps``."""
+    import torch
+    ns = setup.H.ngram.N_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    prequeue(min(0.2, 3e-4 * steps + 0.01))
+    mask = 0
+    for i in range(steps):
+        mask = setup.step_timed(i % setup.pool, evs[i])
+    torch.cuda.synchronize()
+    names = setup.H.ngram.STAGE_NAMES
+    avg = {}
+    for k in range(ns):  # 0: absorbed into a later stage's kernel
+        avg[names[k]] = (float(np.mean([e[2 * k].elapsed_time(e[2 * k + 1]) for e in evs]))
+                         if mask >> k & 1 else 0.0)
+    return avg
+
+
+def roofline(stage_avg, stages_alg, w, attainable: float):
+    """Roofline of the dominant kernel (the stage with the largest kernel
+    time): its algorithmic bytes or FLOPs per launch over its average launch
+    time, against MI355X's published peak."""
+    dom = max(stage_avg, key=stage_avg.get)
+    sec = stage_avg[dom] * 1e-3
+    a = stages_alg[dom]
+    t_hbm = a["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = a["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if w.dtype == "bf16" and t_mfma > t_hbm:
+        roof = {"bound": "mfma", "achieved": a["flops"] / sec / 1e12,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": a["bytes"] / sec / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+        roof["frac_of_attainable"] = roof["achieved"] / attainable
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = counter_traffic(dom, w)
+    roof.update(kernel=dom, algorithmic_bytes=a["bytes"], algorithmic_flops=a["flops"],
+                avg_ms=stage_avg[dom])
+    return roof
+
+
+def step_fractions(w, total_alg, ms: float):
+    """The whole step against each roofline: algorithmic bytes at 8 TB/s,
+    FLOPs at 2.5 PFLOP/s, and the binding one (the larger of the two floors
+    over the step time)."""
+    t = ms * 1e-3
+    t_hbm = total_alg["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = total_alg["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return {"hbm_frac": t_hbm / t, "mfma_frac": t_mfma / t,
+            "binding": "hbm" if t_hbm >= t_mfma else "mfma",
+            "binding_frac": max(t_hbm, t_mfma) / t}
+
+
+def other_workload(name: str, steps: int, warmup: int, attainable: float):
+    """tokens/s, stage times and roofline figures of one more workload over the
+    tables already resident (the long prefill, the multi-branch sweep)."""
+    import torch
+    print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+    setup = Setup(name, 1)
+    w = setup.w
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        setup.step(0)
+    ms = time_region(lambda i: setup.step(0), steps, stream)
+    stages_alg, total_alg = algorithmic(w)
+    st = stage_timing(setup, max(2, steps // 2))
+    res = {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+           "branches": w.n_branches,
+           "ids": "uniform" if w.zipf_s is None else f"zipf {w.zipf_s}",
+           "tokens_per_step": w.n_tokens, "steps": steps, "ms_per_step": ms,
+           "tokens_per_s": w.n_tokens / (ms * 1e-3), "stage_ms": st,
+           "algorithmic_bytes_per_step": total_alg["bytes"],
+           "algorithmic_flops_per_step": total_alg["flops"],
+           "tflops": total_alg["flops"] / (ms * 1e-3) / 1e12,
+           "step_roofline": step_fractions(w, total_alg, ms),
+           "roofline": roofline(st, stages_alg, w, attainable),
+           "row_reuse": setup.row_reuse()}
+    del setup
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_extras(setup: Setup, steps: int):
+    """The headline decode step three more ways: with a conv-state ring (the
+    realistic long-running decode: three taps read, one row written, residual
+    added), replayed from a HIP graph of one pool of steps (no host work per
+    step), and the host time one ngram_forward call takes to submit."""
+    import torch
+    w = setup.w
+    stream = torch.cuda.current_stream()
+    res = {}
+    for i in range(20):
+        setup.step_ring(i % setup.pool)
+    ms_ring = time_region(lambda i: setup.step_ring(i % setup.pool), steps, stream)
+    _, tot_ring = algorithmic(w, ring=True)
+    res["decode_with_state"] = {
+        "ms_per_step": ms_ring, "tokens_per_s": w.n_tokens / (ms_ring * 1e-3),
+        "algorithmic_bytes_per_step": tot_ring["bytes"],
+        "hbm_pct_of_peak": 100.0 * tot_ring["bytes"] / (ms_ring * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "flags": "NGRAM_UPDATE_STATE | NGRAM_ADD_RESIDUAL"}
+    # host cost of one call: enqueue while a spin kernel holds the GPU
+    torch.cuda.synchronize()
+    prequeue(0.3)
+    t0 = time.perf_counter()
+    for i in range(200):
+        setup.step(i % setup.pool)
+    host_us = (time.perf_counter() - t0) / 200 * 1e6
+    torch.cuda.synchronize()
+    res["host_us_per_call"] = host_us
+    # graph replay of one pool of steps
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(setup.pool):
+                setup.step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // setup.pool)
+    ms_graph = time_region(lambda i: g.replay(), reps, stream) / setup.pool
+    res["graph_replay"] = {"ms_per_step": ms_graph,
+                           "tokens_per_s": w.n_tokens / (ms_graph * 1e-3),
+                           "steps": reps * setup.pool}
+    del g
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +561,8 @@ def main():
     args.workload = args.workload or "qwen_decode"
     args.steps = 2000 if args.steps is None else args.steps
     args.warmup = 100 if args.warmup is None else args.warmup
+    print("[bench] attainable HBM bandwidth (1 GiB device copy)", file=sys.stderr, flush=True)
+    attainable = attainable_gbs()
     print(f"[bench] setting up workload {args.workload}", file=sys.stderr, flush=True)
     setup = Setup(args.workload, args.pool)
     w = setup.w
@@ -310,70 +576,30 @@ def main():
 
     # ---- timed region: exactly `steps` steps, no instrumentation
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        setup.step(i % setup.pool)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = time_region(lambda i: setup.step(i % setup.pool), args.steps, stream)
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1)
-    ms_per_step = ms / args.steps
     tokens_per_s = w.n_tokens / (ms_per_step * 1e-3)
 
-    # ---- stage region: each stage's kernels stamp their own begin / end times
-    # into a HIP event pair on the stream they run on (hipExtLaunchKernel), and
-    # a plain event pair brackets the whole step
+    # ---- stage region: each stage's kernels stamp their own begin / end
+    # times into a HIP event pair on the stream they run on
     print(f"[bench] stage timing {args.stage_steps} steps", file=sys.stderr, flush=True)
-    ns = setup.H.ngram.N_STAGES
-    # a spin kernel holds the GPU while the host enqueues the region (the
-    # hook costs host time per step), so the steps then run back to back and
-    # host submission gaps stay out of the event pairs
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(min(0.2, 3e-4 * args.stage_steps) * 2.5e9))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)]
-           for _ in range(args.stage_steps)]
-    mask = 0
-    for i in range(args.stage_steps):
-        mask = setup.step_timed(i % setup.pool, evs[i])
-    torch.cuda.synchronize()
-    # per-step distribution: one plain event pair around each step, no stage hook
+    stage_avg = stage_timing(setup, args.stage_steps)
+    # per-step distribution: one plain event pair around each step
     step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.stage_steps)]
-    torch.cuda._sleep(int(min(0.2, 3e-4 * args.stage_steps) * 2.5e9))
+    torch.cuda.synchronize()
+    prequeue(min(0.2, 3e-4 * args.stage_steps + 0.01))
     for i in range(args.stage_steps):
         step_evs[i][0].record(stream)
         setup.step(i % setup.pool)
         step_evs[i][1].record(stream)
     torch.cuda.synchronize()
-    names = setup.H.ngram.STAGE_NAMES
-    stage_avg = {}
-    for k in range(ns):
-        if mask >> k & 1:
-            stage_avg[names[k]] = float(np.mean([e[2 * k].elapsed_time(e[2 * k + 1]) for e in evs]))
-        else:
-            stage_avg[names[k]] = 0.0  # absorbed into a later stage's kernel
     step_ms = np.array([a.elapsed_time(b) for a, b in step_evs])
-    dom = max(stage_avg, key=stage_avg.get)
-    dom_s = stage_avg[dom] * 1e-3
-    a = stages_alg[dom]
-    t_hbm = a["bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = a["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    if w.dtype == "bf16" and t_mfma > t_hbm:
-        roof = {"bound": "mfma", "achieved": a["flops"] / dom_s / 1e12,
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": a["bytes"] / dom_s / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic(dom, w)
-    roof["kernel"] = dom
-    roof["algorithmic_bytes"] = a["bytes"]
-    roof["algorithmic_flops"] = a["flops"]
-    roof["avg_ms"] = stage_avg[dom]
+    roof = roofline(stage_avg, stages_alg, w, attainable)
+    steprf = step_fractions(w, total_alg, ms_per_step)
+    roof["step_hbm_frac"] = steprf["hbm_frac"]
+    roof["step_hbm_frac_of_attainable"] = steprf["hbm_frac"] * HBM_PEAK_GBS / attainable
 
     hbm_gbs = total_alg["bytes"] / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -402,18 +628,34 @@ def main():
         "hbm_pct_of_peak": 100.0 * hbm_gbs / HBM_PEAK_GBS,
         "algorithmic_gbs": hbm_gbs,
         "algorithmic_bytes_per_step": total_alg["bytes"],
+        "attainable_hbm_gbs": attainable,
+        "hbm_pct_of_attainable": 100.0 * hbm_gbs / attainable,
         "tflops": total_alg["flops"] / (ms_per_step * 1e-3) / 1e12,
         "step_ms_p50": float(np.percentile(step_ms, 50)),
         "step_ms_p99": float(np.percentile(step_ms, 99)),
         "stage_ms": stage_avg,
+        "stage_algorithmic_bytes": {k: v["bytes"] for k, v in stages_alg.items()},
         "wall_s_timed": wall,
         "roofline": roof,
     }
+    if route(w) == "decode" and not args.no_extras:
+        print("[bench] decode with a conv-state ring, graph replay, host cost", file=sys.stderr,
+              flush=True)
+        result.update(decode_extras(setup, min(args.steps, 1000)))
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        print(f"[bench] cpu baseline (~{1.4 * args.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    if not args.no_extras and args.workload == "qwen_decode":
+        # the largest single-GPU configuration and the locality sweep, over the
+        # same resident tables
+        del setup
+        torch.cuda.empty_cache()
+        result["other_workloads"] = [
+            other_workload(n, args.other_steps, 2, attainable)
+            for n in ("qwen_prefill", "qwen_multibranch_uniform", "qwen_multibranch_zipf13")]
     print(json.dumps(result), flush=True)
 
 

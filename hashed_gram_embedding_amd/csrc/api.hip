@@ -468,14 +468,15 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
                  const int32_t* history, const int32_t* lut, const void* const* tables,
                  const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                  const void* w_v, const void* conv_w, const void* gamma_q, const void* gamma_k,
-                 const void* gamma_u, float* conv_state, const int32_t* state_pos,
+                 const void* gamma_u, float* conv_state, int32_t* state_pos,
                  int32_t flags, void* out, float* gates, int32_t* err_flag, void* workspace,
                  size_t workspace_bytes, hipStream_t s, Timer& tm, bool static_scratch = false) {
   int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
   if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_UPDATE_STATE)) return NGRAM_EINVAL;
-  if ((flags & NGRAM_UPDATE_STATE) && conv_state == nullptr) return NGRAM_EINVAL;
+  if ((flags & NGRAM_UPDATE_STATE) && (conv_state == nullptr || state_pos == nullptr))
+    return NGRAM_EINVAL;
   int64_t h_tok = 0;
   st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
   if (st) return st;
@@ -812,12 +813,13 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
 
 int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t T,
                       const void* conv_w, const void* gamma_u, float* conv_state,
-                      const int32_t* state_pos, int32_t flags, void* out, void* stream) {
+                      int32_t* state_pos, int32_t flags, void* out, void* stream) {
   int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
   if (flags & ~NGRAM_UPDATE_STATE) return NGRAM_EINVAL;
-  if ((flags & NGRAM_UPDATE_STATE) && conv_state == nullptr) return NGRAM_EINVAL;
+  if ((flags & NGRAM_UPDATE_STATE) && (conv_state == nullptr || state_pos == nullptr))
+    return NGRAM_EINVAL;
   if ((int64_t)B * T == 0) return NGRAM_OK;
   if (!u || !conv_w || !out) return NGRAM_EINVAL;
   for (const void* p : {u, conv_w, gamma_u, (const void*)conv_state, (const void*)out})
@@ -864,7 +866,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                   const void* w_v, const void* conv_w, const void* gamma_q,
                   const void* gamma_k, const void* gamma_u, float* conv_state,
-                  const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                  int32_t* state_pos, int32_t flags, void* out, float* gates,
                   int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream) {
   Timer tm;
   return forward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
@@ -878,7 +880,7 @@ int ngram_forward_noalloc(const ngram_config* cfg, const int32_t* raw_ids, int32
                           const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                           const void* w_v, const void* conv_w, const void* gamma_q,
                           const void* gamma_k, const void* gamma_u, float* conv_state,
-                          const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                          int32_t* state_pos, int32_t flags, void* out, float* gates,
                           int32_t* err_flag, void* stream) {
   Timer tm;
   return forward_impl(cfg, raw_ids, B, T, history, lut, tables, hidden, hidden_branch_stride,
@@ -892,7 +894,7 @@ int ngram_forward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t
                         const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                         const void* w_v, const void* conv_w, const void* gamma_q,
                         const void* gamma_k, const void* gamma_u, float* conv_state,
-                        const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                        int32_t* state_pos, int32_t flags, void* out, float* gates,
                         int32_t* err_flag, void* workspace, size_t workspace_bytes,
                         void* stream, void* const* stage_events, int32_t* stage_mask) {
   if (stage_events == nullptr) return NGRAM_EINVAL;

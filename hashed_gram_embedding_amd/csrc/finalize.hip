@@ -92,6 +92,16 @@ __device__ __forceinline__ float inv_rms_row(const T* row, int d, float eps, int
   return 1.0f / sqrtf(ss / (float)d + eps);
 }
 
+// With a ring update, sequence b's ring position moves on by the call's
+// positions.  Every thread of the workgroup read the position from memory and
+// used it (in the addresses of ring reads or writes issued before this
+// point), so after the barrier no read of it can still see the new value.
+__device__ __forceinline__ void advance_ring(const ConvArgs& a, int64_t b, int pos, int T) {
+  if (!a.update_state) return;
+  __syncthreads();
+  if (threadIdx.x == 0) a.state_pos[b] = pos + T;
+}
+
 // ngram_gate: gates and U = g V in the activation dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_values_kernel(ConvArgs a, int64_t M) {
@@ -297,6 +307,8 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
   const T* __restrict__ GQ = static_cast<const T*>(a.gamma_q);
   const T* __restrict__ GK = static_cast<const T*>(a.gamma_k);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int halo = 3 * dil;
+  const int pos = a.state ? ring_pos(a.state_pos, tok, halo) : 0;
 
   auto col4 = [&](int64_t off, int c) {  // sum of the splits, 4 columns
     float4 x = *reinterpret_cast<const float4*>(P + off + c);
@@ -344,8 +356,6 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
   const T* __restrict__ CW = static_cast<const T*>(a.conv_w);
   const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
   T* __restrict__ OUT = static_cast<T*>(a.out);
-  const int halo = 3 * dil;
-  const int pos = a.state ? ring_pos(a.state_pos, tok, halo) : 0;
   for (int br = 0; br < nb; ++br) {
     RowSums r{s_tot[3 * br], s_tot[3 * br + 1], s_tot[3 * br + 2], s_tot[3 * NGRAM_MAX_BRANCHES]};
     float al, sc;
@@ -380,6 +390,7 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
       Elem<T>::store4(OUT, (tok * nb + br) * d + c, D);
     }
   }
+  advance_ring(a, tok, pos, 1);
 }
 
 // The same for d <= 1024 * ITEMS and NB branches, in registers: thread x owns
@@ -446,6 +457,9 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
   const T* __restrict__ gk_p = has_gk ? GK : CW;
   const T* __restrict__ gu_p = has_gu ? GU : CW;
 
+  // the ring position first: the taps' addresses wait for it alone
+  const int halo = 3 * dil;
+  const int pos = a.state ? ring_pos(a.state_pos, tok, halo) : 0;
   float4 v[ITEMS], h[NB][ITEMS], k[NB][ITEMS], gq[ITEMS], gk[ITEMS], cw0[ITEMS], gu[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
@@ -459,6 +473,29 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
     gk[i] = Elem<T>::load4(gk_p, col[i]);
     cw0[i] = Elem<T>::load4(CW, col[i]);
     gu[i] = Elem<T>::load4(gu_p, col[i]);
+  }
+  // the ring's taps at positions -dil, -2 dil, -3 dil (dropped before the
+  // sequence's start), loaded with the rest when they fit in registers; every
+  // read of the ring precedes this call's write to it
+  constexpr bool kPreTaps = NB * ITEMS <= 4;
+  float4 tap[kPreTaps ? NB : 1][3][kPreTaps ? ITEMS : 1];
+  float tw[3];
+  int tslot[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int sl = ring_slot(pos, -(t + 1) * dil, halo);
+    tw[t] = sl >= 0 ? 1.0f : 0.0f;
+    tslot[t] = sl >= 0 ? sl : 0;
+  }
+  if (kPreTaps && a.state) {
+#pragma unroll
+    for (int br = 0; br < (kPreTaps ? NB : 1); ++br)
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int i = 0; i < (kPreTaps ? ITEMS : 1); ++i)
+          tap[br][t][i] = *reinterpret_cast<const float4*>(
+              a.state + ((tok * halo + tslot[t]) * NB + br) * d + col[i]);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above issued before the first wait
   float acc[NQ];
@@ -491,8 +528,6 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
 
   const float fd = (float)d;
   T* __restrict__ OUT = static_cast<T*>(a.out);
-  const int halo = 3 * dil;
-  const int pos = a.state ? ring_pos(a.state_pos, tok, halo) : 0;
   float4 gun[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) gun[i] = gain(gu[i], has_gu);
@@ -507,15 +542,15 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
       const float4 nrm = mul4(mul4(gun[i], v[i]), f4(sc));  // this position's normalised row
       float4 C = mul4(cw0[i], nrm);
       if (a.state) {
-        // taps at positions -dil, -2 dil, -3 dil from the ring, zero before
-        // the sequence's start; every read precedes the write below
-        for (int t = 1; t < 4; ++t) {
-          const int slot = ring_slot(pos, -t * dil, halo);
-          if (slot >= 0) {
-            const float4 st = *reinterpret_cast<const float4*>(
-                a.state + ((tok * halo + slot) * NB + br) * d + col[i]);
-            C = fma4(Elem<T>::load4(CW, (int64_t)t * d + col[i]), st, C);
-          }
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const float4 st = kPreTaps ? tap[kPreTaps ? br : 0][t][kPreTaps ? i : 0]
+                                     : *reinterpret_cast<const float4*>(
+                                           a.state + ((tok * halo + tslot[t]) * NB + br) * d + col[i]);
+          // a position before the sequence's start contributes zero, whatever
+          // its slot holds (selected, not weighted: the slot may hold NaN)
+          C = fma4(Elem<T>::load4(CW, (int64_t)(t + 1) * d + col[i]), tw[t] != 0.0f ? st : f4(0.0f),
+                   C);
         }
         if (a.update_state && ok[i])
           *reinterpret_cast<float4*>(a.state + ((tok * halo + pos % halo) * NB + br) * d + col[i]) =
@@ -527,61 +562,67 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
       if (ok[i]) Elem<T>::store4(OUT, (tok * NB + br) * d + col[i], D);
     }
   }
+  advance_ring(a, tok, pos, 1);
 }
 
 // Ring update after a conv over a [B, T] grid: the normalised rows of the last
-// min(T, 3*DIL) positions of sequence blockIdx.x, branch blockIdx.y, into
-// their slots.  The scalars come from the same folds as the conv's (so the
-// rows equal the ones the conv used): from V and the partials (FUSED) or
-// from the U rows.
+// min(T, 3*DIL) positions of sequence blockIdx.x, every branch, into their
+// slots, and the sequence's ring position advanced by T.  The scalars come
+// from the same folds as the conv's (so the rows equal the ones the conv
+// used): from V and the partials (FUSED) or from the U rows.
 template <int DIL, typename T, bool FUSED>
 __global__ __launch_bounds__(256) void state_update_kernel(ConvArgs a) {
   constexpr int HALO = 3 * DIL;
-  __shared__ float s_scale[HALO];
+  __shared__ float s_scale[NGRAM_MAX_BRANCHES][HALO];
   const int64_t b = blockIdx.x;
-  const int br = blockIdx.y;
   const int nb = a.nb, d = a.d;
-  const int n = a.T < HALO ? a.T : HALO;  // rows written
+  const int n = a.T < HALO ? a.T : HALO;  // rows written per branch
   const int q0 = a.T - n;                  // first position written
   const int64_t seq0 = b * a.T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int pos = ring_pos(a.state_pos, b, HALO);
   if (FUSED) {
     const int sub = lane & 15, grp = lane >> 4;
-    for (int i0 = wave * 4; i0 < n; i0 += nw * 4) {
-      const int i = i0 + grp;
-      const int64_t tok = seq0 + q0 + (i < n ? i : 0);
+    for (int i0 = wave * 4; i0 < n * nb; i0 += nw * 4) {
+      const int k = i0 + grp;             // (branch, row) pair k = br * n + i
+      const int kk = k < n * nb ? k : 0;
+      const int br = kk / n, i = kk - br * n;
+      const int64_t tok = seq0 + q0 + i;
       const RowSums r = fold_partials16(a.parts + tok * (3 * nb + 1) * a.np, a.np, br, nb, sub);
-      if (sub == 0 && i < n) {
+      if (sub == 0 && k < n * nb) {
         float al, sc;
         gate_and_scale(r, (float)d, a.eps, al, sc);
-        s_scale[i] = sc;
+        s_scale[br][i] = sc;
       }
     }
   } else {
     const T* U = static_cast<const T*>(a.u);
-    for (int i = wave; i < n; i += nw) {
+    for (int k = wave; k < n * nb; k += nw) {
+      const int br = k / n, i = k - br * n;
       const float sc = inv_rms_row(U + ((seq0 + q0 + i) * nb + br) * d, d, a.eps, lane);
-      if (lane == 0) s_scale[i] = sc;
+      if (lane == 0) s_scale[br][i] = sc;
     }
   }
   __syncthreads();
   const T* __restrict__ GU = static_cast<const T*>(a.gamma_u);
-  const int pos = ring_pos(a.state_pos, b, HALO);
   for (int c0 = threadIdx.x * 4; c0 < d; c0 += blockDim.x * 4) {
     const float4 gu = GU ? Elem<T>::load4(GU, c0) : f4(1.0f);
-    for (int i = 0; i < n; ++i) {
-      const int64_t tok = seq0 + q0 + i;
-      float4 src;
-      if (FUSED) {
-        src = *reinterpret_cast<const float4*>(a.v + tok * a.v_stride + c0);
-      } else {
-        src = Elem<T>::load4(static_cast<const T*>(a.u), (tok * nb + br) * d + c0);
+    for (int br = 0; br < nb; ++br) {
+      for (int i = 0; i < n; ++i) {
+        const int64_t tok = seq0 + q0 + i;
+        float4 src;
+        if (FUSED) {
+          src = *reinterpret_cast<const float4*>(a.v + tok * a.v_stride + c0);
+        } else {
+          src = Elem<T>::load4(static_cast<const T*>(a.u), (tok * nb + br) * d + c0);
+        }
+        const int slot = (pos + q0 + i) % HALO;
+        *reinterpret_cast<float4*>(a.state + ((b * HALO + slot) * nb + br) * d + c0) =
+            mul4(mul4(gu, src), f4(s_scale[br][i]));
       }
-      const int slot = (pos + q0 + i) % HALO;
-      *reinterpret_cast<float4*>(a.state + ((b * HALO + slot) * nb + br) * d + c0) =
-          mul4(mul4(gu, src), f4(s_scale[i]));
     }
   }
+  advance_ring(a, b, pos, a.T);
 }
 
 template <typename T, bool FUSED>
@@ -688,8 +729,8 @@ hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split
 
 hipError_t launch_state_update(int dtype, bool fused, int32_t dil, const ConvArgs& a,
                                hipStream_t s) {
-  if (a.B == 0 || a.T == 0 || a.state == nullptr) return hipSuccess;
-  const dim3 grid((unsigned)a.B, (unsigned)a.nb);
+  if (a.B == 0 || a.T == 0 || a.state == nullptr || a.state_pos == nullptr) return hipSuccess;
+  const dim3 grid((unsigned)a.B);
 #define NGRAM_SU(D)                                                                         \
   if (dtype == NGRAM_BF16)                                                                  \
     return fused ? launch(state_update_kernel<D, bf16_bits, true>, grid, 256, 0, s, a)      \

@@ -185,9 +185,9 @@ struct ConvArgs {
   // conv-state ring [B, 3*dil, nb, d] (nullable): the normalised row of
   // absolute position p in slot p mod 3*dil; state_pos[b] (nullable = 3*dil)
   // positions of sequence b precede this call's first token; update_state:
-  // the call writes its last rows into the ring
+  // the call writes its last rows into the ring and advances state_pos by T
   float* state;
-  const int32_t* state_pos;
+  int32_t* state_pos;
   int32_t update_state;
   const void* hidden;     // residual source (flag)
   int64_t h_tok_stride, h_branch_stride;

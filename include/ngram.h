@@ -236,12 +236,13 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
  * cleared (state_pos = 0).  A negative state_pos is read as 0.
  * state_pos NULL means state_pos = R for every sequence: slot s holds position
  * s - R, oldest first.
- * With NGRAM_UPDATE_STATE the call also writes the normalised rows of its last
- * min(T, R) positions into their slots (position state_pos[b] + t goes to slot
- * (state_pos[b] + t) mod R), in place, after every read of the ring it needs:
- * the caller then advances state_pos[b] by T, and decode becomes one call per
- * token that costs one ring row written and three read per sequence and
- * branch.
+ * With NGRAM_UPDATE_STATE (which needs both conv_state and state_pos) the call
+ * also writes the normalised rows of its last min(T, R) positions into their
+ * slots (position state_pos[b] + t goes to slot (state_pos[b] + t) mod R), in
+ * place, after every read of the ring it needs, and advances state_pos[b] by
+ * T: the next call of the same sequences passes both on as they are, and
+ * decode becomes one call per token that costs one ring row written and
+ * three read per sequence and branch.
  */
 
 /*
@@ -255,13 +256,14 @@ int ngram_gate(const ngram_config* cfg, const void* hidden, int64_t hidden_branc
  *   gamma_u    device [d] act_dtype, nullable (= 1)
  *   conv_state device float[B, R, n_branches, d] ring of normalised rows (see
  *              above), nullable (zeros before position 0)
- *   state_pos  device int32[B], nullable (see above)
- *   flags      0 or NGRAM_UPDATE_STATE (which needs conv_state)
+ *   state_pos  device int32[B], nullable (see above); advanced in place by
+ *              NGRAM_UPDATE_STATE
+ *   flags      0 or NGRAM_UPDATE_STATE (which needs conv_state and state_pos)
  *   out        device [B, T, n_branches, d] act_dtype (output)
  */
 int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t T,
                       const void* conv_w, const void* gamma_u, float* conv_state,
-                      const int32_t* state_pos, int32_t flags, void* out, void* stream);
+                      int32_t* state_pos, int32_t flags, void* out, void* stream);
 
 /*
  * The whole layer in one call (steps 1-8 above), intermediates in fp32: K is
@@ -292,7 +294,7 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                   const void* w_v, const void* conv_w, const void* gamma_q,
                   const void* gamma_k, const void* gamma_u, float* conv_state,
-                  const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                  int32_t* state_pos, int32_t flags, void* out, float* gates,
                   int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -388,7 +390,7 @@ int ngram_forward_noalloc(const ngram_config* cfg, const int32_t* raw_ids, int32
                           const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                           const void* w_v, const void* conv_w, const void* gamma_q,
                           const void* gamma_k, const void* gamma_u, float* conv_state,
-                          const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                          int32_t* state_pos, int32_t flags, void* out, float* gates,
                           int32_t* err_flag, void* stream);
 
 /*
@@ -414,7 +416,7 @@ int ngram_forward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t
                         const void* hidden, int64_t hidden_branch_stride, const void* w_k,
                         const void* w_v, const void* conv_w, const void* gamma_q,
                         const void* gamma_k, const void* gamma_u, float* conv_state,
-                        const int32_t* state_pos, int32_t flags, void* out, float* gates,
+                        int32_t* state_pos, int32_t flags, void* out, float* gates,
                         int32_t* err_flag, void* workspace, size_t workspace_bytes,
                         void* stream, void* const* stage_events, int32_t* stage_mask);
 int ngram_backward_timed(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,

@@ -193,6 +193,7 @@ def test_entry_points_reject_before_launch(H):
     assert L.ngram_causal_conv(ref, fake, 1, 8, odd, None, None, None, 0, fake, None) == -4
     assert L.ngram_causal_conv(ref, fake, 1, 8, fake, None, None, None, 2, fake, None) == -1
     assert L.ngram_causal_conv(ref, fake, 1, 8, fake, None, fake, None, 4, fake, None) == -1
+    assert L.ngram_causal_conv(ref, fake, 1, 8, fake, None, fake, None, 2, fake, None) == -1
     assert L.ngram_causal_conv(ref, fake, 1, 8, fake, None, fake, ctypes.c_void_p(0x10002), 2,
                                fake, None) == -4
     # forward
@@ -205,6 +206,9 @@ def test_entry_points_reject_before_launch(H):
     assert L.ngram_forward(*bad) == -1
     bad = list(args)
     bad[17] = 2                                            # ring update without a ring
+    assert L.ngram_forward(*bad) == -1
+    bad = list(args)
+    bad[15], bad[17] = fake, 2                             # ... or without its positions
     assert L.ngram_forward(*bad) == -1
     bad = list(args)
     bad[16] = ctypes.c_void_p(0x10002)                     # state_pos misaligned

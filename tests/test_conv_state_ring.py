@@ -5,7 +5,7 @@ causal conv over RMSNorm(U) along the sequence, so a sequence that arrives in
 pieces needs the last 3 * dil normalised rows of the earlier pieces.  With
 NGRAM_UPDATE_STATE ngram_forward writes them into the caller's ring: these
 tests feed sequences one token (or one chunk) per call, carrying only the ring
-and its positions from call to call, and compare with one call over the whole
+and its positions (which the library advances) from call to call, and compare with one call over the whole
 sequence and with the oracle -- outputs within the parity tolerance, row ids
 bit-identical, the ring's rows against the oracle's normalised rows."""
 import numpy as np
@@ -137,7 +137,7 @@ def test_decode_steps_equal_prefill(orc, name, nb, B, L, flags):
         outs.append(o)
         gates.append(g)
         rows.append(layer.row_ids(ws, B, 1))
-        pos += 1
+    assert torch.equal(pos, torch.full_like(pos, L))      # advanced by the library
     out_d = torch.cat(outs, dim=1)
     gates_d = torch.cat(gates, dim=1)
     rows_d = np.stack(rows, axis=1).reshape(B * L, -1)
@@ -179,8 +179,8 @@ def test_chunks_then_decode_equal_prefill(orc, layout):
         torch.cuda.synchronize()
         assert np.array_equal(layer.row_ids(ws, B, T).reshape(B, T, -1), rows_p[:, t0:t0 + T])
         outs.append(o)
-        pos += T
         t0 += T
+        assert torch.equal(pos, torch.full_like(pos, t0))
     G.check(G.to_f64(torch.cat(outs, dim=1)), G.to_f64(out_p), "chunks against one call")
     ref = _oracle(orc, layer, ids, W.hidden_values(w, np.arange(B * L)))
     want = ref["delta"].reshape(B, L, 1, w.hidden) + W.to_f64(
@@ -283,9 +283,9 @@ def test_op_conv_chunks_equal_one_call(orc, chunks):
                             G.conv_w(w), o, gamma_u=gam["u"], conv_state=ring, state_pos=pos,
                             flags=H.UPDATE_STATE)
         outs.append(o)
-        pos += T
         t0 += T
     torch.cuda.synchronize()
+    assert torch.equal(pos, torch.full_like(pos, L))
     G.check(G.to_f64(torch.cat(outs, dim=1)), G.to_f64(full), "chunks against one call")
     ref = orc.conv_block(W.to_f64(u, "bf16"), W.conv_weight_values(w), "bf16", w.max_order,
                          G.to_storage(gam["u"]), w.rms_eps)

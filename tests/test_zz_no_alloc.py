@@ -39,8 +39,9 @@ def _both(w, layout, inp, ring0=None, pos=None, flags=1):
         gates = torch.empty((B, T, w.n_branches), dtype=torch.float32, device="cuda")
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
         ring = None if ring0 is None else ring0.clone()
+        p = None if pos is None else pos.clone()
         kw = dict(history=inp["hist"], gamma_q=inp["gam"]["q"], gamma_k=inp["gam"]["k"],
-                  gamma_u=inp["gam"]["u"], conv_state=ring, state_pos=pos, flags=flags,
+                  gamma_u=inp["gam"]["u"], conv_state=ring, state_pos=p, flags=flags,
                   gates=gates, err_flag=err)
         args = (cfg, inp["ids"], inp["lut"], inp["tables"], inp["hidden"], hbs, inp["wk"],
                 inp["wv"], inp["conv_w"], out)
@@ -49,18 +50,20 @@ def _both(w, layout, inp, ring0=None, pos=None, flags=1):
         else:
             H.ngram_forward(*args, **kw)
         torch.cuda.synchronize()
-        res.append((out, gates, err, ring))
+        res.append((out, gates, err, ring, p))
     return res
 
 
 def _same(res):
-    (o1, g1, e1, r1), (o2, g2, e2, r2) = res
+    (o1, g1, e1, r1, p1), (o2, g2, e2, r2, p2) = res
     bits = torch.int16 if o1.dtype == torch.bfloat16 else torch.int32
     assert torch.equal(o1.view(bits), o2.view(bits)), "out"
     assert torch.equal(g1, g2), "gates"
     assert e1.item() == e2.item()
     if r1 is not None:
         assert torch.equal(r1, r2), "ring"
+    if p1 is not None:
+        assert torch.equal(p1, p2), "ring positions"
 
 
 def test_noalloc_decode_route_two_calls():
