@@ -59,6 +59,10 @@ MUTANTS = [
     ("projection backward uses W transposed",
      "acc += d_out[t * d + n] * load_value(w, dtype, (int64_t)m * d + n);",
      "acc += d_out[t * d + n] * load_value(w, dtype, (int64_t)n * mem + m);"),
+    ("normalised rows drop gamma_u", "out[r * d + n] = g * x[n] * inv;",
+     "out[r * d + n] = x[n] * inv;"),
+    ("normalised rows drop epsilon", "const double inv = 1.0 / sqrt(ss / d + eps);\n    for (int32_t n = 0; n < d; ++n) {\n      const double g",
+     "const double inv = 1.0 / sqrt(ss / d);\n    for (int32_t n = 0; n < d; ++n) {\n      const double g"),
 ]
 
 # the pins run against each mutant (test function, keyword arguments)
@@ -83,6 +87,7 @@ PINS = [
     (P.test_conv_single_tap_alignment, {"tap": 1}),
     (P.test_conv_single_tap_alignment, {"tap": 2}),
     (P.test_conv_causal_and_state_streaming, {}),
+    (P.test_normalised_rows, {}),
     (P.test_fp8_decode_definition_and_library, {}),
     (P.test_gather_fp8_scaled_bf16, {}),
     (BW.test_backward_matches_finite_differences, dict(nb=2, nbh=2, with_state=True, residual=False)),

@@ -161,3 +161,45 @@ def test_backward_rejects_unsupported():
                          G.tables(w), x, 0, x, x, x, x, [x] * w.n_tables, x, x, x,
                          workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
     assert e.value.status == -3  # NGRAM_EDTYPE
+
+
+def test_backward_deterministic_gradients_run_to_run():
+    """Two identical backward calls: the W_K, W_V, conv-tap, query and gain
+    gradients are bit-identical (fixed-order sums, no atomics); only the table
+    gradients, accumulated with fp32 atomics where tokens share a row, may
+    differ in their last bits, and only within rounding."""
+    H = G.H()
+    w = W.get("engram_small").replace(batch=3, seq_len=300, hidden=512, heads=2,
+                                      row_start=10007, n_branches=2)
+    print("[backward] run-to-run determinism", flush=True)
+    ids, hist = W.make_ids(w)
+    n, nb, d = ids.size, w.n_branches, w.hidden
+    cfg = G.config(w, "d_mem")
+    wk, wv = G.weights(w, "d_mem")
+    gam = G.gammas(w, True)
+    rs = np.random.default_rng(21)
+    hidden = _bf16(rs.standard_normal((n, nb, d)).astype(np.float32))
+    d_out = _bf16(rs.standard_normal((n, nb, d)).astype(np.float32))
+    state = torch.from_numpy(rs.standard_normal((w.batch, 3 * w.max_order, nb, d))
+                             .astype(np.float32)).cuda()
+    runs = []
+    for _ in range(2):
+        g = dict(tabs=[torch.zeros((r, w.row_dim), dtype=torch.float32, device="cuda")
+                       for r in w.rows()],
+                 wk=torch.empty((nb, d, w.mem_dim), dtype=torch.float32, device="cuda"),
+                 wv=torch.empty((d, w.mem_dim), dtype=torch.float32, device="cuda"),
+                 cw=torch.empty((4, d), dtype=torch.float32, device="cuda"),
+                 h=torch.empty((n, nb, d), dtype=torch.float32, device="cuda"),
+                 gm=torch.empty((3, d), dtype=torch.float32, device="cuda"))
+        H.ngram_backward(cfg, torch.from_numpy(ids).cuda(),
+                         torch.from_numpy(W.make_lut(w)).cuda(), G.tables(w), hidden, d, wk, wv,
+                         G.conv_w(w), d_out, g["tabs"], g["wk"], g["wv"], g["cw"],
+                         gamma_q=gam["q"], gamma_k=gam["k"], gamma_u=gam["u"], conv_state=state,
+                         flags=1, d_hidden=g["h"], d_gammas=g["gm"])
+        torch.cuda.synchronize()
+        runs.append(g)
+    a, b = runs
+    for k in ("wk", "wv", "cw", "h", "gm"):
+        assert torch.equal(a[k], b[k]), k
+    for ta, tb in zip(a["tabs"], b["tabs"]):
+        assert G.rel_err(tb.double().cpu().numpy(), ta.double().cpu().numpy()) < 1e-6
