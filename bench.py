@@ -76,10 +76,13 @@ _TABLES = {}
 
 def shared_tables(w):
     """Device tables of a workload, built once per parameter set (the Qwen
-    workloads share one 95 GiB set)."""
+    workloads share one 95 GiB set; the 16 x 160 geometry has its own)."""
     from synth import device as SD
+    import torch
     key = (w.param_seed, tuple(w.rows()), w.row_dim, w.tdtype)
     if key not in _TABLES:
+        _TABLES.clear()  # one 95 GiB set resident at a time
+        torch.cuda.empty_cache()
         _TABLES[key] = SD.make_tables(w)
     return _TABLES[key]
 
@@ -253,10 +256,9 @@ def stage_source_sha(stage: str, w):
     return None if srcs is None else source_sha(srcs)
 
 
-def counter_traffic(stage: str, w):
-    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
-    counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for
-    a plain copy of known size), or None when none were taken for this kernel
+def counter_record(stage: str, w):
+    """The committed rocprofv3 record of the stage's kernel at this workload
+    (profiles/counters.json), or None when none was taken for this kernel
     source and workload."""
     if not os.path.exists(COUNTERS):
         return None
@@ -266,7 +268,15 @@ def counter_traffic(stage: str, w):
     sha = stage_source_sha(stage, w)
     if not rec or sha is None or rec.get("source_sha") != sha:
         return None
-    return float(rec["traffic_bytes"])
+    return rec
+
+
+def counter_traffic(stage: str, w):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for
+    a plain copy of known size), or None."""
+    rec = counter_record(stage, w)
+    return None if rec is None else float(rec["traffic_bytes"])
 
 
 # ---------------------------------------------------------------------------
@@ -452,6 +462,12 @@ def roofline(stage_avg, stages_alg, w, attainable: float):
         roof["frac_of_attainable"] = roof["achieved"] / attainable
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, w)
+    rec = counter_record(dom, w)
+    if rec is not None:  # the same figure over the committed rocprofv3 average
+        t = rec["rocprof_avg_us"] * 1e-6
+        work = a["flops"] / 1e12 if roof["unit"] == "TFLOP/s" else a["bytes"] / 1e9
+        roof["avg_ms_rocprof"] = rec["rocprof_avg_us"] * 1e-3
+        roof["frac_rocprof"] = work / t / roof["peak"]
     roof.update(kernel=dom, algorithmic_bytes=a["bytes"], algorithmic_flops=a["flops"],
                 avg_ms=stage_avg[dom])
     return roof
@@ -477,12 +493,15 @@ def other_workload(name: str, steps: int, warmup: int, attainable: float):
     setup = Setup(name, 1)
     w = setup.w
     stream = torch.cuda.current_stream()
+    if w.history_len:  # a decode step: many steps, pre-queued
+        steps *= 100
     for i in range(warmup):
         setup.step(0)
     ms = time_region(lambda i: setup.step(0), steps, stream)
     stages_alg, total_alg = algorithmic(w)
     st = stage_timing(setup, max(2, steps // 2))
     res = {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len,
+           "tables": f"{w.n_tables} x {w.rows()[0]}.. rows x {w.row_dim} {w.tdtype}",
            "branches": w.n_branches,
            "ids": "uniform" if w.zipf_s is None else f"zipf {w.zipf_s}",
            "tokens_per_step": w.n_tokens, "steps": steps, "ms_per_step": ms,
@@ -655,7 +674,8 @@ def main():
         torch.cuda.empty_cache()
         result["other_workloads"] = [
             other_workload(n, args.other_steps, 2, attainable)
-            for n in ("qwen_prefill", "qwen_multibranch_uniform", "qwen_multibranch_zipf13")]
+            for n in ("qwen_prefill", "qwen_multibranch_uniform", "qwen_multibranch_zipf13",
+                      "qwen_decode_16x160", "qwen_prefill_16x160")]
     print(json.dumps(result), flush=True)
 
 

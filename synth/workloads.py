@@ -205,6 +205,17 @@ WORKLOADS = {
                                  history_len=0, orders=(2, 3), heads=4, row_start=20000003,
                                  row_dim=320, hidden=2560, n_branches=1, dtype="bf16",
                                  zipf_s=1.1, copy_prob=0.2, param_index=3, table_dtype="fp8"),
+    # the page's own table geometry: 16 tables (8 heads per order) of ~20M rows
+    # x 160 bf16 values -- the same 2,560-wide E and 51.2B parameters, but
+    # 320-byte rows that straddle 128-byte lines
+    "qwen_decode_16x160": Workload("qwen_decode_16x160", 8, vocab=248320, batch=256, seq_len=1,
+                                   history_len=2, orders=(2, 3), heads=8, row_start=20000003,
+                                   row_dim=160, hidden=2560, n_branches=1, dtype="bf16",
+                                   zipf_s=1.1),
+    "qwen_prefill_16x160": Workload("qwen_prefill_16x160", 9, vocab=248320, batch=1,
+                                    seq_len=262144, history_len=0, orders=(2, 3), heads=8,
+                                    row_start=20000003, row_dim=160, hidden=2560, n_branches=1,
+                                    dtype="bf16", zipf_s=1.1, copy_prob=0.2, param_index=8),
 }
 
 

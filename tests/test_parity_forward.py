@@ -314,3 +314,34 @@ def test_forward_empty_batch():
     H.ngram_forward(cfg, ids, inp["lut"], inp["tables"], inp["hidden"], 0, inp["wk"], inp["wv"],
                     inp["conv_w"], out, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
+
+
+def test_forward_qwen_decode_16x160_full(orc):
+    """The page's own table geometry at full scale: 16 tables of ~20M rows x
+    160 bf16 (320-byte rows across 128-byte lines), 256 decode tokens."""
+    w = W.get("qwen_decode_16x160")
+    print("[forward] qwen_decode_16x160", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, layout="d_mem")
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
+    wk, wv, cw, gam = _host_params(w, inp)
+    ref = orc.forward(ids, hist, W.make_lut(w), w.vocab, w.vocab_compressed, w.orders, w.heads,
+                      w.rows(), W.hash_multipliers(w), G.oracle_rows(w),
+                      W.hidden_values(w, np.arange(ids.size)), wk, wv, cw, w.dtype,
+                      eps=w.rms_eps)
+    G.check(G.to_f64(out).reshape(ref["delta"].shape), ref["delta"], "decode 16x160 out")
+    G.check(gates.cpu().numpy().reshape(ref["gate"].shape), ref["gate"], "decode 16x160 gates")
+
+
+def test_forward_qwen_prefill_16x160(orc):
+    w = W.get("qwen_prefill_16x160")
+    print("[forward] qwen_prefill_16x160 262144 tokens", flush=True)
+    ids, hist = W.make_ids(w)
+    inp = _device_inputs(w, ids, hist, layout="d_mem")
+    out, gates, err = _run(w, inp)
+    assert err == 0
+    _check_ids(orc, w, ids, hist, inp)
+    T = w.seq_len
+    _check_windows(orc, w, ids, hist, inp, out, gates, [(0, 0, 24), (0, 77777, 24), (0, T - 24, 24)])
