@@ -407,6 +407,12 @@ def prequeue(seconds: float):
     torch.cuda._sleep(int(seconds * 2.5e9))
 
 
+def prequeue_seconds(steps: int) -> float:
+    """Spin long enough for the host to enqueue ``steps`` calls (a call takes
+    well under 40 us of host time)."""
+    return min(0.25, 40e-6 * steps + 0.005)
+
+
 def time_region(fn, steps: int, stream, pre: float = 0.0) -> float:
     """Milliseconds per call of fn(i) over ``steps`` calls between two events
     (synchronised on both sides)."""
@@ -528,7 +534,8 @@ def decode_extras(setup: Setup, steps: int):
     res = {}
     for i in range(20):
         setup.step_ring(i % setup.pool)
-    ms_ring = time_region(lambda i: setup.step_ring(i % setup.pool), steps, stream)
+    ms_ring = time_region(lambda i: setup.step_ring(i % setup.pool), steps, stream,
+                          pre=prequeue_seconds(steps))
     _, tot_ring = algorithmic(w, ring=True)
     res["decode_with_state"] = {
         "ms_per_step": ms_ring, "tokens_per_s": w.n_tokens / (ms_ring * 1e-3),
@@ -595,8 +602,12 @@ def main():
 
     # ---- timed region: exactly `steps` steps, no instrumentation
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # the GPU is held by a spin kernel while the host enqueues the region (as
+    # a model's earlier layers would hold it), so the K steps run back to back
+    # and the region times the kernels, not the host's first submissions
+    pre_s = prequeue_seconds(args.steps)
     t0 = time.perf_counter()
-    ms_per_step = time_region(lambda i: setup.step(i % setup.pool), args.steps, stream)
+    ms_per_step = time_region(lambda i: setup.step(i % setup.pool), args.steps, stream, pre=pre_s)
     wall = time.perf_counter() - t0
     tokens_per_s = w.n_tokens / (ms_per_step * 1e-3)
 
@@ -655,6 +666,7 @@ def main():
         "stage_ms": stage_avg,
         "stage_algorithmic_bytes": {k: v["bytes"] for k, v in stages_alg.items()},
         "wall_s_timed": wall,
+        "prequeue_s": pre_s,
         "roofline": roof,
     }
     if route(w) == "decode" and not args.no_extras:

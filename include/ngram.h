@@ -20,11 +20,13 @@
  * Conventions for every entry point
  *  - Device pointers are borrowed for the stream-ordered duration of the call;
  *    the caller owns every buffer.  The library allocates no device memory:
- *    scratch comes from the caller's workspace.
+ *    scratch comes from the caller's workspace (ngram_forward_noalloc alone
+ *    takes it from a static device array instead; see there).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream), never synchronises, keeps no state between calls and is
- *    reentrant.  The library reads no environment variables: tuning overrides
- *    are fields of ngram_config.
+ *    reentrant (ngram_forward_noalloc's shared array is the one exception).
+ *    The library reads no environment variables: tuning overrides are fields
+ *    of ngram_config.
  *  - All arrays are dense row-major.  Device pointers must be 16-byte aligned.
  *  - Arguments are validated on the host before any launch; a failed check
  *    returns a negative ngram_status and launches nothing.  A failed launch
