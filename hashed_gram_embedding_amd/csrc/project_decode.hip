@@ -46,7 +46,14 @@ __global__ __launch_bounds__(64 * kWstatWaves, 1) void proj_wstat_kernel(WstatAr
   __shared__ __attribute__((aligned(16))) bf16_bits s_w[kWstatLdsBytes / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_tile = blockIdx.x % a.tiles_n, ks = blockIdx.x / a.tiles_n;
+  // Workgroup b runs on XCD b % 8: give each XCD a contiguous range of
+  // (k-slice, n-tile) blocks, so that its workgroups share one or two E
+  // slices instead of all of them.  An XCD's L2 then holds its weight blocks
+  // (3.3 MB at Qwen scale, kept from the previous step) beside a 0.3 MB E
+  // slice, where all four slices (1.3 MB) pushed part of the weights out.
+  int bid = (int)blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+  const int n_tile = bid % a.tiles_n, ks = bid / a.tiles_n;
   const int nkd = a.nb * a.d;        // key columns
   const int N = nkd + a.d;           // key columns of every branch, then value columns
   const int n0 = n_tile * NT;
