@@ -39,6 +39,32 @@ def test_gate_each_plan(orc, plan, n):
     G.check(G.to_f64(u), orc.gated_value(g_ref, v), "U")
 
 
+@pytest.mark.parametrize("plan", [8, 11])
+def test_gate_ragged_hidden(orc, plan):
+    """A hidden size that is not a multiple of the column tile (2,080 =
+    8 x 256 + 32 = 16 x 128 + 32): the last column tile's waves hold columns
+    past d, which are computed from clamped weight rows and never stored."""
+    H = G.H()
+    w = W.get("qwen_multibranch_zipf13").replace(hidden=2080)
+    n = 777
+    print(f"[plan {plan}] gate d=2080 n={n}", flush=True)
+    cfg = G.config(w, "d_mem", proj_plan=plan)
+    e = rng.normal_values(91, np.arange(n * w.mem_dim), 0.02, "bf16").reshape(n, w.mem_dim)
+    hid = rng.normal_values(92, np.arange(n * 4 * w.hidden), 1.0, "bf16").reshape(n, 4, w.hidden)
+    wk, wv = G.weights(w, "d_mem")
+    gates = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    u = torch.empty((n, 4, w.hidden), dtype=torch.bfloat16, device="cuda")
+    H.ngram_gate(cfg, G.to_device(hid, w), w.hidden, G.to_device(e, w), wk, wv, gates, u)
+    torch.cuda.synchronize()
+    e64 = W.to_f64(e, "bf16")
+    wk_h, wv_h = G.host_weights(wk, wv, "d_mem")
+    k = np.stack([orc.project(e64, wk_h[b], "bf16") for b in range(4)], axis=1)
+    v = orc.project(e64, wv_h, "bf16")
+    g_ref = orc.gate(hid, "bf16", k, eps=w.rms_eps)
+    G.check(gates.cpu().numpy(), g_ref, "gates")
+    G.check(G.to_f64(u), orc.gated_value(g_ref, v), "U")
+
+
 @pytest.mark.parametrize("plan", PLANS)
 def test_forward_each_plan(orc, plan):
     """Every tile plan in the forward pass (hash, gather to E, projection,
