@@ -64,6 +64,10 @@ def parse():
                     help="timed steps of each other workload (long prefill, multi-branch)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--profile-region", action="store_true",
+                    help="for a profiler's kernel trace: a few warmup steps, then only the "
+                         "timed region, held behind a spin long enough for a profiled host to "
+                         "enqueue it, so the trace averages back-to-back kernels as the line does")
     return ap.parse_args()
 
 
@@ -584,6 +588,9 @@ def main():
     if args.pass_ == "backward":
         main_backward(args)
         return
+    if args.profile_region:
+        profile_region(args)
+        return
     args.workload = args.workload or "qwen_decode"
     args.steps = 2000 if args.steps is None else args.steps
     args.warmup = 100 if args.warmup is None else args.warmup
@@ -689,6 +696,26 @@ def main():
             for n in ("qwen_prefill", "qwen_multibranch_uniform", "qwen_multibranch_zipf13",
                       "qwen_decode_16x160", "qwen_prefill_16x160")]
     print(json.dumps(result), flush=True)
+
+
+def profile_region(args):
+    """The timed region alone (see --profile-region): under a kernel trace the
+    host enqueues each call several times more slowly, so the spin that holds
+    the GPU is sized at 400 us a step instead of 40, and nothing else runs
+    (the stage-event and per-step regions, the extras)."""
+    import torch
+    w_name = args.workload or "qwen_decode"
+    steps = 300 if args.steps is None else args.steps
+    warmup = 3 if args.warmup is None else args.warmup
+    setup = Setup(w_name, args.pool)
+    for i in range(warmup):
+        setup.step(i % setup.pool)
+    torch.cuda.synchronize()
+    pre = min(2.0, 400e-6 * steps + 0.02)
+    ms = time_region(lambda i: setup.step(i % setup.pool), steps, torch.cuda.current_stream(),
+                     pre=pre)
+    print(json.dumps({"profile_region": w_name, "steps": steps, "warmup": warmup,
+                      "ms_per_step": ms, "prequeue_s": pre}), flush=True)
 
 
 # ---------------------------------------------------------------------------
