@@ -7,10 +7,11 @@ when it has not been built.
 """
 from . import ngram  # noqa: F401
 from .ngram import (ADD_RESIDUAL, BF16, F32, FP8_E4M3, MEM_ROWS, MEM_TILES16,  # noqa: F401
-                    UPDATE_STATE, W_D_MEM, W_MEM_D, NgramConfig, NgramError, make_config,
+                    PREFETCHED, UPDATE_STATE, W_D_MEM, W_MEM_D, NgramConfig, NgramError,
+                    make_config,
                     ngram_backward, ngram_backward_timed, ngram_backward_workspace_size,
                     ngram_causal_conv, ngram_compress_ids, ngram_config_validate, ngram_forward,
-                    ngram_forward_noalloc, ngram_forward_timed,
+                    ngram_forward_noalloc, ngram_forward_prefetch, ngram_forward_timed,
                     ngram_forward_workspace_size,
                     ngram_forward_workspace_view, ngram_gate, ngram_gate_workspace_size,
                     ngram_gather, ngram_hash)

@@ -26,7 +26,7 @@ static __device__ __align__(256) unsigned char scratch[NGRAM_NOALLOC_SCRATCH_BYT
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 
 int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : dtype == NGRAM_FP8_E4M3 ? 1 : 4; }
@@ -461,6 +461,28 @@ void* device_scratch() {
   return p;
 }
 
+// Steps 1-4 of the forward into the workspace of layout L: row ids and E
+// (the decode route's one hash + gather kernel, else hash then gather).
+int launch_lookup(const ngram_config* cfg, const Layout& L, const int32_t* raw_ids, int32_t B,
+                  int32_t T, const int32_t* history, const int32_t* lut, const TablePtrs& tp,
+                  int32_t* err_flag, char* ws, hipStream_t s, Timer& tm) {
+  const int64_t n_tok = (int64_t)B * T;
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
+  void* e = ws + L.e;
+  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+  if (L.k_split > 0) {
+    tm.stage(1);
+    return hip_status(launch_hash_gather(cfg->table_dtype, raw_ids, B, T, history, lut, ha,
+                                         cfg->n_tables, cfg->row_dim, tp, e, row_idx, err_flag, s));
+  }
+  tm.stage(0);
+  int st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
+  if (st) return st;
+  tm.stage(1);
+  return hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables,
+                                  cfg->row_dim, tp, e, s));
+}
+
 // Shared by ngram_forward, ngram_forward_timed and ngram_forward_noalloc
 // (static_scratch: the current device's static scratch replaces the
 // workspace, taken once every argument has passed its checks).
@@ -474,7 +496,8 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
   int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
-  if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_UPDATE_STATE)) return NGRAM_EINVAL;
+  if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_UPDATE_STATE | NGRAM_PREFETCHED)) return NGRAM_EINVAL;
+  if ((flags & NGRAM_PREFETCHED) && static_scratch) return NGRAM_EINVAL;
   if ((flags & NGRAM_UPDATE_STATE) && (conv_state == nullptr || state_pos == nullptr))
     return NGRAM_EINVAL;
   int64_t h_tok = 0;
@@ -504,9 +527,7 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
   if (!aligned16(workspace)) return NGRAM_EALIGN;
 
   char* ws = static_cast<char*>(workspace);
-  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + L.row_idx);
   void* e = ws + L.e;
-  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
   ConvArgs ca = conv_args_base(cfg);
   ca.conv_w = conv_w;
   ca.gamma_u = gamma_u;
@@ -526,10 +547,10 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
     // decode: hash + gather -> E, weight-stationary projection, decode finalize
     // (which reads the ring's taps and writes this position's row)
     float* split = reinterpret_cast<float*>(ws + L.split);
-    tm.stage(1);
-    st = hip_status(launch_hash_gather(cfg->table_dtype, raw_ids, B, T, history, lut, ha,
-                                       cfg->n_tables, cfg->row_dim, tp, e, row_idx, err_flag, s));
-    if (st) return st;
+    if (!(flags & NGRAM_PREFETCHED)) {
+      st = launch_lookup(cfg, L, raw_ids, B, T, history, lut, tp, err_flag, ws, s, tm);
+      if (st) return st;
+    }
     tm.stage(2);
     WstatArgs wa{};
     wa.e = static_cast<const bf16_bits*>(e);
@@ -549,13 +570,10 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
   }
   const ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
                                 gamma_k, ws, L, n_tok);
-  tm.stage(0);
-  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, err_flag, s));
-  if (st) return st;
-  tm.stage(1);
-  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n_tok, cfg->n_tables, cfg->row_dim,
-                                tp, e, s));
-  if (st) return st;
+  if (!(flags & NGRAM_PREFETCHED)) {
+    st = launch_lookup(cfg, L, raw_ids, B, T, history, lut, tp, err_flag, ws, s, tm);
+    if (st) return st;
+  }
   tm.stage(2);
   st = hip_status(run_projection(cfg, L, pa, s));
   if (st) return st;
@@ -873,6 +891,29 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                       w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u, conv_state, state_pos, flags,
                       out, gates, err_flag, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream), tm);
+}
+
+int ngram_forward_prefetch(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                           const int32_t* history, const int32_t* lut, const void* const* tables,
+                           int32_t* err_flag, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = validate(cfg, false);
+  if (st) return st;
+  if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
+  const int64_t n_tok = (int64_t)B * T;
+  if (n_tok == 0) return NGRAM_OK;
+  if (!raw_ids || !lut) return NGRAM_EINVAL;
+  TablePtrs tp;
+  st = check_tables(cfg, tables, &tp);
+  if (st) return st;
+  if (!aligned4(raw_ids) || !aligned4(history) || !aligned4(lut) || !aligned4(err_flag))
+    return NGRAM_EALIGN;
+  const Layout L = layout_for(cfg, n_tok, true, T);
+  if (!workspace || workspace_bytes < L.total) return NGRAM_EWORKSPACE;
+  if (!aligned16(workspace)) return NGRAM_EALIGN;
+  Timer tm;
+  return launch_lookup(cfg, L, raw_ids, B, T, history, lut, tp, err_flag,
+                       static_cast<char*>(workspace), static_cast<hipStream_t>(stream), tm);
 }
 
 int ngram_forward_noalloc(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,

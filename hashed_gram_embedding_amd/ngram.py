@@ -17,6 +17,7 @@ MAX_ORDER = 4
 MAX_BRANCHES = 4
 ADD_RESIDUAL = 1
 UPDATE_STATE = 2
+PREFETCHED = 4    # the workspace holds the call's row ids and E (ngram_forward_prefetch)
 MEM_ROWS, MEM_TILES16 = 0, 1  # layouts of E in the forward workspace
 F32, BF16, FP8_E4M3 = 0, 1, 2  # FP8_E4M3: table storage only
 W_MEM_D, W_D_MEM = 0, 1  # projection storage: [mem, d] or [d, mem] (fast path)
@@ -142,6 +143,9 @@ _BWD_ARGS = [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p
 _SIGS["ngram_forward"] = (ctypes.c_int, _FWD_ARGS)
 _SIGS["ngram_forward_timed"] = (ctypes.c_int, _FWD_ARGS + [_p, _p])
 _SIGS["ngram_forward_noalloc"] = (ctypes.c_int, _FWD_ARGS[:-3] + [_p])
+# cfg, raw_ids, B, T, history, lut, tables, err_flag, workspace, bytes, stream
+_SIGS["ngram_forward_prefetch"] = (ctypes.c_int, [_cfgp, _p, _i32, _i32, _p, _p, _p, _p, _p,
+                                                  ctypes.c_size_t, _p])
 NOALLOC_SCRATCH_BYTES = 64 << 20  # NGRAM_NOALLOC_SCRATCH_BYTES
 _SIGS["ngram_backward"] = (ctypes.c_int, _BWD_ARGS)
 _SIGS["ngram_backward_timed"] = (ctypes.c_int, _BWD_ARGS + [_p, _p])
@@ -313,6 +317,18 @@ def ngram_forward(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, 
                                               state_pos, flags, gates, err_flag, workspace,
                                               stream)), "ngram_forward")
     return out
+
+
+def ngram_forward_prefetch(cfg, raw_ids, lut, tables, workspace, history=None, err_flag=None,
+                           stream=None):
+    """Steps 1-4 of ngram_forward into ``workspace`` (row ids and E), for a
+    later ngram_forward(..., flags=PREFETCHED, workspace=workspace)."""
+    B, T = raw_ids.shape
+    _check(lib().ngram_forward_prefetch(ctypes.byref(cfg), _ptr(raw_ids), B, T, _ptr(history),
+                                        _ptr(lut), _table_array(tables), _ptr(err_flag),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ngram_forward_prefetch")
+    return workspace
 
 
 def ngram_forward_noalloc(cfg, raw_ids, lut, tables, hidden, hidden_branch_stride, w_k, w_v,

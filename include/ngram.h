@@ -56,6 +56,8 @@ extern "C" {
 /* flags for ngram_forward / ngram_causal_conv */
 #define NGRAM_ADD_RESIDUAL 1 /* out = hidden (the branch's query row) + Delta (forward only) */
 #define NGRAM_UPDATE_STATE 2 /* write this call's normalised rows into the conv-state ring */
+#define NGRAM_PREFETCHED 4   /* the workspace already holds the call's row ids and E
+                                (ngram_forward_prefetch); forward only */
 
 typedef enum ngram_status {
   NGRAM_OK = 0,
@@ -143,7 +145,8 @@ typedef struct ngram_config {
 /* Human-readable name of a status code (static string). */
 const char* ngram_status_str(int status);
 
-/* Library ABI version: increments whenever a signature or layout changes. */
+/* Library ABI version: increments whenever a signature, a layout or the set
+   of entry points changes. */
 int ngram_abi_version(void);
 
 /*
@@ -281,7 +284,10 @@ int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t
  *   conv_w, gamma_u, conv_state, state_pos: as ngram_causal_conv (with the
  *             ring, one call per new token gives the Delta_t that one call over
  *             the whole sequence gives)
- *   flags     0 or NGRAM_ADD_RESIDUAL and / or NGRAM_UPDATE_STATE
+ *   flags     0 or NGRAM_ADD_RESIDUAL and / or NGRAM_UPDATE_STATE and / or
+ *             NGRAM_PREFETCHED (the hash and gather already ran, see
+ *             ngram_forward_prefetch: raw_ids, history, lut and tables are
+ *             then checked but not read)
  *   out       device [B, T, n_branches, d] act_dtype (output): Delta_t, or
  *             hidden + Delta_t with NGRAM_ADD_RESIDUAL
  *   gates     device float[B, T, n_branches] (output), nullable
@@ -298,6 +304,27 @@ int ngram_forward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   const void* gamma_k, const void* gamma_u, float* conv_state,
                   int32_t* state_pos, int32_t flags, void* out, float* gates,
                   int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The lookup half of ngram_forward, ahead of the rest ("Qwen3.8-Flash-Next
+ * 深度研究" §2.3: the n-gram hash ids are known as soon as the tokens enter the
+ * network, so the lookup can be issued early; "Qwen3.8 加了 51B 查表参数，模型
+ * 开始像数据库了", section "510 亿参数不走算力主干": the lookup positions can be
+ * computed in advance and the fetch overlapped with the model's other work).  Steps 1-4: compresses the
+ * raw ids, hashes the n-grams and gathers E into the workspace, where
+ * ngram_forward_workspace_view locates them; a later ngram_forward with the
+ * same cfg, B, T and workspace and NGRAM_PREFETCHED runs steps 5-8 on them.
+ * A caller that knows the ids before the layer's input is ready -- at the
+ * start of the model's forward pass, the layer sitting after others -- can
+ * run this on a second stream and order the forward after it with an event.
+ * Arguments as ngram_forward; the workspace must stay untouched between the
+ * two calls.  Returns what ngram_forward would for these arguments (and
+ * NGRAM_EWORKSPACE for a workspace too small for the whole forward).
+ */
+int ngram_forward_prefetch(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,
+                           const int32_t* history, const int32_t* lut, const void* const* tables,
+                           int32_t* err_flag, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * Where ngram_forward leaves the row ids and the memory vector of its tokens
@@ -384,7 +411,8 @@ int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, i
  * Every call on one GPU shares that GPU's array and finds the previous call's
  * contents there (no kernel needs it cleared): calls that may overlap on one
  * GPU -- on different streams, or from different threads -- race and must be
- * serialised by the caller.  ngram_forward_workspace_view does not apply.
+ * serialised by the caller.  ngram_forward_workspace_view and
+ * NGRAM_PREFETCHED (NGRAM_EINVAL) do not apply.
  */
 #define NGRAM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int ngram_forward_noalloc(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,

@@ -165,6 +165,15 @@ int main() {
   EXPECT(ngram_forward_noalloc(&t, (int32_t*)fake, 1, 8192, nullptr, (int32_t*)fake, tabs, fake, 0,
                                fake, fake, fake, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                                fake, nullptr, nullptr, nullptr), NGRAM_ESCRATCH);
+  EXPECT(ngram_forward_noalloc(&t, (int32_t*)fake, 256, 1, nullptr, (int32_t*)fake, tabs, fake, 0,
+                               fake, fake, fake, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               NGRAM_PREFETCHED, fake, nullptr, nullptr, nullptr), NGRAM_EINVAL);
+  EXPECT(ngram_forward_prefetch(&t, (int32_t*)fake, 256, 1, nullptr, (int32_t*)fake, tabs, nullptr,
+                                fake, need - 1, nullptr), NGRAM_EWORKSPACE);
+  EXPECT(ngram_forward_prefetch(&t, (int32_t*)fake, 256, 1, nullptr, nullptr, tabs, nullptr, fake,
+                                need, nullptr), NGRAM_EINVAL);
+  EXPECT(ngram_forward_prefetch(&t, (int32_t*)fake, 256, 1, nullptr, (int32_t*)fake, tabs, nullptr,
+                                odd, need, nullptr), NGRAM_EALIGN);
   float* gt[16];
   for (int j = 0; j < 16; ++j) gt[j] = (float*)fake;
   EXPECT(ngram_backward(&t, (int32_t*)fake, 4, 64, nullptr, (int32_t*)fake, tabs, fake, 0, fake,
@@ -180,7 +189,7 @@ int main() {
                         (float*)fake, (float*)fake, (float*)fake, nullptr, nullptr, fake,
                         (size_t)1 << 40, nullptr), NGRAM_ESHAPE);
   for (int s = -9; s <= 1; ++s) (void)ngram_status_str(s);
-  EXPECT(ngram_abi_version(), 4);
+  EXPECT(ngram_abi_version(), 5);
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

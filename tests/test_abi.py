@@ -59,7 +59,7 @@ def test_config_layout_matches_c(H):
 
 
 def test_status_strings_and_version(H):
-    assert H.ngram.abi_version() == 4
+    assert H.ngram.abi_version() == 5
     for code in range(-8, 1):
         assert H.ngram.status_str(code).startswith("NGRAM_")
 
@@ -202,7 +202,7 @@ def test_entry_points_reject_before_launch(H):
     args = [ref, fake, 1, 256, None, fake, tabs, fake, 0, fake, fake, fake, None, None, None,
             None, None, 0, fake, None, None, fake, need, None]
     bad = list(args)
-    bad[17] = 4                                            # unknown flag
+    bad[17] = 8                                            # unknown flag
     assert L.ngram_forward(*bad) == -1
     bad = list(args)
     bad[17] = 2                                            # ring update without a ring
@@ -231,7 +231,7 @@ def test_entry_points_reject_before_launch(H):
     events = (ctypes.c_void_p * 8)(*([0x10000] * 8))
     mask = ctypes.c_int32(-1)
     bad = list(args)
-    bad[17] = 4
+    bad[17] = 8
     assert L.ngram_forward_timed(*bad, events, ctypes.byref(mask)) == -1
     assert L.ngram_forward_timed(*args, None, ctypes.byref(mask)) == -1   # no events
     bad = list(args)
@@ -241,11 +241,40 @@ def test_entry_points_reject_before_launch(H):
     na = args[:21] + [None]
     assert L.ngram_forward_noalloc(*na) != 0                 # no GPU here: the lookup fails
     bad = list(na)
-    bad[17] = 4
+    bad[17] = 8
+    assert L.ngram_forward_noalloc(*bad) == -1
+    bad = list(na)
+    bad[17] = 4                                            # a prefetch needs a workspace
     assert L.ngram_forward_noalloc(*bad) == -1
     bad = list(na)
     bad[2], bad[3] = 0, 256
     assert L.ngram_forward_noalloc(*bad) == 0
+    # the lookup ahead of the forward: the forward's checks of its arguments
+    pf = [ref, fake, 1, 256, None, fake, tabs, None, fake, need, None]
+    bad = list(pf)
+    bad[1] = None
+    assert L.ngram_forward_prefetch(*bad) == -1
+    bad = list(pf)
+    bad[2] = -1
+    assert L.ngram_forward_prefetch(*bad) == -2
+    bad = list(pf)
+    bad[6] = None
+    assert L.ngram_forward_prefetch(*bad) == -1
+    bad = list(pf)
+    bad[8] = None
+    assert L.ngram_forward_prefetch(*bad) == -7
+    bad = list(pf)
+    bad[9] = need - 256                                    # too small for the whole forward
+    assert L.ngram_forward_prefetch(*bad) == -7
+    bad = list(pf)
+    bad[8] = odd
+    assert L.ngram_forward_prefetch(*bad) == -4
+    bad = list(pf)
+    bad[4] = ctypes.c_void_p(0x10002)                      # history misaligned
+    assert L.ngram_forward_prefetch(*bad) == -4
+    bad = list(pf)
+    bad[2], bad[3] = 0, 256
+    assert L.ngram_forward_prefetch(*bad) == 0             # empty: no launch
     q = _cfg(H, "qwen_prefill")
     big = [ctypes.byref(q)] + na[1:]
     big[2], big[3] = 1, 8192                                 # ~16 KB per token > 64 MiB
