@@ -528,10 +528,11 @@ def other_workload(name: str, steps: int, warmup: int, attainable: float):
 
 
 def decode_extras(setup: Setup, steps: int):
-    """The headline decode step three more ways: with a conv-state ring (the
+    """The headline decode step more ways: with a conv-state ring (the
     realistic long-running decode: three taps read, one row written, residual
     added), replayed from a HIP graph of one pool of steps (no host work per
-    step), and the host time one ngram_forward call takes to submit."""
+    step), the host time one ngram_forward call takes to submit, and the
+    layer's kernels alone when its lookup was issued ahead."""
     import torch
     w = setup.w
     stream = torch.cuda.current_stream()
@@ -572,6 +573,24 @@ def decode_extras(setup: Setup, steps: int):
                            "tokens_per_s": w.n_tokens / (ms_graph * 1e-3),
                            "steps": reps * setup.pool}
     del g
+    # the layer's own kernels when its lookup was issued ahead (by
+    # ngram_forward_prefetch, behind a model's earlier layers): the projection
+    # and the gate + conv on the rows already in the workspace
+    setup.H.ngram_forward_prefetch(setup.cfg, setup.ids[0], setup.lut, setup.tables, setup.ws,
+                                   history=setup.hist[0])
+
+    def layer(i):
+        s = setup
+        s.H.ngram_forward(s.cfg, s.ids[0], s.lut, s.tables, s.hidden[0], s.hbs, s.wk, s.wv,
+                          s.conv, s.out, history=s.hist[0], flags=s.H.PREFETCHED,
+                          workspace=s.ws)
+
+    for i in range(20):
+        layer(i)
+    ms_ahead = time_region(layer, steps, stream, pre=prequeue_seconds(steps))
+    res["layer_with_lookup_ahead"] = {
+        "ms_per_step": ms_ahead, "tokens_per_s": w.n_tokens / (ms_ahead * 1e-3),
+        "flags": "NGRAM_PREFETCHED (projection and gate + conv only)"}
     return res
 
 
