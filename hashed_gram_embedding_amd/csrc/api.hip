@@ -1,9 +1,9 @@
 // extern "C" entry points of libngram.so: argument validation on the host,
 // workspace layout, and the launch sequence of each operation.  Every step
 // of the layer runs in the kernels of ids.hip, gather.hip, project.hip,
-// project_async.hip, project_decode.hip, finalize.hip and backward.hip (each
-// cites the passages it implements); this file launches them on the
-// caller's stream.
+// project_async.hip, project_decode.hip, finalize.hip, backward.hip and
+// table_grad.hip (each cites the passages it implements); this file launches
+// them on the caller's stream.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -26,7 +26,7 @@ static __device__ __align__(256) unsigned char scratch[NGRAM_NOALLOC_SCRATCH_BYT
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 
 int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : dtype == NGRAM_FP8_E4M3 ? 1 : 4; }
@@ -259,7 +259,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 // (bf16), the weights transposed, dE (fp32), and dK / dV and E transposed
 // over tokens padded to a multiple of 64.
 struct BwdLayout {
-  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, dw, total;
+  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, dw, tgrad, total;
   int64_t n_pad;
   int32_t dw_split;  // K splits of the dW product
 };
@@ -307,6 +307,10 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
   L.rtmp = take((size_t)32 * 4 * d * 4);
   L.dw_split = dw_split_for(N, mem, L.n_pad);
   L.dw = take((size_t)L.dw_split * N * mem * 4);
+  // the table gradient's sort and carries run last, when K / V are no longer
+  // read: they reuse that region when it is large enough
+  const size_t tg = table_grad_bytes(n, c->n_tables, c->row_dim);
+  L.tgrad = tg <= (size_t)n * N * 4 ? L.kv : take(tg);
   L.total = off;
   return L;
 }
@@ -719,8 +723,9 @@ int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   if (st) return st;
   st = hip_status(launch_sum_splits(dw + kw, L.dw_split, N64 * mem, (int64_t)d * mem, d_w_v, s));
   if (st) return st;
-  // the gather's adjoint
-  return hip_status(launch_scatter_add(row_idx, n, cfg->n_tables, cfg->row_dim, de, gp, s));
+  // the gather's adjoint, each row's contributions added in token order
+  return hip_status(launch_table_grad(row_idx, n, cfg->n_tables, cfg->row_dim, cfg->rows, de, gp,
+                                      ws + L.tgrad, s));
 }
 
 }  // namespace

@@ -4,9 +4,9 @@
 // Each kernel is the chain rule of one forward step ("Qwen3.8-Flash-Next
 // 深度研究" §2.3: E_t -> K_t, V_t; g_t = Gate(Norm(Q_t), Norm(K_t));
 // U_t = g_t V_t; Delta_t = U_t + SiLU(DWConv(RMSNorm(U_t))); Engram's third
-// and fourth components in "Qwen 4用上DeepSeek的Engram").  The table gradient
-// is the gather's adjoint: a scatter-add of dE into the rows the tokens
-// named.  The dense products (K/V recompute, dE = dKV W, dW = dKV^T E) run on
+// and fourth components in "Qwen 4用上DeepSeek的Engram").  The table gradient,
+// the gather's adjoint (a scatter-add of dE into the rows the tokens named),
+// is in table_grad.hip.  The dense products (K/V recompute, dE = dKV W, dW = dKV^T E) run on
 // the MFMA projection kernel with a raw fp32 epilogue; the kernels here do the
 // per-row work between them and the layout transposes that feed them.
 //
@@ -395,29 +395,6 @@ __global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__
       ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
-// 4. The gather's adjoint: one wavefront per token adds the token's dE slices
-// into the fp32 gradient rows of the tables it named (hardware fp32 atomics,
-// 64 consecutive floats per instruction; rows named by several tokens
-// receive every contribution, in no fixed order).
-__global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t* __restrict__ row_idx,
-                                                          int64_t n_tok, int32_t n_tables,
-                                                          int32_t row_dim,
-                                                          const float* __restrict__ d_e,
-                                                          GradTablePtrs g) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t tok = wave0; tok < n_tok; tok += wstride) {
-    const float* src = d_e + tok * (int64_t)n_tables * row_dim;
-    const int32_t* ri = row_idx + tok * n_tables;
-    for (int j = 0; j < n_tables; ++j) {
-      float* dst = g.p[j] + (int64_t)ri[j] * row_dim;
-      const float* sj = src + (int64_t)j * row_dim;
-      for (int c = lane; c < row_dim; c += 64) unsafeAtomicAdd(dst + c, sj[c]);
-    }
-  }
-}
-
 // out[i] = sum_s part[s * stride + i] over the split-K partial products,
 // four floats per thread, the splits added in order.
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part,
@@ -535,14 +512,6 @@ hipError_t launch_bwd_rows(const BwdArgs& a, float* d_conv_w, float* d_gammas,
   e = col_sum(a.part_conv, g2, 4 * (int64_t)a.d, d_conv_w);
   if (e != hipSuccess || d_gammas == nullptr) return e;
   return col_sum(a.part_gain, g3, 3 * (int64_t)a.d, d_gammas);
-}
-
-hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
-                              int32_t row_dim, const float* d_e, const GradTablePtrs& g,
-                              hipStream_t s) {
-  if (n_tok == 0) return hipSuccess;
-  return launch(scatter_add_kernel, grid_of((n_tok + 3) / 4, 65536), 256, 0, s, row_idx, n_tok,
-                n_tables, row_dim, d_e, g);
 }
 
 hipError_t launch_sum_splits(const float* part, int32_t split, int64_t stride, int64_t n,

@@ -289,9 +289,14 @@ constexpr int kBwdBlocks = 1024;    // grid cap of the per-row backward kernels
 // through reduce_tmp [32, 4 d] (d <= 4096)
 hipError_t launch_bwd_rows(const BwdArgs& a, float* d_conv_w, float* d_gammas,
                            float* reduce_tmp, hipStream_t s);
-hipError_t launch_scatter_add(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
-                              int32_t row_dim, const float* d_e, const GradTablePtrs& g,
-                              hipStream_t s);
+// The gather's adjoint: dE slices added into the fp32 gradient rows of the
+// tables the tokens named, every row's contributions in ascending token order
+// (bit-identical run to run), through table_grad_bytes() of scratch;
+// table_rows: the host's row count of each table.
+size_t table_grad_bytes(int64_t n_tok, int32_t n_tables, int32_t row_dim);
+hipError_t launch_table_grad(const int32_t* row_idx, int64_t n_tok, int32_t n_tables,
+                             int32_t row_dim, const int64_t* table_rows, const float* d_e,
+                             const GradTablePtrs& g, void* scratch, hipStream_t s);
 // out[i] = sum_{s < split} part[s * stride + i], i < n (fp32, in split order)
 hipError_t launch_sum_splits(const float* part, int32_t split, int64_t stride, int64_t n,
                              float* out, hipStream_t s);

@@ -370,9 +370,9 @@ int ngram_forward_workspace_view(const ngram_config* cfg, int32_t B, int32_t T,
  *              rejected)
  *   d_out      device [B, T, n_branches, d] bf16: dL/d(out)
  *   d_tables   HOST array of n_tables device pointers, table j an fp32
- *              [rows[j], row_dim] gradient, ACCUMULATED (+=); rows named by
- *              several tokens receive every contribution through fp32
- *              atomics, so their last bits may differ from run to run
+ *              [rows[j], row_dim] gradient, ACCUMULATED (+=); a row named by
+ *              several tokens adds their contributions in ascending token
+ *              order, so every gradient is bit-identical from run to run
  *   d_w_k      device fp32 [n_branches, d, mem_dim] (written), d_w_v fp32 [d, mem_dim]
  *   d_conv_w   device fp32 [conv_kernel, d] (written)
  *   d_hidden   device fp32, hidden's layout (written), nullable

@@ -189,7 +189,7 @@ int main() {
                         (float*)fake, (float*)fake, (float*)fake, nullptr, nullptr, fake,
                         (size_t)1 << 40, nullptr), NGRAM_ESHAPE);
   for (int s = -9; s <= 1; ++s) (void)ngram_status_str(s);
-  EXPECT(ngram_abi_version(), 5);
+  EXPECT(ngram_abi_version(), 6);
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

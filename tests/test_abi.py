@@ -59,7 +59,7 @@ def test_config_layout_matches_c(H):
 
 
 def test_status_strings_and_version(H):
-    assert H.ngram.abi_version() == 5
+    assert H.ngram.abi_version() == 6
     for code in range(-8, 1):
         assert H.ngram.status_str(code).startswith("NGRAM_")
 

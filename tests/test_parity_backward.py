@@ -164,10 +164,11 @@ def test_backward_rejects_unsupported():
 
 
 def test_backward_deterministic_gradients_run_to_run():
-    """Two identical backward calls: the W_K, W_V, conv-tap, query and gain
-    gradients are bit-identical (fixed-order sums, no atomics); only the table
-    gradients, accumulated with fp32 atomics where tokens share a row, may
-    differ in their last bits, and only within rounding."""
+    """Two identical backward calls give bit-identical gradients: W_K, W_V,
+    the conv taps, the query rows and the gains (fixed-order sums, no float
+    atomics), and the tables, whose rows named by several tokens add their
+    contributions in ascending token order.  The id stream repeats rows often
+    (Zipf ids over small tables), so many rows take several terms."""
     H = G.H()
     w = W.get("engram_small").replace(batch=3, seq_len=300, hidden=512, heads=2,
                                       row_start=10007, n_branches=2)
@@ -201,5 +202,10 @@ def test_backward_deterministic_gradients_run_to_run():
     a, b = runs
     for k in ("wk", "wv", "cw", "h", "gm"):
         assert torch.equal(a[k], b[k]), k
+    shared = 0
     for ta, tb in zip(a["tabs"], b["tabs"]):
-        assert G.rel_err(tb.double().cpu().numpy(), ta.double().cpu().numpy()) < 1e-6
+        assert torch.equal(ta, tb)
+    for ta in a["tabs"]:
+        shared += int((ta != 0).any(dim=1).sum().item())
+    # fewer touched rows than (token, table) pairs: rows were shared
+    assert shared < n * w.n_tables
