@@ -153,9 +153,12 @@ __global__ __launch_bounds__(256) void digit_move_kernel(const int32_t* __restri
 }
 
 // Step 2: range w = (table j, range c) of the sorted pairs, one wavefront.
-// Lane l holds the key and token of position p0 + l; the rows' columns are
-// spread over the lanes, kColsPerPass at a time, and eight positions' slices
-// are loaded before they are added (in position order).
+// Lane l holds the key and token of position p0 + l.  A row's columns are
+// spread over the lanes four at a time (16-byte accesses), kColsPerPass per
+// pass; the positions are taken eight at a time, their dE slices -- and the
+// table rows of the runs that end among them -- loaded before any is added,
+// so that a run's read-modify-write costs no round trip of its own.  The
+// slices are added in position order.
 __global__ __launch_bounds__(64) void run_sum_kernel(const int32_t* __restrict__ keys,
                                                      const int32_t* __restrict__ toks, int64_t n,
                                                      int32_t nt, int32_t row_dim, int64_t n_range,
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(64) void run_sum_kernel(const int32_t* __restrict__
                                                      GradTablePtrs g, RowCounts rows,
                                                      float* __restrict__ carry,
                                                      int32_t* __restrict__ flags) {
+  constexpr int UQ = kColsPerPass / 256;  // 16-byte column groups per lane and pass
   const int lane = threadIdx.x;
   const int64_t w = blockIdx.x;
   const int j = (int)(w / n_range);
@@ -173,14 +177,22 @@ __global__ __launch_bounds__(64) void run_sum_kernel(const int32_t* __restrict__
   const int32_t* __restrict__ tj = toks + (int64_t)j * n;
   // (every position holds a token index below n and a row of table j; the
   // clamps only keep the accesses inside their arrays whatever they hold)
-  const int32_t my_key = lane < cnt ? kj[p0 + lane] : -1;
+  const int32_t n_rows = rows.r[j];
+  int32_t my_key = lane < cnt ? kj[p0 + lane] : -1;
+  my_key = my_key >= n_rows ? -1 : my_key;
   int32_t my_tok = lane < cnt ? tj[p0 + lane] : 0;
   my_tok = my_tok < 0 ? 0 : (my_tok >= n ? (int32_t)(n - 1) : my_tok);
-  const int32_t n_rows = rows.r[j];
   const int32_t prev = p0 > 0 ? kj[p0 - 1] : -1;          // rows are >= 0
   const int32_t next = p0 + cnt < n ? kj[p0 + cnt] : -1;
   const bool cont_in = prev == __builtin_amdgcn_readlane(my_key, 0);
   const bool cont_out = next == __builtin_amdgcn_readlane(my_key, cnt - 1);
+  // bit i: a run ends at position i; rmw: ... and its sum goes into the row
+  // (all but a run begun in an earlier range, whose piece is carried)
+  const int32_t key_after = __shfl_down(my_key, 1);
+  const uint64_t ends =
+      __ballot(lane < cnt && (lane + 1 < cnt ? key_after != my_key : !cont_out));
+  uint64_t rmw = ends;
+  if (cont_in && ends) rmw &= rmw - 1;  // the first end closes the carried-in run
   const float* __restrict__ dej = d_e + (int64_t)j * row_dim;
   const int64_t dstride = (int64_t)nt * row_dim;
   float* __restrict__ head = carry + (w * 2) * row_dim;
@@ -188,62 +200,75 @@ __global__ __launch_bounds__(64) void run_sum_kernel(const int32_t* __restrict__
   float* __restrict__ tab = g.p[j];
   int32_t flag = 0;
   for (int cb = 0; cb < row_dim; cb += kColsPerPass) {
-    // this lane's columns of the pass, clamped into the row (their loads are
-    // unconditional; columns past the row are never stored)
-    int col[8];
-    bool ok[8];
+    // this lane's column groups of the pass (row_dim is a multiple of 4);
+    // groups past the row load column 0 and are never stored
+    int col[UQ];
+    bool ok[UQ];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int cc = cb + lane + 64 * u;
+    for (int u = 0; u < UQ; ++u) {
+      const int cc = cb + 4 * lane + 256 * u;
       ok[u] = cc < row_dim;
-      col[u] = ok[u] ? cc : row_dim - 1;
+      col[u] = ok[u] ? cc : 0;
     }
-    float acc[8];
+    float4 acc[UQ];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
-    bool at_start = true;  // the open piece began at p0
+    for (int u = 0; u < UQ; ++u) acc[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     auto emit = [&](float* dst) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (ok[u]) dst[col[u]] = acc[u];
+      for (int u = 0; u < UQ; ++u)
+        if (ok[u]) *reinterpret_cast<float4*>(dst + col[u]) = acc[u];
     };
     for (int i0 = 0; i0 < cnt; i0 += 8) {
-      float v[8][8];
+      float4 v[8][UQ], r[8][UQ];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int i = i0 + q < cnt ? i0 + q : cnt - 1;
         const int32_t t = __builtin_amdgcn_readlane(my_tok, i);
         const float* __restrict__ src = dej + (int64_t)t * dstride;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[q][u] = src[col[u]];
+        for (int u = 0; u < UQ; ++u) v[q][u] = *reinterpret_cast<const float4*>(src + col[u]);
+        const int32_t kp = __builtin_amdgcn_readlane(my_key, i);
+        if (i0 + q < cnt && ((rmw >> (i0 + q)) & 1) && kp >= 0) {
+          const float* row = tab + (int64_t)kp * row_dim;
+#pragma unroll
+          for (int u = 0; u < UQ; ++u) r[q][u] = *reinterpret_cast<const float4*>(row + col[u]);
+        }
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int i = i0 + q;
         if (i < cnt) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc[u] += v[q][u];
-          const int32_t kp = __builtin_amdgcn_readlane(my_key, i);
-          const bool ends = i + 1 < cnt ? __builtin_amdgcn_readlane(my_key, i + 1) != kp : !cont_out;
-          if (ends) {
-            if (at_start && cont_in) {
+          for (int u = 0; u < UQ; ++u) {
+            acc[u].x += v[q][u].x;
+            acc[u].y += v[q][u].y;
+            acc[u].z += v[q][u].z;
+            acc[u].w += v[q][u].w;
+          }
+          if ((ends >> i) & 1) {
+            if ((rmw >> i) & 1) {
+              const int32_t kp = __builtin_amdgcn_readlane(my_key, i);
+              if (kp >= 0) {
+                float* row = tab + (int64_t)kp * row_dim;
+#pragma unroll
+                for (int u = 0; u < UQ; ++u)
+                  if (ok[u])
+                    *reinterpret_cast<float4*>(row + col[u]) =
+                        make_float4(r[q][u].x + acc[u].x, r[q][u].y + acc[u].y,
+                                    r[q][u].z + acc[u].z, r[q][u].w + acc[u].w);
+              }
+            } else {
               emit(head);  // the end of a run begun in an earlier range
               flag |= kHead;
-            } else if (kp >= 0 && kp < n_rows) {
-              float* __restrict__ row = tab + (int64_t)kp * row_dim;
-#pragma unroll
-              for (int u = 0; u < 8; ++u)
-                if (ok[u]) row[col[u]] += acc[u];
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
-            at_start = false;
+            for (int u = 0; u < UQ; ++u) acc[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
           }
         }
       }
     }
     if (cont_out) {  // the open piece continues into the next range
-      if (at_start && cont_in) {
+      if (cont_in && !ends) {
         emit(head);
         flag |= kHead | kMiddle;
       } else {
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(64) void run_sum_kernel(const int32_t* __restrict__
 
 // Step 3: a run that starts in range w and continues: its piece there, then
 // the following ranges' head pieces in order, until a range where the run
-// ends.
+// ends.  The flags of eight ranges are read at a time, then their pieces.
 __global__ __launch_bounds__(64) void run_join_kernel(const int32_t* __restrict__ keys, int64_t n,
                                                       int32_t row_dim, int64_t n_range,
                                                       GradTablePtrs g, RowCounts rows,
@@ -272,14 +297,47 @@ __global__ __launch_bounds__(64) void run_join_kernel(const int32_t* __restrict_
   const int32_t key = keys[(int64_t)j * n + last];
   if (key < 0 || key >= rows.r[j]) return;
   float* __restrict__ row = g.p[j] + (int64_t)key * row_dim;
-  for (int cc = lane; cc < row_dim; cc += 64) {
-    float acc = carry[(w * 2 + 1) * row_dim + cc];
-    for (int64_t c2 = c + 1; c2 < n_range; ++c2) {
-      const int64_t w2 = (int64_t)j * n_range + c2;
-      acc += carry[(w2 * 2) * row_dim + cc];
-      if (!(flags[w2] & kMiddle)) break;
+  const float* __restrict__ cj = carry + (int64_t)j * n_range * 2 * row_dim;
+  for (int cb = 0; cb < row_dim; cb += 256) {
+    const int col = cb + 4 * lane;
+    const bool ok = col < row_dim;
+    const int cl = ok ? col : 0;
+    float4 acc = *reinterpret_cast<const float4*>(carry + (w * 2 + 1) * row_dim + cl);
+    bool done = false;
+    for (int64_t c2 = c + 1; !done && c2 < n_range;) {
+      int32_t f[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = c2 + q < n_range ? flags[(int64_t)j * n_range + c2 + q] : 0;
+      int take = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (!done && c2 + q < n_range) {
+          take = q + 1;
+          done = !(f[q] & kMiddle);
+        }
+      }
+      float4 h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < take) h[q] = *reinterpret_cast<const float4*>(cj + ((c2 + q) * 2) * row_dim + cl);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < take) {
+          acc.x += h[q].x;
+          acc.y += h[q].y;
+          acc.z += h[q].z;
+          acc.w += h[q].w;
+        }
+      c2 += take;
     }
-    row[cc] += acc;
+    if (ok) {
+      float4 x = *reinterpret_cast<const float4*>(row + col);
+      x.x += acc.x;
+      x.y += acc.y;
+      x.z += acc.z;
+      x.w += acc.w;
+      *reinterpret_cast<float4*>(row + col) = x;
+    }
   }
 }
 
