@@ -838,14 +838,25 @@ def main_backward(args):
                       dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def bwd():
+    # the training step: the forward keeps its row ids, E, K and V in the
+    # backward's workspace, and the backward uses them (no recompute)
+    def fwd():
+        H.ngram_forward(setup.cfg, setup.ids[0], setup.lut, setup.tables, setup.hidden[0],
+                        setup.hbs, setup.wk, setup.wv, setup.conv, setup.out,
+                        history=setup.hist[0], flags=H.KEEP_FOR_BACKWARD, workspace=bws)
+
+    def bwd(flags=H.KEEP_FOR_BACKWARD):
         H.ngram_backward(setup.cfg, setup.ids[0], setup.lut, setup.tables, setup.hidden[0],
                          setup.hbs, setup.wk, setup.wv, setup.conv, d_out, d_tabs, d_wk, d_wv,
-                         d_cw, d_hidden=d_h, workspace=bws)
+                         d_cw, d_hidden=d_h, flags=flags, workspace=bws)
 
     def train_step():
-        setup.step(0)
+        fwd()
         bwd()
+
+    def train_step_recompute():  # a plain forward, and a backward that recomputes
+        setup.step(0)
+        bwd(0)
 
     def timed(fn, k):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -868,8 +879,12 @@ def main_backward(args):
     t0 = time.perf_counter()
     ms_step = timed(train_step, steps)
     wall = time.perf_counter() - t0
-    ms_fwd = timed(lambda: setup.step(0), max(10, steps // 4))
+    ms_fwd = timed(fwd, max(10, steps // 4))
     ms_bwd = timed(bwd, max(10, steps // 4))
+    for _ in range(3):
+        train_step_recompute()
+    ms_re = timed(train_step_recompute, max(10, steps // 4))
+    fwd()  # the kept intermediates for the stage timing below
 
     print("[bench] backward stage timing", file=sys.stderr, flush=True)
     k = min(args.stage_steps, 50)
@@ -880,7 +895,8 @@ def main_backward(args):
     for i in range(k):
         mask = H.ngram_backward_timed(evs[i], setup.cfg, setup.ids[0], setup.lut, setup.tables,
                                       setup.hidden[0], setup.hbs, setup.wk, setup.wv, setup.conv,
-                                      d_out, d_tabs, d_wk, d_wv, d_cw, d_hidden=d_h, workspace=bws)
+                                      d_out, d_tabs, d_wk, d_wv, d_cw, d_hidden=d_h,
+                                      flags=H.KEEP_FOR_BACKWARD, workspace=bws)
     torch.cuda.synchronize()
     stage_avg = {BWD_STAGES[s]: (float(np.mean([e[2 * s].elapsed_time(e[2 * s + 1])
                                                 for e in evs])) if mask >> s & 1 else 0.0)
@@ -899,7 +915,8 @@ def main_backward(args):
                 algorithmic_bytes=a["bytes"], algorithmic_flops=a["flops"],
                 avg_ms=stage_avg[dom])
     fwd_flops = 2.0 * n * w.mem_dim * d * (nb + 1)
-    bwd_flops = sum(v["flops"] for v in alg.values())
+    # the backward on the forward's kept intermediates runs no recompute
+    bwd_flops = sum(v["flops"] for k, v in alg.items() if k != "recompute")
     result = {
         "metric": "N-gram-embedding training-step tokens/sec (forward + backward), 1 MI355X",
         "value": n / (ms_step * 1e-3),
@@ -916,6 +933,9 @@ def main_backward(args):
         "tflops_step": (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12,
         "tflops_backward": bwd_flops / (ms_bwd * 1e-3) / 1e12,
         "stage_ms": stage_avg, "wall_s_timed": wall, "roofline": roof,
+        "flags": "forward NGRAM_KEEP_FOR_BACKWARD, backward NGRAM_KEEP_FOR_BACKWARD",
+        "with_recompute": {"ms_per_step": ms_re, "tokens_per_s": n / (ms_re * 1e-3),
+                           "flags": "none: a plain forward, the backward recomputes"},
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)

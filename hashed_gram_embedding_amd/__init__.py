@@ -6,8 +6,8 @@ ctypes binding.  Importing this package loads the library and fails loudly
 when it has not been built.
 """
 from . import ngram  # noqa: F401
-from .ngram import (ADD_RESIDUAL, BF16, F32, FP8_E4M3, MEM_ROWS, MEM_TILES16,  # noqa: F401
-                    PREFETCHED, UPDATE_STATE, W_D_MEM, W_MEM_D, NgramConfig, NgramError,
+from .ngram import (ADD_RESIDUAL, BF16, F32, FP8_E4M3, KEEP_FOR_BACKWARD, MEM_ROWS,  # noqa: F401
+                    MEM_TILES16, PREFETCHED, UPDATE_STATE, W_D_MEM, W_MEM_D, NgramConfig, NgramError,
                     make_config,
                     ngram_backward, ngram_backward_timed, ngram_backward_workspace_size,
                     ngram_causal_conv, ngram_compress_ids, ngram_config_validate, ngram_forward,

@@ -26,7 +26,7 @@ static __device__ __align__(256) unsigned char scratch[NGRAM_NOALLOC_SCRATCH_BYT
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 
 int esize_of(int dtype) { return dtype == NGRAM_BF16 ? 2 : dtype == NGRAM_FP8_E4M3 ? 1 : 4; }
@@ -259,7 +259,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 // (bf16), the weights transposed, dE (fp32), and dK / dV and E transposed
 // over tokens padded to a multiple of 64.
 struct BwdLayout {
-  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, dw, tgrad, total;
+  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, dw, tgrad, fparts, total;
   int64_t n_pad;
   int32_t dw_split;  // K splits of the dW product
 };
@@ -307,12 +307,34 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
   L.rtmp = take((size_t)32 * 4 * d * 4);
   L.dw_split = dw_split_for(N, mem, L.n_pad);
   L.dw = take((size_t)L.dw_split * N * mem * 4);
-  // the table gradient's sort and carries run last, when K / V are no longer
-  // read: they reuse that region when it is large enough
+  // the table gradient's sort and carries run last, after the dW product has
+  // read the transposed operands: they reuse that region when it is large
+  // enough (row ids, E and K / V stay intact, so a forward's kept
+  // intermediates serve any number of backward calls)
   const size_t tg = table_grad_bytes(n, c->n_tables, c->row_dim);
-  L.tgrad = tg <= (size_t)n * N * 4 ? L.kv : take(tg);
+  L.tgrad = tg <= (size_t)N * L.n_pad * 2 ? L.dkvt : take(tg);
+  // a forward that keeps its intermediates for this pass puts its gate
+  // partials where dE goes later
+  const size_t fp = (size_t)n * (3 * nb + 1) * layout_for(c, n, true, 0).plan.np * 4;
+  L.fparts = fp <= (size_t)n * mem * 4 ? L.de : take(fp);
   L.total = off;
   return L;
+}
+
+// The backward's products index their operands with 32-bit offsets: the dW
+// operands [., n_pad], and the dE product's weights transposed to
+// [mem, (nb+1) d] (whose split sums also take (nb+1) d mem as a 32-bit
+// stride).  Also the supported set of the backward pass.
+int backward_shape_ok(const ngram_config* cfg, int64_t n) {
+  if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM || !async_path(cfg))
+    return NGRAM_EDTYPE;
+  if (cfg->hidden_dim % 64 != 0 || cfg->hidden_dim > 4096) return NGRAM_ESHAPE;
+  const int64_t n_pad = (n + 63) / 64 * 64;
+  const int64_t N64 = (int64_t)(cfg->n_branches + 1) * cfg->hidden_dim;
+  if (N64 * n_pad >= (int64_t(1) << 31) || (int64_t)cfg->mem_dim * n_pad >= (int64_t(1) << 31) ||
+      N64 * cfg->mem_dim >= (int64_t(1) << 31))
+    return NGRAM_ESHAPE;
+  return NGRAM_OK;
 }
 
 // C[M, (nb+1)*dd] = A[M, K] B^T in fp32 (B: nb key blocks of dd rows from wk,
@@ -403,6 +425,8 @@ ProjArgs proj_args(const ngram_config* c, const void* e, const void* w_k, const 
   a.nb = c->n_branches;
   a.np = L.plan.np;
   a.w_dk = c->w_layout == NGRAM_W_D_MEM;
+  a.v_ld = c->hidden_dim;
+  a.k_keep = nullptr;
   return a;
 }
 
@@ -423,6 +447,8 @@ AsyncProjArgs async_args(const ProjArgs& p) {
   a.epi.d = p.d;
   a.epi.nb = p.nb;
   a.epi.np = p.np;
+  a.epi.v_ld = p.v_ld;
+  a.epi.k_keep = p.k_keep;
   a.K = p.K;
   a.group_m = 4;
   return a;
@@ -500,8 +526,15 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
   int st = validate(cfg, false);
   if (st) return st;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
-  if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_UPDATE_STATE | NGRAM_PREFETCHED)) return NGRAM_EINVAL;
+  if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_UPDATE_STATE | NGRAM_PREFETCHED | NGRAM_KEEP_FOR_BACKWARD))
+    return NGRAM_EINVAL;
   if ((flags & NGRAM_PREFETCHED) && static_scratch) return NGRAM_EINVAL;
+  const bool keep = flags & NGRAM_KEEP_FOR_BACKWARD;
+  if (keep && (static_scratch || (flags & NGRAM_PREFETCHED))) return NGRAM_EINVAL;
+  if (keep) {
+    st = backward_shape_ok(cfg, (int64_t)B * T);
+    if (st) return st;
+  }
   if ((flags & NGRAM_UPDATE_STATE) && (conv_state == nullptr || state_pos == nullptr))
     return NGRAM_EINVAL;
   int64_t h_tok = 0;
@@ -519,7 +552,21 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
   for (const void* p : {hidden, w_k, w_v, conv_w, gamma_q, gamma_k, gamma_u,
                         (const void*)conv_state, (const void*)out, (const void*)gates})
     if (!aligned16(p)) return NGRAM_EALIGN;
-  const Layout L = layout_for(cfg, n_tok, true, T);
+  // keeping: the prefill route, its row ids, E, K and V where the backward
+  // pass reads them (K / V fp32 [n, (nb+1) d]), its partials in a region the
+  // backward fills only later
+  Layout L = layout_for(cfg, n_tok, true, keep ? 0 : T);
+  BwdLayout BL{};
+  if (keep) {
+    BL = bwd_layout(cfg, n_tok);
+    L.row_idx = BL.row_idx;
+    L.e = BL.e;
+    L.v = BL.kv;
+    L.v_stride = (int64_t)(cfg->n_branches + 1) * cfg->hidden_dim;
+    L.v_offset = (int64_t)cfg->n_branches * cfg->hidden_dim;
+    L.parts = BL.fparts;
+    L.total = BL.total;
+  }
   if (static_scratch) {  // ngram_forward_noalloc, after every other check
     if (L.total > NGRAM_NOALLOC_SCRATCH_BYTES) return NGRAM_ESCRATCH;
     workspace = device_scratch();
@@ -572,8 +619,13 @@ int forward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int
     ca.gamma_k = gamma_k;
     return hip_status(launch_decode_finalize(cfg->act_dtype, L.k_split, split, ca, s));
   }
-  const ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
-                                gamma_k, ws, L, n_tok);
+  ProjArgs pa = proj_args(cfg, e, w_k, w_v, hidden, h_tok, hidden_branch_stride, gamma_q,
+                          gamma_k, ws, L, n_tok);
+  if (keep) {
+    pa.k_keep = reinterpret_cast<float*>(ws + L.v);
+    pa.v = pa.k_keep + L.v_offset;
+    pa.v_ld = L.v_stride;
+  }
   if (!(flags & NGRAM_PREFETCHED)) {
     st = launch_lookup(cfg, L, raw_ids, B, T, history, lut, tp, err_flag, ws, s, tm);
     if (st) return st;
@@ -605,10 +657,11 @@ int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
                   void* workspace, size_t workspace_bytes, hipStream_t s, Timer& tm) {
   int st = validate(cfg, false);
   if (st) return st;
-  if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM) return NGRAM_EDTYPE;
-  if (cfg->hidden_dim % 64 != 0 || cfg->hidden_dim > 4096) return NGRAM_ESHAPE;
   if (B < 0 || T < 0 || (int64_t)B * T > kMaxTokens) return NGRAM_ESHAPE;
-  if (flags & ~NGRAM_ADD_RESIDUAL) return NGRAM_EINVAL;
+  st = backward_shape_ok(cfg, (int64_t)B * T);
+  if (st) return st;
+  if (flags & ~(NGRAM_ADD_RESIDUAL | NGRAM_KEEP_FOR_BACKWARD)) return NGRAM_EINVAL;
+  const bool kept = flags & NGRAM_KEEP_FOR_BACKWARD;
   int64_t h_tok = 0;
   st = check_hidden_stride(cfg, hidden_branch_stride, &h_tok);
   if (st) return st;
@@ -636,12 +689,6 @@ int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   const BwdLayout L = bwd_layout(cfg, n);
   const int nb = cfg->n_branches, d = cfg->hidden_dim, mem = cfg->mem_dim;
   const int64_t N64 = (int64_t)(nb + 1) * d;
-  // the products index their operands with 32-bit offsets: the dW operands
-  // [., n_pad], and the dE product's weights transposed to [mem, (nb+1) d]
-  // (whose split sums also take (nb+1) d mem as a 32-bit stride)
-  if (N64 * L.n_pad >= (int64_t(1) << 31) || (int64_t)mem * L.n_pad >= (int64_t(1) << 31) ||
-      N64 * mem >= (int64_t(1) << 31))
-    return NGRAM_ESHAPE;
   if (!workspace || workspace_bytes < L.total) return NGRAM_EWORKSPACE;
   if (!aligned16(workspace)) return NGRAM_EALIGN;
 
@@ -658,15 +705,18 @@ int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   const bf16_bits* wk = static_cast<const bf16_bits*>(w_k);
   const bf16_bits* wv = static_cast<const bf16_bits*>(w_v);
 
-  // recompute: row ids, E, and K / V in fp32
-  tm.stage(0);
-  const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
-  st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, nullptr, s));
-  if (st) return st;
-  st = hip_status(launch_gather(cfg->table_dtype, row_idx, n, cfg->n_tables, cfg->row_dim, tp, e, s));
-  if (st) return st;
-  st = hip_status(raw_gemm(e, n, mem, wk, wv, nb, d, kv, N, s));
-  if (st) return st;
+  // recompute: row ids, E, and K / V in fp32 (unless a forward kept them here)
+  if (!kept) {
+    tm.stage(0);
+    const HashArgs ha = hash_args(cfg, cfg->orders[cfg->n_orders - 1] - 1);
+    st = hip_status(launch_hash(true, raw_ids, B, T, history, lut, ha, row_idx, nullptr, s));
+    if (st) return st;
+    st = hip_status(
+        launch_gather(cfg->table_dtype, row_idx, n, cfg->n_tables, cfg->row_dim, tp, e, s));
+    if (st) return st;
+    st = hip_status(raw_gemm(e, n, mem, wk, wv, nb, d, kv, N, s));
+    if (st) return st;
+  }
   // the per-row backward: gates, conv, RMSNorms -> dK, dV (bf16), d_hidden, d_conv_w, d_gammas
   tm.stage(1);
   BwdArgs ba;

@@ -63,6 +63,8 @@ __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], con
   const int64_t M = a.M;
   const int nq = 3 * a.nb + 1;
   if (seg < a.nb) {
+    // K itself is kept only for a later backward pass (fp32, streamed)
+    float* __restrict__ K = a.k_keep ? a.k_keep + (int64_t)seg * d : nullptr;
     float g[NI];
     bool cv[NI];
 #pragma unroll
@@ -87,6 +89,7 @@ __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], con
           if (cv[ni] && row < M) {
             const float h = hread(row, col);
             const float k = acc[mi][ni][r];
+            if (K) __builtin_nontemporal_store(k, &K[row * a.v_ld + col]);
             xd[r] += g[ni] * h * k;
             xk[r] += k * k;
             xh[r] += h * h;
@@ -120,7 +123,7 @@ __device__ __forceinline__ void gate_epilogue(const floatx16 (&acc)[MI][NI], con
             const int64_t row = wrow0 + mi * 32 + acc_row(r, lane);
             if (row < M) {
               const float v = acc[mi][ni][r];
-              __builtin_nontemporal_store(v, &V[row * d + col]);  // read once, by the conv
+              __builtin_nontemporal_store(v, &V[row * a.v_ld + col]);  // read once, by the conv
               xv[r] += v * v;
             }
           }

@@ -137,6 +137,8 @@ struct ProjArgs {
   int64_t M;
   int32_t K, d, nb, np;
   int32_t w_dk;           // fp32 path: W stored [d, K] instead of [K, d]
+  int64_t v_ld;           // bf16 path: fp32 elements between V rows (d, or (nb+1) d when kept)
+  float* k_keep;          // bf16 path, nullable: K of branch s written at k_keep + s d, rows v_ld apart
 };
 
 // Epilogue of the projections: gate row partials for key segments, fp32 V
@@ -146,10 +148,12 @@ struct EpiArgs {
   int64_t h_tok_stride, h_branch_stride;
   const bf16_bits* gamma_q;  // nullable
   const bf16_bits* gamma_k;  // nullable
-  float* v;                  // [M, d]
+  float* v;                  // [M, v_ld]: row m's values at v + m v_ld
   float* parts;              // [M, 3*nb+1, np]
   int64_t M;
   int32_t d, nb, np;
+  int64_t v_ld;
+  float* k_keep;             // nullable: key segment s also stored at k_keep + m v_ld + s d
 };
 
 // Projection with operands copied global -> LDS (W stored [d, mem]); the A

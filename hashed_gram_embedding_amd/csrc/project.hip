@@ -196,6 +196,8 @@ __global__ __launch_bounds__(256, 1) void proj_bf16_kernel(ProjArgs a, int tiles
   ea.d = d;
   ea.nb = a.nb;
   ea.np = a.np;
+  ea.v_ld = d;
+  ea.k_keep = nullptr;
   gate_epilogue<TL::MI, TL::NI>(acc, ea, seg, m0 + wm * TL::WM, wcol0, wcol0 / TL::WN, lane);
 }
 

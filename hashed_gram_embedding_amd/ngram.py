@@ -17,7 +17,8 @@ MAX_ORDER = 4
 MAX_BRANCHES = 4
 ADD_RESIDUAL = 1
 UPDATE_STATE = 2
-PREFETCHED = 4    # the workspace holds the call's row ids and E (ngram_forward_prefetch)
+PREFETCHED = 4
+KEEP_FOR_BACKWARD = 8    # the workspace holds the call's row ids and E (ngram_forward_prefetch)
 MEM_ROWS, MEM_TILES16 = 0, 1  # layouts of E in the forward workspace
 F32, BF16, FP8_E4M3 = 0, 1, 2  # FP8_E4M3: table storage only
 W_MEM_D, W_D_MEM = 0, 1  # projection storage: [mem, d] or [d, mem] (fast path)

@@ -58,6 +58,9 @@ extern "C" {
 #define NGRAM_UPDATE_STATE 2 /* write this call's normalised rows into the conv-state ring */
 #define NGRAM_PREFETCHED 4   /* the workspace already holds the call's row ids and E
                                 (ngram_forward_prefetch); forward only */
+#define NGRAM_KEEP_FOR_BACKWARD 8 /* ngram_forward: leave row ids, E, K and V in the
+                                     workspace for ngram_backward; ngram_backward: use
+                                     them instead of recomputing (see ngram_backward) */
 
 typedef enum ngram_status {
   NGRAM_OK = 0,
@@ -287,7 +290,8 @@ int ngram_causal_conv(const ngram_config* cfg, const void* u, int32_t B, int32_t
  *   flags     0 or NGRAM_ADD_RESIDUAL and / or NGRAM_UPDATE_STATE and / or
  *             NGRAM_PREFETCHED (the hash and gather already ran, see
  *             ngram_forward_prefetch: raw_ids, history, lut and tables are
- *             then checked but not read)
+ *             then checked but not read) or NGRAM_KEEP_FOR_BACKWARD (training:
+ *             see ngram_backward; not with NGRAM_PREFETCHED)
  *   out       device [B, T, n_branches, d] act_dtype (output): Delta_t, or
  *             hidden + Delta_t with NGRAM_ADD_RESIDUAL
  *   gates     device float[B, T, n_branches] (output), nullable
@@ -382,6 +386,18 @@ int ngram_forward_workspace_view(const ngram_config* cfg, int32_t B, int32_t T,
  * dK and dV enter the dE and dW products as bf16 (fp32 accumulation); the
  * other gradients are fp32 throughout.  Returns NGRAM_EDTYPE / NGRAM_ESHAPE
  * for configurations outside the supported set, otherwise as ngram_forward.
+ *
+ * Training without the recompute: an ngram_forward call with
+ * NGRAM_KEEP_FOR_BACKWARD and a workspace of ngram_backward_workspace_size()
+ * bytes leaves its row ids, E and fp32 K and V there (the prefill route is
+ * taken whatever B and T are; same supported set as this call, else
+ * NGRAM_EDTYPE / NGRAM_ESHAPE).  An ngram_backward with
+ * NGRAM_KEEP_FOR_BACKWARD, the same cfg, B, T and workspace, then skips its
+ * first stage and uses them; raw_ids, history, lut and tables are checked
+ * but not read.  The backward leaves them intact, so several backward calls
+ * may follow one forward.  The caller must not use the workspace for
+ * anything else in between; ngram_forward_workspace_view does not describe
+ * this layout.
  */
 size_t ngram_backward_workspace_size(const ngram_config* cfg, int32_t B, int32_t T);
 int ngram_backward(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, int32_t T,

@@ -174,6 +174,16 @@ int main() {
                                 need, nullptr), NGRAM_EINVAL);
   EXPECT(ngram_forward_prefetch(&t, (int32_t*)fake, 256, 1, nullptr, (int32_t*)fake, tabs, nullptr,
                                 odd, need, nullptr), NGRAM_EALIGN);
+  // keeping the intermediates for a backward: a backward workspace, no prefetch
+  EXPECT(ngram_forward(&t, (int32_t*)fake, 256, 1, nullptr, (int32_t*)fake, tabs, fake, 0, fake,
+                       fake, fake, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       NGRAM_KEEP_FOR_BACKWARD, fake, nullptr, nullptr, fake, need, nullptr),
+         NGRAM_EWORKSPACE);
+  EXPECT(ngram_forward(&t, (int32_t*)fake, 256, 1, nullptr, (int32_t*)fake, tabs, fake, 0, fake,
+                       fake, fake, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       NGRAM_KEEP_FOR_BACKWARD | NGRAM_PREFETCHED, fake, nullptr, nullptr, fake,
+                       (size_t)1 << 40, nullptr),
+         NGRAM_EINVAL);
   float* gt[16];
   for (int j = 0; j < 16; ++j) gt[j] = (float*)fake;
   EXPECT(ngram_backward(&t, (int32_t*)fake, 4, 64, nullptr, (int32_t*)fake, tabs, fake, 0, fake,
@@ -188,8 +198,13 @@ int main() {
                         fake, fake, nullptr, nullptr, nullptr, nullptr, nullptr, 0, fake, gt,
                         (float*)fake, (float*)fake, (float*)fake, nullptr, nullptr, fake,
                         (size_t)1 << 40, nullptr), NGRAM_ESHAPE);
+  EXPECT(ngram_forward(&big, (int32_t*)fake, 1, 64, nullptr, (int32_t*)fake, tabs, fake, 0, fake,
+                       fake, fake, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       NGRAM_KEEP_FOR_BACKWARD, fake, nullptr, nullptr, fake, (size_t)1 << 40,
+                       nullptr),
+         NGRAM_ESHAPE);
   for (int s = -9; s <= 1; ++s) (void)ngram_status_str(s);
-  EXPECT(ngram_abi_version(), 6);
+  EXPECT(ngram_abi_version(), 7);
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -59,7 +59,7 @@ def test_config_layout_matches_c(H):
 
 
 def test_status_strings_and_version(H):
-    assert H.ngram.abi_version() == 6
+    assert H.ngram.abi_version() == 7
     for code in range(-8, 1):
         assert H.ngram.status_str(code).startswith("NGRAM_")
 
@@ -202,8 +202,21 @@ def test_entry_points_reject_before_launch(H):
     args = [ref, fake, 1, 256, None, fake, tabs, fake, 0, fake, fake, fake, None, None, None,
             None, None, 0, fake, None, None, fake, need, None]
     bad = list(args)
-    bad[17] = 8                                            # unknown flag
+    bad[17] = 16                                           # unknown flag
     assert L.ngram_forward(*bad) == -1
+    bad = list(args)
+    bad[17] = 8                                            # keep for backward: bf16 only
+    assert L.ngram_forward(*bad) == -3
+    bad = list(args)
+    bad[17] = 8 | 4                                        # ... and never with a prefetch
+    assert L.ngram_forward(*bad) == -1
+    ecfg = _cfg(H, "engram_small", w_layout=1)             # W stored [d, mem]
+    keep = [ctypes.byref(ecfg)] + args[1:]
+    keep[6] = (ctypes.c_void_p * 16)(*([0x10000] * 16))
+    keep[17] = 8
+    keep[22] = L.ngram_backward_workspace_size(ctypes.byref(ecfg), 1, 256) - 256
+    assert keep[22] > L.ngram_forward_workspace_size(ctypes.byref(ecfg), 1, 256)
+    assert L.ngram_forward(*keep) == -7                    # it needs a backward workspace
     bad = list(args)
     bad[17] = 2                                            # ring update without a ring
     assert L.ngram_forward(*bad) == -1
@@ -231,7 +244,7 @@ def test_entry_points_reject_before_launch(H):
     events = (ctypes.c_void_p * 8)(*([0x10000] * 8))
     mask = ctypes.c_int32(-1)
     bad = list(args)
-    bad[17] = 8
+    bad[17] = 16
     assert L.ngram_forward_timed(*bad, events, ctypes.byref(mask)) == -1
     assert L.ngram_forward_timed(*args, None, ctypes.byref(mask)) == -1   # no events
     bad = list(args)
@@ -241,10 +254,13 @@ def test_entry_points_reject_before_launch(H):
     na = args[:21] + [None]
     assert L.ngram_forward_noalloc(*na) != 0                 # no GPU here: the lookup fails
     bad = list(na)
-    bad[17] = 8
+    bad[17] = 16
     assert L.ngram_forward_noalloc(*bad) == -1
     bad = list(na)
     bad[17] = 4                                            # a prefetch needs a workspace
+    assert L.ngram_forward_noalloc(*bad) == -1
+    bad = list(na)
+    bad[17] = 8                                            # so does keeping for a backward
     assert L.ngram_forward_noalloc(*bad) == -1
     bad = list(na)
     bad[2], bad[3] = 0, 256
