@@ -155,6 +155,28 @@ def test_kept_forward_on_a_decode_shaped_call():
         _close(got[k], ref[k], k)
 
 
+def test_kept_forward_advances_the_ring_alike():
+    """With NGRAM_UPDATE_STATE as well, the kept forward writes the same ring
+    rows and positions as the plain one."""
+    H = G.H()
+    w = W.get("engram_small").replace(batch=2, seq_len=100, hidden=256, heads=2, row_start=10007)
+    print("[keep] ring update, 2 x 100", flush=True)
+    L = _Layer(w, 7, True)
+    ring0, pos0 = L.state.clone(), L.pos.clone()
+    ws_plain = torch.empty(H.ngram_forward_workspace_size(L.cfg, L.B, L.T), dtype=torch.uint8,
+                           device="cuda")
+    ws_keep = torch.empty(H.ngram_backward_workspace_size(L.cfg, L.B, L.T), dtype=torch.uint8,
+                          device="cuda")
+    out0, gates0 = L.forward(H.UPDATE_STATE, ws_plain)
+    ring1, pos1 = L.state.clone(), L.pos.clone()
+    L.state.copy_(ring0)
+    L.pos.copy_(pos0)
+    out1, gates1 = L.forward(H.UPDATE_STATE | H.KEEP_FOR_BACKWARD, ws_keep)
+    assert torch.equal(_bits(out0), _bits(out1)) and torch.equal(gates0, gates1)
+    assert torch.equal(L.state, ring1) and torch.equal(L.pos, pos1)
+    assert not torch.equal(ring1, ring0)
+
+
 def test_kept_refusals():
     H = G.H()
     w = W.get("engram_small").replace(batch=1, seq_len=64, hidden=256, heads=2, row_start=10007)

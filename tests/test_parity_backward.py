@@ -141,6 +141,14 @@ def test_backward_single_token_sequences_and_ragged(orc):
     _case(orc, w, 1, False, True, False, seed=10)
 
 
+def test_backward_wide_rows(orc):
+    """576-wide table rows (E of 2,304): the table gradient's wavefronts take
+    each row in two column passes, the second ragged (64 of 512 columns)."""
+    w = SMALL.replace(row_dim=576, batch=2, seq_len=200)
+    print("[backward] 576-wide rows, 2 x 200 tokens", flush=True)
+    _case(orc, w, 1, True, True, True, seed=51)
+
+
 @pytest.mark.parametrize("orders", [(1,), (2,), (2, 3, 4)])
 def test_backward_other_dilations(orc, orders):
     """The conv block's backward at dilations 1, 2 and 4 (the largest order),
