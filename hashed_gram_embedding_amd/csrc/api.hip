@@ -259,7 +259,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
 // (bf16), the weights transposed, dE (fp32), and dK / dV and E transposed
 // over tokens padded to a multiple of 64.
 struct BwdLayout {
-  size_t row_idx, e, kv, stats, dc, dkv, wt, de, dkvt, et, part, rtmp, dw, tgrad, fparts, total;
+  size_t row_idx, e, kv, stats, dc, dkv, wt, de, part, rtmp, dw, tgrad, fparts, total;
   int64_t n_pad;
   int32_t dw_split;  // K splits of the dW product
 };
@@ -294,25 +294,25 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
     return at;
   };
   L.row_idx = take((size_t)n * c->n_tables * 4);
-  L.e = take((size_t)n * mem * 2);
+  // E and [dK dV] hold n_pad rows: the dW product reads both K-outer over
+  // n_pad tokens, the rows past n zero
+  L.e = take((size_t)L.n_pad * mem * 2);
   L.kv = take((size_t)n * N * 4);
   L.stats = take((size_t)n * nb * kStatsStride * 4);
   L.dc = take((size_t)n * nb * d * 4);
-  L.dkv = take((size_t)n * N * 2);
+  L.dkv = take((size_t)L.n_pad * N * 2);
   L.wt = take((size_t)mem * N * 2);
   L.de = take((size_t)n * mem * 4);
-  L.dkvt = take((size_t)N * L.n_pad * 2);
-  L.et = take((size_t)mem * L.n_pad * 2);
   L.part = take((size_t)kBwdBlocks * 7 * d * 4);
   L.rtmp = take((size_t)32 * 4 * d * 4);
   L.dw_split = dw_split_for(N, mem, L.n_pad);
   L.dw = take((size_t)L.dw_split * N * mem * 4);
-  // the table gradient's sort and carries run last, after the dW product has
-  // read the transposed operands: they reuse that region when it is large
-  // enough (row ids, E and K / V stay intact, so a forward's kept
-  // intermediates serve any number of backward calls)
+  // the table gradient's sort and carries run last, when dC is no longer
+  // read: they reuse that region when it is large enough (row ids, E and
+  // K / V stay intact, so a forward's kept intermediates serve any number of
+  // backward calls)
   const size_t tg = table_grad_bytes(n, c->n_tables, c->row_dim);
-  L.tgrad = tg <= (size_t)N * L.n_pad * 2 ? L.dkvt : take(tg);
+  L.tgrad = tg <= (size_t)n * nb * d * 4 ? L.dc : take(tg);
   // a forward that keeps its intermediates for this pass puts its gate
   // partials where dE goes later
   const size_t fp = (size_t)n * (3 * nb + 1) * layout_for(c, n, true, 0).plan.np * 4;
@@ -321,10 +321,11 @@ BwdLayout bwd_layout(const ngram_config* c, int64_t n) {
   return L;
 }
 
-// The backward's products index their operands with 32-bit offsets: the dW
-// operands [., n_pad], and the dE product's weights transposed to
-// [mem, (nb+1) d] (whose split sums also take (nb+1) d mem as a 32-bit
-// stride).  Also the supported set of the backward pass.
+// The backward's products index some operands with 32-bit offsets: the dE
+// product's weights transposed to [mem, (nb+1) d] (whose split sums also
+// take (nb+1) d mem as a 32-bit stride); (nb+1) d n_pad and mem n_pad are
+// held to the same bound, conservatively.  Also the supported set of the
+// backward pass.
 int backward_shape_ok(const ngram_config* cfg, int64_t n) {
   if (cfg->act_dtype != NGRAM_BF16 || cfg->w_layout != NGRAM_W_D_MEM || !async_path(cfg))
     return NGRAM_EDTYPE;
@@ -700,8 +701,6 @@ int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   bf16_bits* dkv = reinterpret_cast<bf16_bits*>(ws + L.dkv);
   bf16_bits* wt = reinterpret_cast<bf16_bits*>(ws + L.wt);
   float* de = reinterpret_cast<float*>(ws + L.de);
-  bf16_bits* dkvt = reinterpret_cast<bf16_bits*>(ws + L.dkvt);
-  bf16_bits* et = reinterpret_cast<bf16_bits*>(ws + L.et);
   const bf16_bits* wk = static_cast<const bf16_bits*>(w_k);
   const bf16_bits* wv = static_cast<const bf16_bits*>(w_v);
 
@@ -758,15 +757,35 @@ int backward_impl(const ngram_config* cfg, const int32_t* raw_ids, int32_t B, in
   if (st) return st;
   st = hip_status(raw_gemm(dkv, n, N, nullptr, wt, 0, mem, de, mem, s));
   if (st) return st;
-  // dW = [dK dV]^T E: both operands transposed to [., n_pad], tokens padded with zeros
+  // dW = [dK dV]^T E over n_pad tokens, both operands read as they lie (a row
+  // per token) by the K-outer product
   tm.stage(3);
-  st = hip_status(launch_transpose_bf16(dkv, n, N, N, dkvt, L.n_pad, L.n_pad, s));
-  if (st) return st;
-  st = hip_status(launch_transpose_bf16(e, n, mem, mem, et, L.n_pad, L.n_pad, s));
-  if (st) return st;
+  // the tokens past n contribute nothing: zero rows of both operands
+  if (L.n_pad > n) {
+    st = hip_status(launch_zero_f32(reinterpret_cast<float*>(dkv + n * N), (L.n_pad - n) * N / 2, s));
+    if (st) return st;
+    st = hip_status(launch_zero_f32(reinterpret_cast<float*>(e + n * mem), (L.n_pad - n) * mem / 2, s));
+    if (st) return st;
+  }
   // one split-K product for every row of [dK dV]^T, the splits summed into d_w_k and d_w_v
   float* dw = reinterpret_cast<float*>(ws + L.dw);
-  st = hip_status(raw_gemm(dkvt, N, (int32_t)L.n_pad, nullptr, et, 0, mem, dw, mem, s, L.dw_split));
+  {
+    AsyncProjArgs a;
+    memset(&a, 0, sizeof a);
+    a.e = dkv;
+    a.wv = e;
+    a.tn_lda = N;
+    a.tn_ldb = mem;
+    a.epi.M = N;
+    a.epi.d = mem;
+    a.K = (int32_t)L.n_pad;
+    a.group_m = 4;
+    a.raw_out = dw;
+    a.raw_ld = mem;
+    a.raw_split = L.dw_split;
+    a.raw_split_stride = N64 * mem;
+    st = hip_status(launch_projection_raw_tn(a, s));
+  }
   if (st) return st;
   const int64_t kw = (int64_t)nb * d * mem;
   st = hip_status(launch_sum_splits(dw, L.dw_split, N64 * mem, kw, d_w_k, s));

@@ -173,6 +173,9 @@ struct AsyncProjArgs {
   int64_t raw_ld;
   int32_t raw_split;
   int64_t raw_split_stride;
+  // launch_projection_raw_tn: A = e [K][M] and B = wv [K][N] with these row
+  // strides (elements); M = epi.M, N = epi.d
+  int64_t tn_lda, tn_ldb;
 };
 
 // Gate + gated value + conv block over a [B, T] token grid.
@@ -333,6 +336,7 @@ int async_plan(int64_t M, int override_plan);
 int async_wave_cols(int plan);
 hipError_t launch_projection_async(int plan, const AsyncProjArgs& a, hipStream_t s);
 hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s);
+hipError_t launch_projection_raw_tn(const AsyncProjArgs& a, hipStream_t s);
 // split-K raw-tile variant for small M (decode); E given densely
 // Decode E tiles: the decode step's E [M, K] bf16 is stored as 1 KB tiles of
 // 16 tokens x 32 K values, tile (mb, kk) at element ((mb * K/32) + kk) * 512,

@@ -300,6 +300,170 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   }
 }
 
+// The raw product with both operands stored K-outer ("TN"): C[M, N] =
+// A^T B over K, A [K][M] (row stride tn_lda) and B [K][N] (row stride
+// tn_ldb), both bf16 -- the backward's dW = [dK dV]^T E, whose operands are
+// row-per-token, without transposing them first.  The tiles are copied
+// global -> LDS as they lie (a K row of the tile is BM contiguous elements,
+// its 16-byte chunks XOR-swizzled by (row & 3) << 2), and the MFMA operands,
+// which hold 8 consecutive K per lane, come out of LDS through gfx950's
+// transposing read ds_read_b64_tr_b16: within a group of 16 lanes, lane j
+// names 4 elements of K row j / 4; lane i receives element i % 4 of rows
+// 4r + i / 4's lane, r = 0..3 -- so lanes naming rows k0..k0+3 at columns
+// c + 4 (j % 4) hand lane i the 4 K values of column c + i.  A 16-lane group
+// thus reads a 4 x 16 block; two reads give an operand's 8 K values.  The
+// swizzle puts the 4 rows x 64 bytes that lanes 0-31 read on distinct banks.
+// Rows of K past the product's K are the caller's zeros; columns past M or N
+// are clamped to the last chunk, computed and never stored.
+template <int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_raw_tn_kernel(AsyncProjArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;
+  constexpr int NW = WGM * WGN;
+  constexpr int RPC = 2;                    // K rows per wave-wide copy (512-byte rows)
+  constexpr int A_INS = BK / (RPC * NW);    // copies per wave per stage and operand
+  constexpr int PER_STAGE = 2 * A_INS;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int A_ELEMS = BK * BM;
+  constexpr int STAGE_ELEMS = BK * (BM + BN);
+  static_assert(A_INS * RPC * NW == BK, "copy shape");
+  static_assert(MI * 32 == WTM && NI * 32 == WTN, "wave tile");
+
+  __shared__ __attribute__((aligned(16))) bf16_bits ring0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring1[STAGE_ELEMS];
+  auto slot = [&](int sl) -> bf16_bits* { return sl ? ring1 : ring0; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int split = a.raw_split > 1 ? a.raw_split : 1;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int ksl = split > 1 ? (int)blockIdx.x / tiles : 0;
+  const int bid = split > 1 ? (int)blockIdx.x - ksl * tiles : (int)blockIdx.x;
+  int m_tile, seg, n_tile;
+  map_tile(bid, a.tiles_m, 1, a.tiles_n, a.group_m, m_tile, seg, n_tile);
+  const int64_t M = a.epi.M;
+  const int N = a.epi.d;
+  const int m0 = m_tile * BM, n0 = n_tile * BN;
+  const int K = a.K;
+  const int kt_first = split > 1 ? ksl * (K / BK) / split : 0;
+  const int nk = split > 1 ? (ksl + 1) * (K / BK) / split - kt_first : K / BK;
+
+  // copy lanes: K row 2 i + lane / 32 of the copy, physical chunk lane % 32
+  // holding logical chunk (lane % 32) ^ ((row & 3) << 2); the copy's first
+  // row is even, so row & 3 = 2 (i & 1) + lane / 32
+  const int cpc = lane & 31, crow = lane >> 5;
+  auto issue = [&](int kt, int sl) {
+    bf16_bits* As = slot(sl);
+    bf16_bits* Bs = As + A_ELEMS;
+    const int64_t k0 = (int64_t)(kt_first + kt) * BK;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = (wave * A_INS + i) * RPC + crow;  // K row within the tile
+      const int lch = cpc ^ ((r & 3) << 2);
+      int ma = m0 + lch * 8;
+      if (ma > M - 8) ma = (int)M - 8;
+      int nb_ = n0 + lch * 8;
+      if (nb_ > N - 8) nb_ = N - 8;
+      copy16_to_lds(a.e + (k0 + r) * a.tn_lda + ma, As + (wave * A_INS + i) * RPC * BM);
+      copy16_to_lds(a.wv + (k0 + r) * a.tn_ldb + nb_, Bs + (wave * A_INS + i) * RPC * BN);
+    }
+  };
+
+  floatx16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  // operand lanes: group g = lane / 16 takes columns 16 (g & 1) + 4 (j & 3)
+  // of a 32-column block and K rows 8 (g >> 1) + j / 4 (+4 for the second
+  // read) of a 16-wide K step; row & 3 = j / 4 for every read, so the
+  // swizzle is fixed per lane
+  const int j = lane & 15, g = lane >> 4, q = j >> 2;
+  const uint32_t lane_row_b = (uint32_t)((8 * (g >> 1) + q) * (BM * 2));  // BM == BN
+  const int lane_cin = 2 * (g & 1) + ((j & 3) >> 1);   // chunk within a 32-column block
+  const uint32_t lane_half_b = (uint32_t)(8 * (j & 1));
+  auto frag_off = [&](int blk32) -> uint32_t {          // byte offset within a K row
+    return (uint32_t)((((blk32 ^ q) << 2) | lane_cin) * 16) + lane_half_b;
+  };
+  uint32_t a_off[MI], b_off[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) a_off[mi] = frag_off((wm * WTM) / 32 + mi);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) b_off[ni] = frag_off((wn * WTN) / 32 + ni);
+
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef short s8v __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) s4v lds_s4v;
+  auto tr8 = [&](const char* base, uint32_t off) -> bf16x8 {
+    const lds_s4v* p0 = (const lds_s4v*)(const __attribute__((address_space(3))) char*)(base + off);
+    const lds_s4v* p1 = (const lds_s4v*)(const __attribute__((address_space(3))) char*)(
+        base + off + 4 * BM * 2);
+    const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)p0);
+    const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)p1);
+    const s8v x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, x);
+  };
+  auto compute = [&](int sl) {
+    const char* As = reinterpret_cast<const char*>(slot(sl));
+    const char* Bs = As + A_ELEMS * 2;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const uint32_t rb = lane_row_b + (uint32_t)(kk * 16 * BM * 2);
+      bf16x8 af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[mi] = tr8(As, rb + a_off[mi]);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = tr8(Bs, rb + b_off[ni]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  // the same two-slot ring as proj_async_kernel (its loop-header argument
+  // applies unchanged)
+  issue(0, 1);
+  if (nk > 0) issue(0, 0);
+  for (int base = 0; base < nk; base += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int kt = base + u;
+      if (kt < nk) {
+        if (kt + STAGES - 2 < nk)
+          wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+        else
+          wait_vmcnt<0>();
+        barrier_keep_copies();
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (u + STAGES - 1) % STAGES);
+        compute(u);
+      }
+    }
+  }
+
+  // fp32 out, as the raw epilogue of proj_async_kernel
+  const int wcol0 = n0 + wn * WTN;
+  if (wcol0 >= N) return;
+  float* __restrict__ C = a.raw_out + ksl * a.raw_split_stride;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = wcol0 + ni * 32 + (lane & 31);
+      if (col < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * WTM + mi * 32 + acc_row(r, lane);
+          if (row < M) __builtin_nontemporal_store(acc[mi][ni][r], &C[row * a.raw_ld + col]);
+        }
+      }
+    }
+}
+
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
 hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
   AsyncProjArgs a = a0;
@@ -364,6 +528,24 @@ int async_wave_cols(int plan) {
   NGRAM_ASYNC_PLANS(NGRAM_WAVE_COLS)
 #undef NGRAM_WAVE_COLS
   return -1;
+}
+
+// The raw product of two K-outer operands (proj_raw_tn_kernel): K a
+// multiple of 64 whose rows past the true K are zero, M and N multiples of 8,
+// the operands' rows 16-byte aligned.
+hipError_t launch_projection_raw_tn(const AsyncProjArgs& a0, hipStream_t s) {
+  AsyncProjArgs a = a0;
+  if (a.epi.M == 0 || a.epi.d == 0) return hipSuccess;
+  if (a.raw_out == nullptr || a.K % 64 != 0 || a.epi.M % 8 != 0 || a.epi.d % 8 != 0 ||
+      a.tn_lda % 8 != 0 || a.tn_ldb % 8 != 0 || a.tn_lda < a.epi.M || a.tn_ldb < a.epi.d)
+    return hipErrorInvalidValue;
+  a.tiles_m = (int)((a.epi.M + 255) / 256);
+  a.tiles_n = (a.epi.d + 255) / 256;
+  const int split = a.raw_split > 1 ? a.raw_split : 1;
+  if (split > a.K / 64) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * split;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  return launch(proj_raw_tn_kernel<2, 4>, (unsigned)blocks, 512, 0, s, a);
 }
 
 // The raw product serves the backward pass; it is built for the default
