@@ -64,6 +64,8 @@ def parse():
                     help="timed steps of each other workload (long prefill, multi-branch)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--proj-plan", type=int, default=None, metavar="ID",
+                    help="prefill projection tile plan id (the library picks one by default)")
     ap.add_argument("--profile-region", action="store_true",
                     help="for a profiler's kernel trace: a few warmup steps, then only the "
                          "timed region, held behind a spin long enough for a profiled host to "
@@ -92,7 +94,7 @@ def shared_tables(w):
 
 
 class Setup:
-    def __init__(self, name: str, pool: int):
+    def __init__(self, name: str, pool: int, proj_plan=None):
         import torch
 
         import hashed_gram_embedding_amd as H
@@ -104,7 +106,7 @@ class Setup:
         self.w = w
         # projection weights stored [d, mem] (torch.nn.Linear layout): the
         # library's fast path
-        self.cfg = H.make_config(**W.layer_config(w, "d_mem"))
+        self.cfg = H.make_config(**W.layer_config(w, "d_mem"), proj_plan=proj_plan)
         self.pool = pool if w.history_len else 1
         dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
         self.tables = shared_tables(w)
@@ -495,12 +497,12 @@ def step_fractions(w, total_alg, ms: float):
             "binding_frac": max(t_hbm, t_mfma) / t}
 
 
-def other_workload(name: str, steps: int, warmup: int, attainable: float):
+def other_workload(name: str, steps: int, warmup: int, attainable: float, proj_plan=None):
     """tokens/s, stage times and roofline figures of one more workload over the
     tables already resident (the long prefill, the multi-branch sweep)."""
     import torch
     print(f"[bench] workload {name}", file=sys.stderr, flush=True)
-    setup = Setup(name, 1)
+    setup = Setup(name, 1, proj_plan)
     w = setup.w
     stream = torch.cuda.current_stream()
     if w.history_len:  # a decode step: many steps, pre-queued
@@ -616,7 +618,7 @@ def main():
     print("[bench] attainable HBM bandwidth (1 GiB device copy)", file=sys.stderr, flush=True)
     attainable = attainable_gbs()
     print(f"[bench] setting up workload {args.workload}", file=sys.stderr, flush=True)
-    setup = Setup(args.workload, args.pool)
+    setup = Setup(args.workload, args.pool, args.proj_plan)
     w = setup.w
     stages_alg, total_alg = algorithmic(w)
     stream = torch.cuda.current_stream()
@@ -711,7 +713,7 @@ def main():
         del setup
         torch.cuda.empty_cache()
         result["other_workloads"] = [
-            other_workload(n, args.other_steps, 2, attainable)
+            other_workload(n, args.other_steps, 2, attainable, args.proj_plan)
             for n in ("qwen_prefill", "qwen_multibranch_uniform", "qwen_multibranch_zipf13",
                       "qwen_decode_16x160", "qwen_prefill_16x160")]
     print(json.dumps(result), flush=True)
@@ -726,7 +728,7 @@ def profile_region(args):
     w_name = args.workload or "qwen_decode"
     steps = 300 if args.steps is None else args.steps
     warmup = 3 if args.warmup is None else args.warmup
-    setup = Setup(w_name, args.pool)
+    setup = Setup(w_name, args.pool, args.proj_plan)
     for i in range(warmup):
         setup.step(i % setup.pool)
     torch.cuda.synchronize()
@@ -820,7 +822,7 @@ def main_backward(args):
 
     name = args.workload or "qwen_train"
     print(f"[bench] setting up training workload {name}", file=sys.stderr, flush=True)
-    setup = Setup(name, 1)
+    setup = Setup(name, 1, args.proj_plan)
     H, w = setup.H, setup.w
     if w.dtype != "bf16" or w.seq_len == 1:
         raise SystemExit("--pass backward needs a bf16 prefill-shaped workload")

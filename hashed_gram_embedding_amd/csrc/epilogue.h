@@ -3,6 +3,8 @@
 // (value segment).  See project.hip for the layer context.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ngram {
@@ -153,6 +155,124 @@ __device__ __forceinline__ uint32_t mod_prime(uint64_t key, uint64_t p, uint64_t
   uint64_t r = key - q * p;
   if (r >= p) r -= p;
   return (uint32_t)r;
+}
+
+// The same for a wave tile of 16x16-MFMA blocks (v_mfma_f32_16x16x32_bf16):
+// accumulator register j of lane l holds row 4 * (l / 16) + j, column l % 16
+// of its block, so a row's columns are spread over the 16 lanes of one
+// quarter-wave.  Each lane sums its columns of the tile's blocks first, then
+// the quarter-wave sums its four rows by recursive halving (5 shuffles a
+// quantity instead of 16); lane l ends up with row owner4(l) of its quarter
+// (the four lanes l & ~3 .. l | 3 hold the same value).
+__device__ __forceinline__ float xsum4_16(float (&x)[4], int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const bool up = lane & 8;
+    const float keep = up ? x[2 + q] : x[q];
+    const float send = up ? x[q] : x[2 + q];
+    x[q] = keep + __shfl_xor(send, 8);
+  }
+  {
+    const bool up = lane & 4;
+    const float keep = up ? x[1] : x[0];
+    const float send = up ? x[0] : x[1];
+    x[0] = keep + __shfl_xor(send, 4);
+  }
+  x[0] += __shfl_xor(x[0], 2);
+  return x[0] + __shfl_xor(x[0], 1);
+}
+
+__device__ __forceinline__ int owner4(int lane) { return ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1); }
+
+template <int MI, int NI, class HRead>
+__device__ __forceinline__ void gate_epilogue16(const floatx4 (&acc)[MI][NI], const EpiArgs& a,
+                                                int seg, int64_t wrow0, int wcol0, int pidx,
+                                                int lane, HRead&& hread) {
+  const int d = a.d;
+  const int64_t M = a.M;
+  const int nq = 3 * a.nb + 1;
+  const int rq = 4 * (lane >> 4);  // first of the lane's four rows in a block
+  if (seg < a.nb) {
+    float* __restrict__ K = a.k_keep ? a.k_keep + (int64_t)seg * d : nullptr;
+    float g[NI];
+    bool cv[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = wcol0 + ni * 16 + (lane & 15);
+      cv[ni] = col < d;
+      const int cc = cv[ni] ? col : 0;
+      g[ni] = (a.gamma_q ? bf16_to_f32(a.gamma_q[cc]) : 1.0f) *
+              (a.gamma_k ? bf16_to_f32(a.gamma_k[cc]) : 1.0f);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      float xd[4], xk[4], xh[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xd[j] = xk[j] = xh[j] = 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = wcol0 + ni * 16 + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t row = wrow0 + mi * 16 + rq + j;
+          if (cv[ni] && row < M) {
+            const float h = hread(row, col);
+            const float k = acc[mi][ni][j];
+            if (K) __builtin_nontemporal_store(k, &K[row * a.v_ld + col]);
+            xd[j] += g[ni] * h * k;
+            xk[j] += k * k;
+            xh[j] += h * h;
+          }
+        }
+      }
+      const float sd = xsum4_16(xd, lane);
+      const float sk = xsum4_16(xk, lane);
+      const float sh = xsum4_16(xh, lane);
+      const int64_t row = wrow0 + mi * 16 + rq + owner4(lane);
+      if (!(lane & 3) && row < M) {
+        float* p = a.parts + (row * nq + 3 * seg) * a.np + pidx;
+        p[0] = sd;
+        p[a.np] = sk;
+        p[2 * a.np] = sh;
+      }
+    }
+  } else {
+    float* __restrict__ V = a.v;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      float xv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = wcol0 + ni * 16 + (lane & 15);
+        if (col < d) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t row = wrow0 + mi * 16 + rq + j;
+            if (row < M) {
+              const float v = acc[mi][ni][j];
+              __builtin_nontemporal_store(v, &V[row * a.v_ld + col]);  // read once, by the conv
+              xv[j] += v * v;
+            }
+          }
+        }
+      }
+      const float sv = xsum4_16(xv, lane);
+      const int64_t row = wrow0 + mi * 16 + rq + owner4(lane);
+      if (!(lane & 3) && row < M) a.parts[(row * nq + 3 * a.nb) * a.np + pidx] = sv;
+    }
+  }
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void gate_epilogue16(const floatx4 (&acc)[MI][NI], const EpiArgs& a,
+                                                int seg, int64_t wrow0, int wcol0, int pidx,
+                                                int lane) {
+  const bf16_bits* __restrict__ H = a.hidden + seg * a.h_branch_stride;
+  const int64_t ht = a.h_tok_stride;
+  gate_epilogue16<MI, NI>(acc, a, seg, wrow0, wcol0, pidx, lane,
+                          [&](int64_t row, int col) { return bf16_to_f32(H[row * ht + col]); });
 }
 
 }  // namespace ngram

@@ -17,6 +17,7 @@ namespace ngram {
 typedef uint16_t bf16_bits;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -331,7 +332,7 @@ ProjPlan plan_projection(int dtype, int64_t M, int32_t d);
 hipError_t launch_projection(int dtype, const ProjPlan& plan, const ProjArgs& a, hipStream_t s);
 
 // Tile plan for M rows (override: a plan id >= 0); wave_cols = partial width.
-constexpr int kAsyncPlans = 12;
+constexpr int kAsyncPlans = 13;
 int async_plan(int64_t M, int override_plan);
 int async_wave_cols(int plan);
 hipError_t launch_projection_async(int plan, const AsyncProjArgs& a, hipStream_t s);

@@ -95,7 +95,10 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int n_seg, int ti
   n = sn - seg * tiles_n;
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool RAW = false>
+// MF: the MFMA shape, v_mfma_f32_32x32x16_bf16 (32) or v_mfma_f32_16x16x32_bf16
+// (16).  Both read their operands as 16 lanes x 16 bytes of 16 consecutive
+// rows per pass, so the ring, the copies and the swizzle are the same.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool RAW = false, int MF = 32>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProjArgs a) {
   constexpr int NW = WGM * WGN;          // waves per workgroup
   constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
@@ -104,11 +107,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   constexpr int B_INS = BN / (RPI * NW);
   constexpr int PER_STAGE = A_INS + B_INS;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int MI = WTM / MF, NI = WTN / MF;
+  constexpr int AR = MF == 32 ? 16 : 4;   // accumulator registers per MFMA block
+  typedef std::conditional_t<MF == 32, floatx16, floatx4> acc_t;
   constexpr int A_ELEMS = BM * BK;
   constexpr int STAGE_ELEMS = (BM + BN) * BK;
   static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "tile / copy shape");
-  static_assert(MI * 32 == WTM && NI * 32 == WTN, "wave tile");
+  static_assert(MI * MF == WTM && NI * MF == WTN, "wave tile");
+  static_assert(MF == 32 || (MF == 16 && !RAW && BK % 32 == 0), "MFMA shape");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
   __shared__ __attribute__((aligned(16))) bf16_bits ring0[STAGE_ELEMS];
@@ -148,10 +154,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   const int lrow = lane / CH, pch = lane - (lane / CH) * CH;
   const int lch8 = (pch ^ swz<BK>(lrow)) * 8;  // element offset of the fetched chunk
   // Operand-read lanes: LDS byte offset of this lane's A and B rows for
-  // mi = ni = 0; the other blocks are +32 rows (immediate offsets), and the
+  // mi = ni = 0; the other blocks are +MF rows (immediate offsets), and the
   // swizzle of all of them equals that of the lane's row (rows differ by
   // multiples of 16, which leaves row bits 0..3 alone).
-  const int frow = lane & 31;
+  const int frow = lane & (MF - 1);
   const uint32_t a_row_b = (uint32_t)((wm * WTM + frow) * BK * 2);
   const uint32_t b_row_b = (uint32_t)((wn * WTN + frow) * BK * 2);
   const int fsw = swz<BK>(frow);
@@ -180,33 +186,42 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     }
   };
 
-  floatx16 acc[MI][NI];
+  acc_t acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+      for (int r = 0; r < AR; ++r) acc[mi][ni][r] = 0.0f;
 
-  // MFMAs over the K step held in ring slot sl
+  // MFMAs over the K step held in ring slot sl: BK / (512 / MF) sub-steps,
+  // lane l reading row l % MF of each block and the 16-byte chunk
+  // l / MF of the sub-step (MF = 32: 2 chunks of 16 K; 16: 4 chunks of 32 K)
   auto compute = [&](int sl) {
     const char* As = reinterpret_cast<const char*>(slot(sl));
     const char* Bs = As + A_ELEMS * 2;
+    constexpr int CPS = 64 / MF;  // chunks per sub-step
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const uint32_t co = (uint32_t)(((kk * 2 + (lane >> 5)) ^ fsw) * 16);
+    for (int kk = 0; kk < BK / (8 * CPS); ++kk) {
+      const uint32_t co = (uint32_t)(((kk * CPS + lane / MF) ^ fsw) * 16);
       bf16x8 af[MI], bfr[NI];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(As + a_row_b + co + mi * 32 * BK * 2);
+        af[mi] = *reinterpret_cast<const bf16x8*>(As + a_row_b + co + mi * MF * BK * 2);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        bfr[ni] = *reinterpret_cast<const bf16x8*>(Bs + b_row_b + co + ni * 32 * BK * 2);
+        bfr[ni] = *reinterpret_cast<const bf16x8*>(Bs + b_row_b + co + ni * MF * BK * 2);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < NI; ++ni) {
+          if constexpr (MF == 32)
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          else
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        }
     }
   };
 
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
 
   const int wcol0 = n0 + wn * WTN;
   if (wcol0 >= d) return;
-  if (RAW) {
+  if constexpr (RAW) {
     // plain product in fp32: a half-wave stores 32 consecutive columns (128
     // bytes) of one row per register, streamed (the products are larger than
     // the caches and read by a later kernel)
@@ -287,16 +302,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
           }
         }
       }
-    return;
-  }
-  if (HSTAGE) {
-    gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane,
-                          [&](int64_t row, int col) {
-                            const int rl = (int)(row - m0), cl = col - n0;
-                            return bf16_to_f32(slot(rl / RPS)[(rl % RPS) * BN + cl]);
-                          });
   } else {
-    gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+    auto staged = [&](int64_t row, int col) {
+      const int rl = (int)(row - m0), cl = col - n0;
+      return bf16_to_f32(slot(rl / RPS)[(rl % RPS) * BN + cl]);
+    };
+    if constexpr (MF == 32) {
+      if (HSTAGE)
+        gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane, staged);
+      else
+        gate_epilogue<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+    } else {
+      if (HSTAGE)
+        gate_epilogue16<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane, staged);
+      else
+        gate_epilogue16<MI, NI>(acc, ep, seg, m0 + wm * WTM, wcol0, wcol0 / WTN, lane);
+    }
   }
 }
 
@@ -478,7 +499,7 @@ hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
                 64 * WGM * WGN, 0, s, a);
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int MF>
 hipError_t launch_async_t(const AsyncProjArgs& a0, hipStream_t s) {
   constexpr int WTN = BN / WGN;  // columns per wave = width of one row partial
   AsyncProjArgs a = a0;
@@ -488,25 +509,26 @@ hipError_t launch_async_t(const AsyncProjArgs& a0, hipStream_t s) {
   a.tiles_m = (int)((a.epi.M + BM - 1) / BM);
   a.tiles_n = (a.epi.d + BN - 1) / BN;
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n;
-  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN>, (unsigned)blocks,
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, false, MF>, (unsigned)blocks,
                 64 * WGM * WGN, 0, s, a);
 }
 
 // One table of tile plans serves both the launch and the host's partial
 // count, so the two cannot drift apart.
-#define NGRAM_ASYNC_PLANS(X)  \
-  X(0, 256, 128, 32, 4, 2, 2) \
-  X(1, 128, 128, 64, 4, 2, 2) \
-  X(2, 64, 64, 64, 4, 2, 2)   \
-  X(3, 256, 128, 64, 3, 2, 2) \
-  X(4, 128, 64, 64, 4, 2, 2)  \
-  X(5, 64, 128, 64, 4, 2, 2)  \
-  X(6, 256, 256, 32, 2, 2, 4) \
-  X(7, 256, 256, 64, 2, 2, 4) \
-  X(8, 128, 128, 64, 2, 2, 2) \
-  X(9, 256, 128, 32, 2, 2, 2) \
-  X(10, 256, 256, 32, 4, 2, 4) \
-  X(11, 256, 256, 64, 2, 4, 2)
+#define NGRAM_ASYNC_PLANS(X)      \
+  X(0, 256, 128, 32, 4, 2, 2, 32)  \
+  X(1, 128, 128, 64, 4, 2, 2, 32)  \
+  X(2, 64, 64, 64, 4, 2, 2, 32)    \
+  X(3, 256, 128, 64, 3, 2, 2, 32)  \
+  X(4, 128, 64, 64, 4, 2, 2, 32)   \
+  X(5, 64, 128, 64, 4, 2, 2, 32)   \
+  X(6, 256, 256, 32, 2, 2, 4, 32)  \
+  X(7, 256, 256, 64, 2, 2, 4, 32)  \
+  X(8, 128, 128, 64, 2, 2, 2, 32)  \
+  X(9, 256, 128, 32, 2, 2, 2, 32)  \
+  X(10, 256, 256, 32, 4, 2, 4, 32) \
+  X(11, 256, 256, 64, 2, 4, 2, 32) \
+  X(12, 256, 256, 64, 2, 4, 2, 16)
 
 }  // namespace
 
@@ -516,14 +538,16 @@ hipError_t launch_async_t(const AsyncProjArgs& a0, hipStream_t s) {
 int async_plan(int64_t M, int override_plan) {
   if (override_plan >= 0 && override_plan < kAsyncPlans) return override_plan;
   // 256 x 256 tiles from 8,192 rows: waves as 4 x 2 (64 x 128 each; 1 %
-  // faster than 2 x 4 at Qwen prefill, multibranch and engram sizes)
-  if (M >= 8192) return 11;
+  // faster than 2 x 4 at Qwen prefill, multibranch and engram sizes), on
+  // 16x16x32 MFMAs (projection 4 % faster than on 32x32x16 at Qwen prefill,
+  // 2-4 % at multibranch, the same at engram_small)
+  if (M >= 8192) return 12;
   if (M >= 1024) return 8;
   return 2;
 }
 
 int async_wave_cols(int plan) {
-#define NGRAM_WAVE_COLS(id, bm, bn, bk, st, wgm, wgn) \
+#define NGRAM_WAVE_COLS(id, bm, bn, bk, st, wgm, wgn, mf) \
   if (plan == id) return bn / wgn;
   NGRAM_ASYNC_PLANS(NGRAM_WAVE_COLS)
 #undef NGRAM_WAVE_COLS
@@ -562,8 +586,8 @@ hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s
 
 hipError_t launch_projection_async(int plan, const AsyncProjArgs& a, hipStream_t s) {
   if (a.epi.M == 0) return hipSuccess;
-#define NGRAM_LAUNCH_PLAN(id, bm, bn, bk, st, wgm, wgn) \
-  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm, wgn>(a, s);
+#define NGRAM_LAUNCH_PLAN(id, bm, bn, bk, st, wgm, wgn, mf) \
+  if (plan == id) return launch_async_t<bm, bn, bk, st, wgm, wgn, mf>(a, s);
   NGRAM_ASYNC_PLANS(NGRAM_LAUNCH_PLAN)
 #undef NGRAM_LAUNCH_PLAN
   return hipErrorInvalidValue;

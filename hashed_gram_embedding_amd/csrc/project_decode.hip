@@ -31,7 +31,6 @@ namespace ngram {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWstatWaves = 16;  // one 16-row block per wave (MI = 1)
 

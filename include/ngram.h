@@ -136,7 +136,7 @@ typedef struct ngram_config {
   float table_scale[NGRAM_MAX_TABLES];                   /* fp8 tables: finite, > 0 */
   /* Tile-plan overrides; 0 everywhere = the library's own choice.  They change
      how the work is tiled, never the result beyond fp32 summation order.
-     tune_proj_plan: 1 + id of the prefill projection's tile plan (0..11) for
+     tune_proj_plan: 1 + id of the prefill projection's tile plan (0..12) for
      bf16 with W stored [d, mem].  tune_decode_ni / tune_decode_split: the decode
      projection's 16-column blocks per workgroup (2..6) and K slices; both or
      neither, and the pair must fit (see ngram_config_validate). */

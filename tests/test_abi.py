@@ -127,8 +127,8 @@ def test_validation_codes(H):
     c.table_dtype = 2                                              # fp8 tables, fp32 activations
     assert H.ngram_config_validate(c) == E["DTYPE"]
     assert H.ngram.lib().ngram_config_validate(None) == E["INVAL"]
-    # tile-plan overrides: a prefill plan id 0..11, decode (ni, split) pairs that fit
-    assert v(proj_plan=11) == 0 and v(proj_plan=12) == E["INVAL"]
+    # tile-plan overrides: a prefill plan id 0..12, decode (ni, split) pairs that fit
+    assert v(proj_plan=12) == 0 and v(proj_plan=13) == E["INVAL"]
     q = lambda **o: H.ngram_config_validate(_cfg(H, "qwen_decode", **o))  # noqa: E731
     assert q(decode_plan=(5, 4)) == 0 and q(decode_plan=(3, 2)) == 0
     assert q(decode_plan=(7, 4)) == E["INVAL"]                     # ni past 6

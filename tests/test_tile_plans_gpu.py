@@ -13,7 +13,7 @@ from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-PLANS = list(range(12))
+PLANS = list(range(13))
 
 
 @pytest.mark.parametrize("plan", PLANS)
