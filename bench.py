@@ -485,6 +485,22 @@ def roofline(stage_avg, stages_alg, w, attainable: float):
     return roof
 
 
+def gather_op(w, stage_ms):
+    """The gather kernel of the materialised route as an operation of its own
+    (the ngram_gather entry point): the row ids in, the table rows in and E
+    out, over its event-timed average.  Within the fused forward E is an
+    intermediate; as an operation it is the output."""
+    if route(w) != "materialised" or not stage_ms.get("gather"):
+        return None
+    tes = {"f32": 4, "bf16": 2, "fp8": 1}[w.tdtype]
+    es = 4 if w.dtype == "f32" else 2
+    n = w.n_tokens
+    nbytes = n * w.n_tables * 4 + n * w.n_tables * w.row_dim * tes + n * w.mem_dim * es
+    gbs = nbytes / (stage_ms["gather"] * 1e-3) / 1e9
+    return {"bytes": nbytes, "avg_ms": stage_ms["gather"], "achieved_gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
 def step_fractions(w, total_alg, ms: float):
     """The whole step against each roofline: algorithmic bytes at 8 TB/s,
     FLOPs at 2.5 PFLOP/s, and the binding one (the larger of the two floors
@@ -523,6 +539,7 @@ def other_workload(name: str, steps: int, warmup: int, attainable: float, proj_p
            "tflops": total_alg["flops"] / (ms * 1e-3) / 1e12,
            "step_roofline": step_fractions(w, total_alg, ms),
            "roofline": roofline(st, stages_alg, w, attainable),
+           "gather_op": gather_op(w, st),
            "row_reuse": setup.row_reuse()}
     del setup
     torch.cuda.empty_cache()
@@ -697,6 +714,8 @@ def main():
         "prequeue_s": pre_s,
         "roofline": roof,
     }
+    if gather_op(w, stage_avg):
+        result["gather_op"] = gather_op(w, stage_avg)
     if route(w) == "decode" and not args.no_extras:
         print("[bench] decode with a conv-state ring, graph replay, host cost", file=sys.stderr,
               flush=True)

@@ -67,6 +67,19 @@ def test_gather_bytes_follow_the_table_format(name, tes):
     assert sum(v["bytes"] for v in stages.values()) == total["bytes"]
 
 
+def test_gather_operation_bytes():
+    """The gather as an operation at Qwen prefill (262,144 tokens): 8 row ids
+    of 4 bytes in, 8 rows of 320 bf16 values in, E of 2,560 bf16 values out
+    per token -- 2,692,743,168 bytes, so 1 ms is 2.69 TB/s; decode has no
+    separate gather kernel to report."""
+    w = W.get("qwen_prefill")
+    g = bench.gather_op(w, {"gather": 1.0})
+    assert g["bytes"] == 262144 * (32 + 5120 + 5120) == 2692743168
+    assert abs(g["achieved_gbs"] - 2692.743168) < 1e-6
+    assert abs(g["hbm_frac"] - 2692.743168 / 8000) < 1e-9
+    assert bench.gather_op(W.get("qwen_decode"), {"gather": 1.0}) is None
+
+
 def test_multibranch_counts_every_key_projection():
     """Four branches with their own W_K and a shared W_V: five d x mem
     products per token and five weight matrices."""
