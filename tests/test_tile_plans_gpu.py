@@ -39,7 +39,7 @@ def test_gate_each_plan(orc, plan, n):
     G.check(G.to_f64(u), orc.gated_value(g_ref, v), "U")
 
 
-@pytest.mark.parametrize("plan", [8, 11])
+@pytest.mark.parametrize("plan", [8, 11, 12])
 def test_gate_ragged_hidden(orc, plan):
     """A hidden size that is not a multiple of the column tile (2,080 =
     8 x 256 + 32 = 16 x 128 + 32): the last column tile's waves hold columns
