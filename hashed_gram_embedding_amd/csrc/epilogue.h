@@ -243,17 +243,47 @@ __device__ __forceinline__ void gate_epilogue16(const floatx4 (&acc)[MI][NI], co
       float xv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) xv[j] = 0.0f;
+      if constexpr (NI % 2 == 0) {
+        // Column blocks in pairs: quarter-waves 2p and 2p+1 swap halves
+        // (lane l and l ^ 16), so that each store writes 32 consecutive
+        // columns (128 bytes) of two rows instead of 16 columns of four --
+        // the even quarter's rows from block ni then ni + 1, the odd
+        // quarter's likewise, one row in each store.
+        const bool qodd = (lane >> 4) & 1;
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int col = wcol0 + ni * 16 + (lane & 15);
-        if (col < d) {
+        for (int ni = 0; ni < NI; ni += 2) {
+          const int c0 = wcol0 + ni * 16 + (lane & 15);
+          const int cs = c0 + (qodd ? 16 : 0);  // the column this lane stores
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
+            const float x0 = acc[mi][ni][j], x1 = acc[mi][ni + 1][j];
             const int64_t row = wrow0 + mi * 16 + rq + j;
             if (row < M) {
-              const float v = acc[mi][ni][j];
-              __builtin_nontemporal_store(v, &V[row * a.v_ld + col]);  // read once, by the conv
-              xv[j] += v * v;
+              if (c0 < d) xv[j] += x0 * x0;
+              if (c0 + 16 < d) xv[j] += x1 * x1;
+            }
+            const float got = __shfl_xor(qodd ? x0 : x1, 16);
+            const int64_t re = wrow0 + mi * 16 + 4 * ((lane >> 4) & ~1) + j;  // even quarter's row
+            if (cs < d) {  // read once, by the conv
+              if (re < M) __builtin_nontemporal_store(qodd ? got : x0, &V[re * a.v_ld + cs]);
+              if (re + 4 < M)
+                __builtin_nontemporal_store(qodd ? x1 : got, &V[(re + 4) * a.v_ld + cs]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = wcol0 + ni * 16 + (lane & 15);
+          if (col < d) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int64_t row = wrow0 + mi * 16 + rq + j;
+              if (row < M) {
+                const float v = acc[mi][ni][j];
+                __builtin_nontemporal_store(v, &V[row * a.v_ld + col]);  // read once, by the conv
+                xv[j] += v * v;
+              }
             }
           }
         }
