@@ -104,6 +104,10 @@ CASES = [
                                                row_start=10007, n_branches=2), True, 1),
     ("fp8_tables", W.get("engram_small").replace(batch=2, seq_len=300, hidden=256, heads=2,
                                                  row_start=10007, table_dtype="fp8"), True, 1),
+    # 8,400 tokens: the forward's projection takes the default 256 x 256 plan
+    # on 16x16 MFMAs, whose epilogue then also stores K and V for the backward
+    ("rows_8400", W.get("engram_small").replace(batch=2, seq_len=4200, hidden=256, heads=2,
+                                                row_start=10007), True, 1),
 ]
 
 

@@ -123,6 +123,15 @@ def test_backward_split_k_weight_gradients(orc, nb):
     _case(orc, w, 1, False, True, True, seed=20 + nb)
 
 
+def test_backward_8400_tokens(orc):
+    """8,400 tokens (from 8,192 rows the K / V recompute and the dE product
+    take the 256 x 256 tile, here 33 row tiles with a ragged last one of 208
+    rows) at small dimensions, so that the oracle's backward stays quick."""
+    w = SMALL.replace(batch=2, seq_len=4200)
+    print("[backward] 2 x 4200 tokens", flush=True)
+    _case(orc, w, 1, True, True, True, seed=30)
+
+
 def test_backward_widest_hidden(orc):
     """d = 4,096, the widest hidden size the backward takes (four column
     groups per thread in the per-row kernels)."""
