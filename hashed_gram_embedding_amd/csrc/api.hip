@@ -357,8 +357,9 @@ hipError_t raw_gemm(const bf16_bits* A, int64_t M, int32_t K, const bf16_bits* w
   a.raw_ld = ldc;
   a.raw_split = split;
   a.raw_split_stride = M * ldc;
-  // split-K products run on the 256 x 256 plan, whose tile count the split was chosen for
-  return launch_projection_raw(split > 1 || M >= 8192 ? 7 : M >= 1024 ? 8 : 2, a, s);
+  // split-K products run on the 256 x 256 plan, whose tile count the split was
+  // chosen for; from 8,192 rows on its 16x16x32 form
+  return launch_projection_raw(split > 1 ? 7 : M >= 8192 ? 12 : M >= 1024 ? 8 : 2, a, s);
 }
 
 // Stage timing of one instrumented call (ngram_forward_timed /

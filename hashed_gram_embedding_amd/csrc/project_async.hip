@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
   constexpr int STAGE_ELEMS = (BM + BN) * BK;
   static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "tile / copy shape");
   static_assert(MI * MF == WTM && NI * MF == WTN, "wave tile");
-  static_assert(MF == 32 || (MF == 16 && !RAW && BK % 32 == 0), "MFMA shape");
+  static_assert(MF == 32 || (MF == 16 && BK % 32 == 0 && NI % 2 == 0), "MFMA shape");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 
   __shared__ __attribute__((aligned(16))) bf16_bits ring0[STAGE_ELEMS];
@@ -289,19 +289,43 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_async_kernel(AsyncProj
     // bytes) of one row per register, streamed (the products are larger than
     // the caches and read by a later kernel)
     float* __restrict__ C = a.raw_out + ksl * a.raw_split_stride + (int64_t)seg * d;
+    if constexpr (MF == 32) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int col = wcol0 + ni * 32 + (lane & 31);
-        if (col < d) {
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = wcol0 + ni * 32 + (lane & 31);
+          if (col < d) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * WTM + mi * 32 + acc_row(r, lane);
-            if (row < M) __builtin_nontemporal_store(acc[mi][ni][r], &C[row * a.raw_ld + col]);
+            for (int r = 0; r < 16; ++r) {
+              const int64_t row = m0 + wm * WTM + mi * 32 + acc_row(r, lane);
+              if (row < M) __builtin_nontemporal_store(acc[mi][ni][r], &C[row * a.raw_ld + col]);
+            }
           }
         }
-      }
+    } else {
+      // 16x16 blocks in column pairs, quarter-waves 2p and 2p + 1 swapping
+      // halves, so that each store writes 128 contiguous bytes of two rows
+      // (as the value epilogue of gate_epilogue16 does)
+      const bool qodd = (lane >> 4) & 1;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ni += 2) {
+          const int cs = wcol0 + ni * 16 + (lane & 15) + (qodd ? 16 : 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x0 = acc[mi][ni][j], x1 = acc[mi][ni + 1][j];
+            const float got = __shfl_xor(qodd ? x0 : x1, 16);
+            const int64_t re = m0 + wm * WTM + mi * 16 + 4 * ((lane >> 4) & ~1) + j;
+            if (cs < d) {
+              if (re < M) __builtin_nontemporal_store(qodd ? got : x0, &C[re * a.raw_ld + cs]);
+              if (re + 4 < M)
+                __builtin_nontemporal_store(qodd ? x1 : got, &C[(re + 4) * a.raw_ld + cs]);
+            }
+          }
+        }
+    }
   } else {
     auto staged = [&](int64_t row, int col) {
       const int rl = (int)(row - m0), cl = col - n0;
@@ -485,7 +509,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_raw_tn_kernel(AsyncPro
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int MF = 32>
 hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
   AsyncProjArgs a = a0;
   if (a.raw_out == nullptr || a.K % BK != 0) return hipErrorInvalidValue;
@@ -495,7 +519,7 @@ hipError_t launch_raw_t(const AsyncProjArgs& a0, hipStream_t s) {
   if (split > a.K / BK) return hipErrorInvalidValue;  // every split needs a K step
   const int64_t blocks = (int64_t)a.tiles_m * (a.epi.nb + 1) * a.tiles_n * split;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true>, (unsigned)blocks,
+  return launch(proj_async_kernel<BM, BN, BK, STAGES, WGM, WGN, true, MF>, (unsigned)blocks,
                 64 * WGM * WGN, 0, s, a);
 }
 
@@ -580,6 +604,7 @@ hipError_t launch_projection_raw(int plan, const AsyncProjArgs& a, hipStream_t s
     case 2: return launch_raw_t<64, 64, 64, 4, 2, 2>(a, s);
     case 7: return launch_raw_t<256, 256, 64, 2, 2, 4>(a, s);
     case 8: return launch_raw_t<128, 128, 64, 2, 2, 2>(a, s);
+    case 12: return launch_raw_t<256, 256, 64, 2, 4, 2, 16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
