@@ -156,10 +156,23 @@ __global__ __launch_bounds__(512) void conv_kernel(ConvArgs a) {
   __shared__ float s_scale[kMaxTile + kMaxHalo];
 
   const int tiles = (a.T + a.tile - 1) / a.tile;
-  const int b = blockIdx.x / tiles;
-  const int p0 = (blockIdx.x - b * tiles) * a.tile;
+  // Block -> (sequence tile, branch), branch innermost: the branches of one
+  // tile read the same V rows, so their workgroups run together, and on one
+  // XCD (workgroup w runs on XCD w % 8) when the tile count allows it, where
+  // one L2 then serves the later ones.  One branch: block = tile.
+  const int nbr = a.nb, blk = (int)blockIdx.x;
+  int tl, br;
+  if (((int64_t)a.B * tiles) % 8 == 0) {
+    const int slot = blk >> 3;
+    tl = (slot / nbr) * 8 + (blk & 7);
+    br = slot % nbr;
+  } else {
+    tl = blk / nbr;
+    br = blk % nbr;
+  }
+  const int b = tl / tiles;
+  const int p0 = (tl - b * tiles) * a.tile;
   const int p1 = min(p0 + a.tile, a.T);
-  const int br = blockIdx.y;
   const int qs = p0 - HALO;
   const int L = p1 - qs;
   const int nb = a.nb, d = a.d;
@@ -628,13 +641,15 @@ __global__ __launch_bounds__(256) void state_update_kernel(ConvArgs a) {
 template <typename T, bool FUSED>
 hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
   const int tiles = (a.T + a.tile - 1) / a.tile;
-  dim3 grid((unsigned)((int64_t)a.B * tiles), (unsigned)a.nb);
+  const int64_t blocks = (int64_t)a.B * tiles * a.nb;  // (tile, branch) pairs, see conv_kernel
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
   // Few tiles (fewer than 4 per CU): one 4-column group per thread, so each
   // tile brings more waves (engram_small's 512 tiles: 0.20 -> 0.12 ms).  Many
   // tiles: 256 threads, which keeps more tiles resident per CU (at Qwen
   // prefill's 4,096 tiles, larger blocks measured 25-35 % slower).
   int threads = 256;
-  if ((int64_t)grid.x * grid.y < 4 * 256) {
+  if (blocks < 4 * 256) {
     threads = (a.d / 4 + 63) / 64 * 64;
     if (threads > 512) threads = 512;
     if (threads < 256) threads = 256;
