@@ -406,20 +406,22 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(ConvArgs a, const 
   advance_ring(a, tok, pos, 1);
 }
 
-// The same for d <= 1024 * ITEMS and NB branches, in registers: thread x owns
-// the 4-column groups c = 4 * (x + 256 * i), i < ITEMS.  Every load the token
+// The same for d <= 4 * BS * ITEMS and NB branches, in registers: thread x of
+// the BS owns the 4-column groups c = 4 * (x + BS * i), i < ITEMS.  Every load the token
 // needs before its row reductions is issued up front (addresses past d are
 // clamped to a valid column and their contribution dropped, so the code is
 // branch-free and the loads go out together), V and h stay in registers for
 // the outputs, and one block reduction separates the two memory round trips.
 // KS > 0: exactly KS K slices, summed with every load issued up front;
 // KS == 0: k_split slices in a loop.
-template <typename T, int NB, int ITEMS, int KS>
-__global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
+template <typename T, int NB, int ITEMS, int KS, int BS>
+__global__ __launch_bounds__(BS) void decode_finalize_reg_kernel(ConvArgs a,
                                                                   const float* __restrict__ split,
                                                                   int32_t k_split, int32_t dil) {
   constexpr int NQ = 3 * NB + 1;
-  __shared__ float s_red[4][NQ];
+  static_assert(BS % 64 == 0 && BS >= 64 * 2 && BS <= 1024, "whole waves, enough for NQ sums");
+  constexpr int NW = BS / 64;
+  __shared__ float s_red[NW][NQ];
   __shared__ float s_tot[NQ];
   const int64_t tok = blockIdx.x;  // T == 1: token = sequence
   const int d = a.d;
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
   bool ok[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int c = 4 * ((int)threadIdx.x + 256 * i);
+    const int c = 4 * ((int)threadIdx.x + BS * i);
     ok[i] = c < d;
     col[i] = ok[i] ? c : d - 4;
   }
@@ -534,9 +536,12 @@ __global__ __launch_bounds__(256) void decode_finalize_reg_kernel(ConvArgs a,
     if (lane == 0) s_red[wave][q] = acc[q];
   }
   __syncthreads();
-  if (threadIdx.x < NQ)
-    s_tot[threadIdx.x] = s_red[0][threadIdx.x] + s_red[1][threadIdx.x] + s_red[2][threadIdx.x] +
-                         s_red[3][threadIdx.x];
+  if (threadIdx.x < NQ) {
+    float t = s_red[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += s_red[w][threadIdx.x];
+    s_tot[threadIdx.x] = t;
+  }
   __syncthreads();
 
   const float fd = (float)d;
@@ -672,38 +677,48 @@ hipError_t launch_conv_t(int32_t dil, const ConvArgs& a, hipStream_t s) {
   }
 }
 
-template <typename T, int NB, int ITEMS>
+template <typename T, int NB, int ITEMS, int BS>
 hipError_t launch_finalize_reg_items(int32_t k_split, const float* split, const ConvArgs& a,
                                      hipStream_t s) {
   const unsigned g = (unsigned)a.B;
   switch (k_split) {
-    case 1: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 1>, g, 256, 0, s, a, split, k_split, a.dil);
-    case 2: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 2>, g, 256, 0, s, a, split, k_split, a.dil);
-    case 4: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 4>, g, 256, 0, s, a, split, k_split, a.dil);
-    default: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 0>, g, 256, 0, s, a, split, k_split, a.dil);
+    case 1: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 1, BS>, g, BS, 0, s, a, split, k_split, a.dil);
+    case 2: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 2, BS>, g, BS, 0, s, a, split, k_split, a.dil);
+    case 4: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 4, BS>, g, BS, 0, s, a, split, k_split, a.dil);
+    default: return launch(decode_finalize_reg_kernel<T, NB, ITEMS, 0, BS>, g, BS, 0, s, a, split, k_split, a.dil);
   }
 }
 
+// items 4-column groups per thread of a 256-thread block, or (wide) of a
+// 320-thread block, which covers d = 1,280 * items with no clamped group
 template <typename T, int NB>
-hipError_t launch_finalize_reg_nb(int items, int32_t k_split, const float* split, const ConvArgs& a,
-                                  hipStream_t s) {
+hipError_t launch_finalize_reg_nb(int items, bool wide, int32_t k_split, const float* split,
+                                  const ConvArgs& a, hipStream_t s) {
+  if (wide) {
+    switch (items) {
+      case 1: return launch_finalize_reg_items<T, NB, 1, 320>(k_split, split, a, s);
+      case 2: return launch_finalize_reg_items<T, NB, 2, 320>(k_split, split, a, s);
+      case 3: return launch_finalize_reg_items<T, NB, 3, 320>(k_split, split, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (items) {
-    case 1: return launch_finalize_reg_items<T, NB, 1>(k_split, split, a, s);
-    case 2: return launch_finalize_reg_items<T, NB, 2>(k_split, split, a, s);
-    case 3: return launch_finalize_reg_items<T, NB, 3>(k_split, split, a, s);
-    case 4: return launch_finalize_reg_items<T, NB, 4>(k_split, split, a, s);
+    case 1: return launch_finalize_reg_items<T, NB, 1, 256>(k_split, split, a, s);
+    case 2: return launch_finalize_reg_items<T, NB, 2, 256>(k_split, split, a, s);
+    case 3: return launch_finalize_reg_items<T, NB, 3, 256>(k_split, split, a, s);
+    case 4: return launch_finalize_reg_items<T, NB, 4, 256>(k_split, split, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
-hipError_t launch_finalize_reg(int nb, int items, int32_t k_split, const float* split,
+hipError_t launch_finalize_reg(int nb, int items, bool wide, int32_t k_split, const float* split,
                                const ConvArgs& a, hipStream_t s) {
   switch (nb) {
-    case 1: return launch_finalize_reg_nb<T, 1>(items, k_split, split, a, s);
-    case 2: return launch_finalize_reg_nb<T, 2>(items, k_split, split, a, s);
-    case 3: return launch_finalize_reg_nb<T, 3>(items, k_split, split, a, s);
-    case 4: return launch_finalize_reg_nb<T, 4>(items, k_split, split, a, s);
+    case 1: return launch_finalize_reg_nb<T, 1>(items, wide, k_split, split, a, s);
+    case 2: return launch_finalize_reg_nb<T, 2>(items, wide, k_split, split, a, s);
+    case 3: return launch_finalize_reg_nb<T, 3>(items, wide, k_split, split, a, s);
+    case 4: return launch_finalize_reg_nb<T, 4>(items, wide, k_split, split, a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -731,10 +746,15 @@ hipError_t launch_op_conv(int dtype, int32_t dil, const ConvArgs& a, hipStream_t
 hipError_t launch_decode_finalize(int dtype, int32_t k_split, const float* split, const ConvArgs& a,
                                   hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  const int items = (a.d + 1023) / 1024;
+  int items = (a.d + 1023) / 1024;  // 4-column groups per thread of 256
+  // one fewer group per thread on 320 threads when that still covers d (at
+  // d = 2,560: two groups each instead of three, the third half clamped)
+  const bool wide = items >= 2 && items <= 4 && a.d <= 1280 * (items - 1);
+  if (wide) --items;
   if (items <= 4) {
-    return dtype == NGRAM_BF16 ? launch_finalize_reg<bf16_bits>(a.nb, items, k_split, split, a, s)
-                               : launch_finalize_reg<float>(a.nb, items, k_split, split, a, s);
+    return dtype == NGRAM_BF16
+               ? launch_finalize_reg<bf16_bits>(a.nb, items, wide, k_split, split, a, s)
+               : launch_finalize_reg<float>(a.nb, items, wide, k_split, split, a, s);
   }
   if (dtype == NGRAM_BF16)
     return launch(decode_finalize_kernel<bf16_bits>, (unsigned)a.B, 256, 0, s, a, split, k_split,
